@@ -1,0 +1,286 @@
+"""CPU oracle for SAF3R head-wise dynamic sparse global attention.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg are the only callers.  The product library never imports,
+links or runs anything here, and nothing here imports the product package.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over
+independent rows); this module builds it with gcc, binds it with ctypes and
+assembles per-head key sets the way the pages describe them:
+
+* position heads  -- static set: all special tokens, the anchor frame and the
+  query's own frame (Sec. 4.1 "Static Kernel"; Sec. 3 Obs. #2);
+* vertical heads  -- top-K of the mean-query probe qbar K^T / sqrt(D), shared by
+  all queries (Sec. 4.1 "Query-Probe Top-K", Sec. 4.3);
+* correspondence  -- per-patch top-K of DINO cosine similarity against other
+  frames (Sec. 4.1 "DINO Top-K", Sec. 4.3); special-token queries, which have
+  no DINO feature, attend to every key;
+* scanning heads  -- fixed stride of the token index plus all special tokens
+  (Sec. 4.1 "Uniform Sampling Kernel");
+* dense           -- every key (full global attention).
+
+Parity pins: see tests/test_oracle_pins.py.  Every function has at least one
+pin independent of its own code (brute force, closed form, printed values).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Dict, Iterable, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ROLE_POSITION, ROLE_VERTICAL, ROLE_CORRESPONDENCE, ROLE_SCANNING, ROLE_DENSE = 0, 1, 2, 3, 4
+MODE_TOTAL, MODE_PER_FRAME = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc -O2 -fopenmp)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = C.CDLL(_LIB)
+        P = C.c_void_p
+        i32, i64, dbl = C.c_int32, C.c_int64, C.c_double
+        L.oracle_position_set.restype = i64
+        L.oracle_position_set.argtypes = [i32, i32, i32, i32, i32, P]
+        L.oracle_scan_set.restype = i64
+        L.oracle_scan_set.argtypes = [i32, i32, i32, i32, P]
+        L.oracle_topk.restype = i64
+        L.oracle_topk.argtypes = [P, P, i64, i64, P, P, P]
+        L.oracle_mean_query.restype = C.c_int
+        L.oracle_mean_query.argtypes = [P, C.c_int, i64, i32, i64, P]
+        L.oracle_probe_scores.restype = C.c_int
+        L.oracle_probe_scores.argtypes = [P, C.c_int, i64, i32, i64, P, P]
+        L.oracle_feature_norms.restype = C.c_int
+        L.oracle_feature_norms.argtypes = [P, C.c_int, i64, i32, i64, P]
+        L.oracle_corr_scores.restype = C.c_int
+        L.oracle_corr_scores.argtypes = [P, C.c_int, i32, i32, i32, i64, P, P, i64, P]
+        L.oracle_corr_index.restype = i64
+        L.oracle_corr_index.argtypes = [P, C.c_int, i32, i32, i32, i32, i64, i32, i32, P, i64, P, P, P]
+        L.oracle_attention.restype = C.c_int
+        L.oracle_attention.argtypes = [P, P, P, C.c_int, i32, i64, i64, i64, P, P, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError("oracle inputs are float32 or bfloat16 bits (uint16)")
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _i64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+# ---------------------------------------------------------------------------
+# Key sets
+# ---------------------------------------------------------------------------
+def position_set(S: int, ns: int, P: int, anchor: int, frame: int) -> np.ndarray:
+    n = lib().oracle_position_set(S, ns, P, anchor, frame, None)
+    out = np.empty(n, dtype=np.int64)
+    lib().oracle_position_set(S, ns, P, anchor, frame, _p(out))
+    return out
+
+
+def scan_set(S: int, ns: int, P: int, stride: int) -> np.ndarray:
+    n = lib().oracle_scan_set(S, ns, P, stride, None)
+    out = np.empty(n, dtype=np.int64)
+    lib().oracle_scan_set(S, ns, P, stride, _p(out))
+    return out
+
+
+def topk(scores: np.ndarray, K: int, ids: Optional[np.ndarray] = None):
+    """(ids ascending, score of the K-th kept, best dropped score)."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    idv = None if ids is None else _i64(ids)
+    out = np.empty(min(K, s.size), dtype=np.int64)
+    kth, nxt = C.c_double(), C.c_double()
+    n = lib().oracle_topk(_p(s), _p(idv), s.size, K, _p(out), C.byref(kth), C.byref(nxt))
+    if n < 0:
+        raise MemoryError("oracle_topk")
+    return out[:n], kth.value, nxt.value
+
+
+def mean_query(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q)
+    N, d = q.shape
+    out = np.empty(d, dtype=np.float64)
+    lib().oracle_mean_query(_p(q), _dt(q), N, d, d, _p(out))
+    return out
+
+
+def probe_scores(k: np.ndarray, qbar: np.ndarray) -> np.ndarray:
+    k = np.ascontiguousarray(k)
+    N, d = k.shape
+    qb = np.ascontiguousarray(qbar, dtype=np.float64)
+    out = np.empty(N, dtype=np.float64)
+    lib().oracle_probe_scores(_p(k), _dt(k), N, d, d, _p(qb), _p(out))
+    return out
+
+
+def vertical_index(q: np.ndarray, k: np.ndarray, K: int):
+    """Top-K keys of the mean-query probe: (ids, scores r, kth, next)."""
+    r = probe_scores(k, mean_query(q))
+    ids, kth, nxt = topk(r, K)
+    return ids, r, kth, nxt
+
+
+def feature_norms(F: np.ndarray) -> np.ndarray:
+    F = np.ascontiguousarray(F)
+    Np, Df = F.shape
+    out = np.empty(Np, dtype=np.float64)
+    lib().oracle_feature_norms(_p(F), _dt(F), Np, Df, Df, _p(out))
+    return out
+
+
+def corr_scores(F: np.ndarray, S: int, P: int, rows: Sequence[int]) -> np.ndarray:
+    """Cosines of the listed patches against all patches (NaN in own frame)."""
+    F = np.ascontiguousarray(F)
+    Np, Df = F.shape
+    rows = _i64(rows)
+    norms = feature_norms(F)
+    out = np.empty((rows.size, Np), dtype=np.float64)
+    lib().oracle_corr_scores(_p(F), _dt(F), S, P, Df, Df, _p(norms), _p(rows), rows.size, _p(out))
+    return out
+
+
+def corr_index(F: np.ndarray, S: int, ns: int, P: int, K: int, rows: Sequence[int],
+               mode: int = MODE_TOTAL):
+    """Correspondence key rows for the listed patch numbers.
+
+    Returns (idx [nrows, kc] global token ids ascending, tau, next)."""
+    F = np.ascontiguousarray(F)
+    Np, Df = F.shape
+    rows = _i64(rows)
+    if mode == MODE_TOTAL:
+        kc = min(K, (S - 1) * P)
+    else:
+        kc = (S - 1) * min(K, P)
+    out = np.empty((rows.size, kc), dtype=np.int64)
+    tau = np.empty(rows.size, dtype=np.float64)
+    nxt = np.empty(rows.size, dtype=np.float64)
+    r = lib().oracle_corr_index(_p(F), _dt(F), S, ns, P, Df, Df, K, mode, _p(rows), rows.size,
+                                _p(out), _p(tau), _p(nxt))
+    if r < 0:
+        raise ValueError(f"oracle_corr_index failed ({r})")
+    return out, tau, nxt
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+def attention_sets(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, row_set, sets) -> np.ndarray:
+    """Softmax attention of the listed query rows over their key sets.
+
+    sets: list of int arrays; row r uses sets[row_set[r]].  q, k, v: [N, d]."""
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    d = q.shape[1]
+    rows, row_set = _i64(rows), _i64(row_set)
+    lens = np.array([len(s) for s in sets], dtype=np.int64)
+    set_ptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    keys = _i64(np.concatenate([np.asarray(s, dtype=np.int64) for s in sets]) if sets else [])
+    out = np.empty((rows.size, d), dtype=np.float64)
+    rc = lib().oracle_attention(_p(q), _p(k), _p(v), _dt(q), d, d, d, rows.size, _p(rows),
+                                _p(row_set), _p(set_ptr), _p(keys), _p(out))
+    if rc != 0:
+        raise ValueError("empty key set")
+    return out
+
+
+def attention(q, k, v, rows, keys) -> np.ndarray:
+    """All listed rows attend to one shared key set."""
+    rows = _i64(rows)
+    return attention_sets(q, k, v, rows, np.zeros(rows.size, dtype=np.int64), [keys])
+
+
+# ---------------------------------------------------------------------------
+# One layer: every head by its role, on a subset of query rows.
+# ---------------------------------------------------------------------------
+def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int = MODE_TOTAL,
+               rows: Optional[np.ndarray] = None, corr_rows: Optional[Dict[int, np.ndarray]] = None):
+    """Key sets per head for the given query rows, from the oracle's own selection.
+
+    Returns (per-head (row_set, sets), corr rows dict, vertical info dict)."""
+    S, ns, P, N, T = geom.S, geom.ns, geom.P, geom.N, geom.T
+    rows = np.arange(N, dtype=np.int64) if rows is None else _i64(rows)
+    frame = rows // T
+    is_special = (rows % T) < ns
+    out = {}
+    vert = {}
+    corr = dict(corr_rows or {})
+    if any(p[0] == ROLE_CORRESPONDENCE for p in plan):
+        need = [int((i // T) * P + (i % T) - ns) for i in rows[~is_special]]
+        missing = sorted(set(need) - set(corr))
+        if missing:
+            idx, _, _ = corr_index(dino, S, ns, P, corr_K, missing, corr_mode)
+            for u, r in zip(missing, idx):
+                corr[u] = r
+    for h, (role, budget, anchor, _flags) in enumerate(plan):
+        if role == ROLE_POSITION:
+            frames = np.unique(frame)
+            sets = [position_set(S, ns, P, anchor, int(f)) for f in frames]
+            row_set = np.searchsorted(frames, frame)
+        elif role == ROLE_SCANNING:
+            sets = [scan_set(S, ns, P, budget)]
+            row_set = np.zeros(rows.size, dtype=np.int64)
+        elif role == ROLE_VERTICAL:
+            ids, r, kth, nxt = vertical_index(q[h], k[h], budget)
+            vert[h] = dict(ids=ids, scores=r, kth=kth, next=nxt)
+            sets = [ids]
+            row_set = np.zeros(rows.size, dtype=np.int64)
+        elif role == ROLE_CORRESPONDENCE:
+            sets = [np.arange(N, dtype=np.int64)]
+            row_set = np.zeros(rows.size, dtype=np.int64)
+            for r_i, i in enumerate(rows):
+                if not is_special[r_i]:
+                    u = int((i // T) * P + (i % T) - ns)
+                    row_set[r_i] = len(sets)
+                    sets.append(corr[u])
+        elif role == ROLE_DENSE:
+            sets = [np.arange(N, dtype=np.int64)]
+            row_set = np.zeros(rows.size, dtype=np.int64)
+        else:
+            raise ValueError(f"unknown role {role}")
+        out[h] = (row_set, sets)
+    return out, corr, vert
+
+
+def layer(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int = MODE_TOTAL,
+          rows: Optional[np.ndarray] = None, corr_rows: Optional[Dict[int, np.ndarray]] = None,
+          heads: Optional[Iterable[int]] = None):
+    """Oracle outputs [H][nrows, d] (float64) for the listed query rows."""
+    rows = np.arange(geom.N, dtype=np.int64) if rows is None else _i64(rows)
+    sets, corr, vert = layer_sets(geom, plan, q, k, v, dino, corr_K, corr_mode, rows, corr_rows)
+    heads = range(geom.H) if heads is None else heads
+    outs = {}
+    for h in heads:
+        row_set, s = sets[h]
+        outs[h] = attention_sets(q[h], k[h], v[h], rows, row_set, s)
+    return outs, corr, vert
