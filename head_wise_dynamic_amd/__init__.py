@@ -1,0 +1,260 @@
+"""Head-wise dynamic sparse global attention on MI355X (gfx950).
+
+Thin ctypes binding of ``libsaf3r.so`` (declared in ``include/saf3r.h``).
+The raw C entry points are exposed under their C names (``saf_create``,
+``saf_sparse_attention`` ...); ``Context`` marshals torch tensors (device
+pointers, strides, the current HIP stream) into those calls.  Every step of
+the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback: if the library is missing, loading fails with an error.
+
+torch is imported before the library is loaded so that both resolve the same
+HIP runtime (libamdhip64.so.7).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsaf3r.so")
+
+SAF_OK, SAF_EINVAL, SAF_ENOMEM, SAF_EHIP, SAF_EUNSUPPORTED, SAF_ESTATE = 0, -1, -2, -3, -4, -5
+SAF_F32, SAF_BF16 = 0, 1
+SAF_POSITION, SAF_VERTICAL, SAF_CORRESPONDENCE, SAF_SCANNING, SAF_DENSE = 0, 1, 2, 3, 4
+SAF_CORR_TOTAL, SAF_CORR_PER_FRAME = 0, 1
+
+_STATUS_NAMES = {0: "SAF_OK", -1: "SAF_EINVAL", -2: "SAF_ENOMEM", -3: "SAF_EHIP",
+                 -4: "SAF_EUNSUPPORTED", -5: "SAF_ESTATE"}
+
+
+class saf_geometry_t(C.Structure):
+    _fields_ = [("num_frames", C.c_int32), ("specials_per_frame", C.c_int32),
+                ("patches_per_frame", C.c_int32), ("num_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("dtype", C.c_int32)]
+
+
+class saf_layout_t(C.Structure):
+    _fields_ = [("head_stride", C.c_int64), ("token_stride", C.c_int64)]
+
+
+class saf_head_plan_t(C.Structure):
+    _fields_ = [("role", C.c_int32), ("budget", C.c_int32), ("anchor_frame", C.c_int32),
+                ("flags", C.c_int32)]
+
+
+class SafError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+_lib = None
+_VP, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_PROTOS = {
+    "saf_create": (C.c_int, [C.POINTER(saf_geometry_t), C.POINTER(_VP)]),
+    "saf_destroy": (None, [_VP]),
+    "saf_last_error": (C.c_char_p, [_VP]),
+    "saf_workspace_size": (C.c_int, [_VP, _VP, C.POINTER(_SZ)]),
+    "saf_build_corr_index": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _VP]),
+    "saf_set_corr_index": (C.c_int, [_VP, _VP, _I32, _VP]),
+    "saf_get_corr_index": (C.c_int, [_VP, _VP, C.POINTER(_I32), _VP]),
+    "saf_build_vertical_index": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _VP, _VP, _SZ, _VP]),
+    "saf_sparse_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _I64, _VP, _SZ, _VP]),
+    "saf_dense_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _SZ, _VP]),
+}
+
+
+def lib() -> C.CDLL:
+    """Load libsaf3r.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with head_wise_dynamic_amd._build "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _PROTOS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols() -> Sequence[str]:
+    return tuple(_PROTOS)
+
+
+# Raw C entry points under their C names (argument marshalling is the caller's).
+def saf_create(geometry: saf_geometry_t, out: C.c_void_p) -> int:
+    return lib().saf_create(C.byref(geometry), C.byref(out))
+
+
+def saf_destroy(ctx) -> None:
+    lib().saf_destroy(ctx)
+
+
+def saf_last_error(ctx) -> str:
+    return (lib().saf_last_error(ctx) or b"").decode()
+
+
+def saf_workspace_size(ctx, plan, nbytes: C.c_size_t) -> int:
+    return lib().saf_workspace_size(ctx, plan, C.byref(nbytes))
+
+
+def saf_build_corr_index(ctx, dino, dino_dtype, Df, row_stride, K, mode, stream) -> int:
+    return lib().saf_build_corr_index(ctx, dino, dino_dtype, Df, row_stride, K, mode, stream)
+
+
+def saf_set_corr_index(ctx, dev_idx, Kc, stream) -> int:
+    return lib().saf_set_corr_index(ctx, dev_idx, Kc, stream)
+
+
+def saf_get_corr_index(ctx, dev_out, Kc: C.c_int32, stream) -> int:
+    return lib().saf_get_corr_index(ctx, dev_out, C.byref(Kc), stream)
+
+
+def saf_build_vertical_index(ctx, q, k, layout, head, K, dev_idx_out, ws, ws_bytes, stream) -> int:
+    return lib().saf_build_vertical_index(ctx, q, k, layout, head, K, dev_idx_out, ws, ws_bytes, stream)
+
+
+def saf_sparse_attention(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, ws, ws_bytes, stream) -> int:
+    return lib().saf_sparse_attention(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, ws, ws_bytes, stream)
+
+
+def saf_dense_attention(ctx, q, k, v, o, layout, ws, ws_bytes, stream) -> int:
+    return lib().saf_dense_attention(ctx, q, k, v, o, layout, ws, ws_bytes, stream)
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+_DT = {torch.float32: SAF_F32, torch.bfloat16: SAF_BF16}
+
+
+def make_plan(plan: Sequence[Tuple[int, int, int, int]]):
+    arr = (saf_head_plan_t * len(plan))()
+    for i, p in enumerate(plan):
+        role, budget, anchor, flags = (tuple(p) + (0, 0, 0, 0))[:4]
+        arr[i] = saf_head_plan_t(int(role), int(budget), int(anchor), int(flags))
+    return arr
+
+
+def _stream(stream: Optional[torch.cuda.Stream]):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+class Context:
+    """One geometry (S frames of ns special + P patch tokens, H heads of 64)."""
+
+    def __init__(self, S: int, ns: int, P: int, H: int = 16, d: int = 64,
+                 dtype: torch.dtype = torch.bfloat16):
+        self.S, self.ns, self.P, self.H, self.d = S, ns, P, H, d
+        self.T = ns + P
+        self.N = S * self.T
+        self.Np = S * P
+        self.dtype = dtype
+        self._ctx = C.c_void_p()
+        geom = saf_geometry_t(S, ns, P, H, d, _DT.get(dtype, 99))
+        self._check(saf_create(geom, self._ctx), None)
+        self._ws = None
+
+    def close(self):
+        if self._ctx:
+            saf_destroy(self._ctx)
+            self._ctx = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st: int, ctx=...):
+        if st != SAF_OK:
+            raise SafError(st, saf_last_error(self._ctx if ctx is ... else ctx))
+
+    # -- tensors ------------------------------------------------------------
+    def layout_of(self, t: torch.Tensor) -> saf_layout_t:
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError("expected a 3-D tensor with contiguous channels")
+        if t.shape == (self.H, self.N, self.d):
+            return saf_layout_t(t.stride(0), t.stride(1))
+        if t.shape == (self.N, self.H, self.d):
+            return saf_layout_t(t.stride(1), t.stride(0))
+        raise ValueError(f"tensor shape {tuple(t.shape)} is neither [H,N,d] nor [N,H,d]")
+
+    def workspace(self, nbytes: int, device) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < nbytes or self._ws.device != device:
+            self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self._ws
+
+    def workspace_size(self, plan) -> int:
+        n = C.c_size_t()
+        self._check(saf_workspace_size(self._ctx, make_plan(plan) if plan is not None else None, n))
+        return n.value
+
+    # -- index builders -----------------------------------------------------
+    def build_corr_index(self, dino: torch.Tensor, K: int, mode: int = SAF_CORR_TOTAL, stream=None):
+        if dino.dim() != 2 or dino.stride(1) != 1:
+            raise ValueError("dino must be [S*P, Df] with contiguous channels")
+        self._check(saf_build_corr_index(self._ctx, C.c_void_p(dino.data_ptr()), _DT.get(dino.dtype, 99),
+                                         dino.shape[1], dino.stride(0), K, mode, _stream(stream)))
+
+    def set_corr_index(self, idx: torch.Tensor, stream=None):
+        if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():
+            raise ValueError("index must be a contiguous int32 [S*P, Kc] tensor")
+        self._check(saf_set_corr_index(self._ctx, C.c_void_p(idx.data_ptr()), idx.shape[1], _stream(stream)))
+
+    def corr_k(self) -> int:
+        kc = C.c_int32()
+        self._check(saf_get_corr_index(self._ctx, None, kc, None))
+        return kc.value
+
+    def get_corr_index(self, device="cuda", stream=None) -> torch.Tensor:
+        kc = self.corr_k()
+        out = torch.empty((self.Np, kc), dtype=torch.int32, device=device)
+        self._check(saf_get_corr_index(self._ctx, C.c_void_p(out.data_ptr()), C.c_int32(), _stream(stream)))
+        return out
+
+    def build_vertical_index(self, q: torch.Tensor, k: torch.Tensor, head: int, K: int, stream=None):
+        lay = self.layout_of(q)
+        plan = [(SAF_VERTICAL, K, 0, 0)] + [(SAF_DENSE, 0, 0, 0)] * (self.H - 1)
+        ws = self.workspace(self.workspace_size(plan), q.device)
+        out = torch.empty(min(K, self.N), dtype=torch.int32, device=q.device)
+        self._check(saf_build_vertical_index(self._ctx, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                                             lay, head, K, C.c_void_p(out.data_ptr()),
+                                             C.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+        return out
+
+    # -- attention ----------------------------------------------------------
+    def sparse_attention(self, plan, q, k, v, o=None, vert_idx: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+        lay = self.layout_of(q)
+        if o is None:
+            o = torch.empty_like(q)
+        cplan = make_plan(plan)
+        need = self.workspace_size(plan)
+        ws = self.workspace(need, q.device)
+        vptr, vld = None, 0
+        if vert_idx is not None:
+            if vert_idx.dtype != torch.int32 or vert_idx.dim() != 2 or not vert_idx.is_contiguous():
+                raise ValueError("vert_idx must be a contiguous int32 [H, ld] tensor")
+            vptr, vld = C.c_void_p(vert_idx.data_ptr()), vert_idx.shape[1]
+        self._check(saf_sparse_attention(self._ctx, cplan, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                                         C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), lay, vptr, vld,
+                                         C.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+        return o
+
+    def dense_attention(self, q, k, v, o=None, stream=None) -> torch.Tensor:
+        lay = self.layout_of(q)
+        if o is None:
+            o = torch.empty_like(q)
+        self._check(saf_dense_attention(self._ctx, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
+                                        C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), lay, None, 0,
+                                        _stream(stream)))
+        return o

@@ -1,0 +1,573 @@
+// C ABI of libsaf3r.so: argument validation, the context (correspondence
+// index cache), workspace layout and kernel dispatch.  The declarations and
+// their contracts are in include/saf3r.h.
+//
+// Every argument check runs before the first HIP call, so errors come back
+// synchronously and a context can be created and validated without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/saf3r.h"
+#include "saf_internal.h"
+
+struct saf_ctx {
+    saf::Geom g{};
+    std::string err;
+    int32_t *corr_idx = nullptr;  // [Np, corr_k]
+    int32_t corr_k = 0;
+    size_t corr_bytes = 0;
+    void *corr_scratch = nullptr;
+    size_t corr_scratch_bytes = 0;
+};
+
+namespace {
+
+std::string g_create_error;
+
+saf_status_t fail(saf_ctx_t *c, saf_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (c)
+        c->err = buf;
+    else
+        g_create_error = buf;
+    return st;
+}
+
+saf_status_t hip_fail(saf_ctx_t *c, hipError_t e, const char *what) {
+    return fail(c, SAF_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int QT = 128;           // query tile of the matrix-core kernel
+constexpr int kSplitKeys = 8192;  // keys per split for dense special rows
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+saf_status_t check_layout(saf_ctx_t *c, const saf_layout_t &lay) {
+    const saf::Geom &g = c->g;
+    const int64_t q = g.dtype == saf::BF16 ? 8 : 4;  // elements per 16 bytes
+    if (lay.token_stride < g.d || lay.head_stride < 0)
+        return fail(c, SAF_EINVAL, "layout: token_stride %lld < head_dim or negative head_stride",
+                    (long long)lay.token_stride);
+    if (lay.token_stride % q || lay.head_stride % q)
+        return fail(c, SAF_EINVAL, "layout: strides must be multiples of 16 bytes");
+    // heads and tokens must not overlap: either [H,N,d] or [N,H,d] style
+    const bool hnd = lay.head_stride >= (int64_t)g.N * lay.token_stride;
+    const bool nhd = lay.token_stride >= (int64_t)g.H * lay.head_stride && lay.head_stride >= g.d;
+    if (g.H > 1 && !hnd && !nhd)
+        return fail(c, SAF_EINVAL, "layout: head and token strides overlap");
+    return SAF_OK;
+}
+
+saf_status_t check_tensors(saf_ctx_t *c, const void *q, const void *k, const void *v, void *o) {
+    if (!q || !k || !v || !o) return fail(c, SAF_EINVAL, "null q/k/v/o pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(c, SAF_EINVAL, "q/k/v/o must be 16-byte aligned");
+    return SAF_OK;
+}
+
+struct PlanInfo {
+    int nvert = 0, ncorr = 0;
+    int64_t vert_ws = 0;      // bytes for in-call vertical index builds
+    int64_t split_ws = 0;     // bytes for dense-row split partials
+    int corr_splits = 1;
+};
+
+int corr_special_splits(const saf::Geom &g) {
+    const int64_t s = (g.N + kSplitKeys - 1) / kSplitKeys;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+
+int64_t split_part_bytes(const saf::Geom &g, int nsplit) {
+    const int64_t rows = ((int64_t)g.ns * g.S + QT - 1) / QT * QT;
+    return (int64_t)align256(sizeof(float) * 66 * rows * nsplit);
+}
+
+saf_status_t check_plan(saf_ctx_t *c, const saf_head_plan_t *plan, PlanInfo *pi) {
+    const saf::Geom &g = c->g;
+    if (!plan) return fail(c, SAF_EINVAL, "null plan");
+    *pi = PlanInfo{};
+    for (int h = 0; h < g.H; ++h) {
+        const saf_head_plan_t &p = plan[h];
+        if (p.flags != 0) return fail(c, SAF_EUNSUPPORTED, "head %d: flags must be 0", h);
+        switch (p.role) {
+        case SAF_POSITION:
+            if (p.anchor_frame < 0 || p.anchor_frame >= g.S)
+                return fail(c, SAF_EINVAL, "head %d: anchor frame %d outside [0, %d)", h, p.anchor_frame, g.S);
+            break;
+        case SAF_VERTICAL:
+            if (p.budget < 1) return fail(c, SAF_EINVAL, "head %d: vertical budget %d < 1", h, p.budget);
+            ++pi->nvert;
+            break;
+        case SAF_CORRESPONDENCE:
+            if (g.S < 2) return fail(c, SAF_EINVAL, "head %d: correspondence needs S >= 2", h);
+            if (p.budget < 0) return fail(c, SAF_EINVAL, "head %d: negative budget", h);
+            ++pi->ncorr;
+            break;
+        case SAF_SCANNING:
+            if (p.budget < 1) return fail(c, SAF_EINVAL, "head %d: scanning stride %d < 1", h, p.budget);
+            if (g.ns == 0 && p.budget > g.N) {
+                // stride set is {0}: still non-empty
+            }
+            break;
+        case SAF_DENSE:
+            break;
+        default:
+            return fail(c, SAF_EINVAL, "head %d: unknown role %d", h, p.role);
+        }
+    }
+    pi->vert_ws = (int64_t)pi->nvert * (int64_t)(align256(saf::vertical_ws_bytes(g.N)) +
+                                                 align256(sizeof(int32_t) * g.N));
+    if (pi->ncorr && g.dtype == saf::BF16) {
+        pi->corr_splits = corr_special_splits(g);
+        if (pi->corr_splits > 1) pi->split_ws = (int64_t)pi->ncorr * split_part_bytes(g, pi->corr_splits);
+    }
+    return SAF_OK;
+}
+
+hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+}  // namespace
+
+extern "C" {
+
+saf_status_t saf_create(const saf_geometry_t *geom, saf_ctx_t **out) {
+    if (!out) return fail(nullptr, SAF_EINVAL, "null output pointer");
+    *out = nullptr;
+    if (!geom) return fail(nullptr, SAF_EINVAL, "null geometry");
+    const saf_geometry_t &G = *geom;
+    if (G.num_frames < 1 || G.specials_per_frame < 0 || G.patches_per_frame < 1 || G.num_heads < 1 ||
+        G.num_heads > 64)
+        return fail(nullptr, SAF_EINVAL, "geometry: need S >= 1, ns >= 0, P >= 1, 1 <= H <= 64");
+    if (G.dtype != SAF_F32 && G.dtype != SAF_BF16) return fail(nullptr, SAF_EINVAL, "geometry: bad dtype");
+    if (G.head_dim != 64) return fail(nullptr, SAF_EUNSUPPORTED, "geometry: head_dim must be 64");
+    const int64_t T = (int64_t)G.specials_per_frame + G.patches_per_frame;
+    const int64_t N = T * G.num_frames;
+    if (N >= (int64_t)1 << 31) return fail(nullptr, SAF_EINVAL, "geometry: N must be < 2^31");
+    saf_ctx_t *c = new (std::nothrow) saf_ctx_t();
+    if (!c) return fail(nullptr, SAF_ENOMEM, "out of host memory");
+    c->g.S = G.num_frames;
+    c->g.ns = G.specials_per_frame;
+    c->g.P = G.patches_per_frame;
+    c->g.T = (int32_t)T;
+    c->g.H = G.num_heads;
+    c->g.d = G.head_dim;
+    c->g.N = N;
+    c->g.Np = (int64_t)G.num_frames * G.patches_per_frame;
+    c->g.dtype = G.dtype;
+    *out = c;
+    return SAF_OK;
+}
+
+void saf_destroy(saf_ctx_t *c) {
+    if (!c) return;
+    if (c->corr_idx || c->corr_scratch) {
+        (void)hipDeviceSynchronize();
+        if (c->corr_idx) (void)hipFree(c->corr_idx);
+        if (c->corr_scratch) (void)hipFree(c->corr_scratch);
+    }
+    delete c;
+}
+
+const char *saf_last_error(const saf_ctx_t *c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+saf_status_t saf_workspace_size(const saf_ctx_t *cc, const saf_head_plan_t *plan, size_t *bytes) {
+    saf_ctx_t *c = const_cast<saf_ctx_t *>(cc);
+    if (!c) return SAF_EINVAL;
+    if (!bytes) return fail(c, SAF_EINVAL, "null bytes pointer");
+    *bytes = 0;
+    if (!plan) return SAF_OK;  // dense attention needs none
+    PlanInfo pi;
+    const saf_status_t st = check_plan(c, plan, &pi);
+    if (st != SAF_OK) return st;
+    *bytes = (size_t)(pi.vert_ws + pi.split_ws) + 256;
+    return SAF_OK;
+}
+
+static saf_status_t ensure_corr_storage(saf_ctx_t *c, int32_t K) {
+    const size_t need = sizeof(int32_t) * (size_t)c->g.Np * (size_t)K;
+    if (c->corr_idx && c->corr_bytes == need) return SAF_OK;
+    if (c->corr_idx) {
+        hipError_t e = hipFree(c->corr_idx);
+        c->corr_idx = nullptr;
+        c->corr_bytes = 0;
+        if (e != hipSuccess) return hip_fail(c, e, "hipFree(corr index)");
+    }
+    hipError_t e = hipMalloc((void **)&c->corr_idx, need);
+    if (e != hipSuccess) {
+        c->corr_idx = nullptr;
+        (void)hipGetLastError();
+        return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for the correspondence index failed", need);
+    }
+    c->corr_bytes = need;
+    return SAF_OK;
+}
+
+saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_dtype, int32_t Df,
+                                  int64_t row_stride, int32_t K, int32_t mode, void *stream) {
+    if (!c) return SAF_EINVAL;
+    const saf::Geom &g = c->g;
+    if (!dino) return fail(c, SAF_EINVAL, "null dino pointer");
+    if (dino_dtype != SAF_F32 && dino_dtype != SAF_BF16) return fail(c, SAF_EINVAL, "bad dino dtype");
+    if (g.S < 2) return fail(c, SAF_EINVAL, "correspondence index needs S >= 2");
+    if (K < 1) return fail(c, SAF_EINVAL, "K %d < 1", K);
+    if (Df < 1) return fail(c, SAF_EINVAL, "Df %d < 1", Df);
+    if (row_stride < Df) return fail(c, SAF_EINVAL, "dino row stride %lld < Df", (long long)row_stride);
+    if (mode == SAF_CORR_PER_FRAME) return fail(c, SAF_EUNSUPPORTED, "per-frame mode is not implemented");
+    if (mode != SAF_CORR_TOTAL) return fail(c, SAF_EINVAL, "bad mode %d", mode);
+    if (Df > 4096) return fail(c, SAF_EUNSUPPORTED, "Df %d > 4096", Df);
+    const int64_t q = dino_dtype == SAF_BF16 ? 8 : 4;
+    if (row_stride % q || !aligned16(dino))
+        return fail(c, SAF_EINVAL, "dino rows must be 16-byte aligned");
+    const int64_t ncand = (int64_t)(g.S - 1) * g.P;
+    const int32_t Kc = (int32_t)std::min<int64_t>(K, ncand);
+    if (Kc > 1024) return fail(c, SAF_EUNSUPPORTED, "K %d > 1024", Kc);
+
+    saf_status_t st = ensure_corr_storage(c, Kc);
+    if (st != SAF_OK) return st;
+    const int32_t cap = saf::corr_capacity(g, Kc);
+    const size_t sb = saf::corr_scratch_bytes(g, Kc, cap);
+    if (c->corr_scratch_bytes < sb) {
+        if (c->corr_scratch) {
+            hipError_t e = hipFree(c->corr_scratch);
+            c->corr_scratch = nullptr;
+            c->corr_scratch_bytes = 0;
+            if (e != hipSuccess) return hip_fail(c, e, "hipFree(corr scratch)");
+        }
+        hipError_t e = hipMalloc(&c->corr_scratch, sb);
+        if (e != hipSuccess) {
+            c->corr_scratch = nullptr;
+            (void)hipGetLastError();
+            return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for index scratch failed", sb);
+        }
+        c->corr_scratch_bytes = sb;
+    }
+    saf::CorrBuild B{};
+    B.g = g;
+    B.dino = dino;
+    B.dino_dtype = dino_dtype;
+    B.Df = Df;
+    B.row_stride = row_stride;
+    B.K = Kc;
+    B.cap = cap;
+    B.idx_out = c->corr_idx;
+    B.scratch = c->corr_scratch;
+    hipError_t e = saf::launch_corr_build(B, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "correspondence index kernels");
+    c->corr_k = Kc;
+    return SAF_OK;
+}
+
+saf_status_t saf_set_corr_index(saf_ctx_t *c, const int32_t *dev_idx, int32_t Kc, void *stream) {
+    if (!c) return SAF_EINVAL;
+    if (!dev_idx) return fail(c, SAF_EINVAL, "null index pointer");
+    if (c->g.S < 2) return fail(c, SAF_EINVAL, "correspondence index needs S >= 2");
+    if (Kc < 1 || (int64_t)Kc > (int64_t)(c->g.S - 1) * c->g.P)
+        return fail(c, SAF_EINVAL, "Kc %d outside [1, (S-1)P]", Kc);
+    saf_status_t st = ensure_corr_storage(c, Kc);
+    if (st != SAF_OK) return st;
+    hipError_t e = hipMemcpyAsync(c->corr_idx, dev_idx, c->corr_bytes, hipMemcpyDeviceToDevice, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync(index)");
+    c->corr_k = Kc;
+    return SAF_OK;
+}
+
+saf_status_t saf_get_corr_index(const saf_ctx_t *cc, int32_t *dev_out, int32_t *Kc, void *stream) {
+    saf_ctx_t *c = const_cast<saf_ctx_t *>(cc);
+    if (!c) return SAF_EINVAL;
+    if (!c->corr_idx) return fail(c, SAF_ESTATE, "no correspondence index has been built");
+    if (Kc) *Kc = c->corr_k;
+    if (!dev_out) return SAF_OK;
+    hipError_t e = hipMemcpyAsync(dev_out, c->corr_idx, c->corr_bytes, hipMemcpyDeviceToDevice, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync(index)");
+    return SAF_OK;
+}
+
+saf_status_t saf_build_vertical_index(saf_ctx_t *c, const void *q, const void *k, saf_layout_t lay,
+                                      int32_t head, int32_t K, int32_t *dev_idx_out, void *ws,
+                                      size_t ws_bytes, void *stream) {
+    if (!c) return SAF_EINVAL;
+    if (!q || !k || !dev_idx_out || !ws) return fail(c, SAF_EINVAL, "null pointer");
+    if (head < 0 || head >= c->g.H) return fail(c, SAF_EINVAL, "head %d outside [0, %d)", head, c->g.H);
+    if (K < 1) return fail(c, SAF_EINVAL, "K %d < 1", K);
+    saf_status_t st = check_layout(c, lay);
+    if (st != SAF_OK) return st;
+    if (!aligned16(q) || !aligned16(k)) return fail(c, SAF_EINVAL, "q/k must be 16-byte aligned");
+    const size_t need = saf::vertical_ws_bytes(c->g.N);
+    if (ws_bytes < need) return fail(c, SAF_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
+    hipError_t e = saf::launch_vertical_index(c->g, q, k, lay.head_stride, lay.token_stride, head, K,
+                                              dev_idx_out, ws, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
+    return SAF_OK;
+}
+
+saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, const void *q, const void *k,
+                                  const void *v, void *o, saf_layout_t lay, const int32_t *vert_idx,
+                                  int64_t vert_ld, void *ws, size_t ws_bytes, void *stream) {
+    if (!c) return SAF_EINVAL;
+    const saf::Geom &g = c->g;
+    PlanInfo pi;
+    saf_status_t st = check_plan(c, plan, &pi);
+    if (st != SAF_OK) return st;
+    if ((st = check_tensors(c, q, k, v, o)) != SAF_OK) return st;
+    if ((st = check_layout(c, lay)) != SAF_OK) return st;
+    if (vert_idx && pi.nvert && vert_ld < 1) return fail(c, SAF_EINVAL, "vert_ld must be >= 1");
+    for (int h = 0; h < g.H && vert_idx; ++h)
+        if (plan[h].role == SAF_VERTICAL && vert_ld < std::min<int64_t>(plan[h].budget, g.N))
+            return fail(c, SAF_EINVAL, "vert_ld %lld < head %d's key count", (long long)vert_ld, h);
+    if (pi.ncorr) {
+        if (!c->corr_idx) return fail(c, SAF_ESTATE, "a correspondence head needs a built index");
+        for (int h = 0; h < g.H; ++h)
+            if (plan[h].role == SAF_CORRESPONDENCE && plan[h].budget != 0 && plan[h].budget != c->corr_k)
+                return fail(c, SAF_ESTATE, "head %d budget %d differs from the index's K %d", h,
+                            plan[h].budget, c->corr_k);
+    }
+    size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws);
+    if (need > 0) need += 256;  // room to align the start to 256 bytes
+    if (need > 0 && (!ws || ws_bytes < need))
+        return fail(c, SAF_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (ws && !aligned16(ws)) return fail(c, SAF_EINVAL, "workspace must be 16-byte aligned");
+
+    hipStream_t s = as_stream(stream);
+    char *wp = (char *)ws;
+    if (wp) wp = (char *)(((uintptr_t)wp + 255) & ~(uintptr_t)255);
+    // 1. vertical key sets
+    std::vector<const int32_t *> vlist(g.H, nullptr);
+    for (int h = 0; h < g.H; ++h) {
+        if (plan[h].role != SAF_VERTICAL) continue;
+        if (vert_idx) {
+            vlist[h] = vert_idx + (int64_t)h * vert_ld;
+            continue;
+        }
+        int32_t *idx = (int32_t *)wp;
+        wp += align256(sizeof(int32_t) * g.N);
+        void *vws = wp;
+        wp += align256(saf::vertical_ws_bytes(g.N));
+        hipError_t e = saf::launch_vertical_index(g, q, k, lay.head_stride, lay.token_stride, h,
+                                                  plan[h].budget, idx, vws, s);
+        if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
+        vlist[h] = idx;
+    }
+
+    if (g.dtype == saf::F32) {
+        // fp32: every head on the VALU row kernel
+        saf::ValuLaunch L{};
+        L.g = g;
+        L.q = q;
+        L.k = k;
+        L.v = v;
+        L.o = o;
+        L.head_stride = lay.head_stride;
+        L.token_stride = lay.token_stride;
+        L.corr_idx = c->corr_idx;
+        L.corr_k = c->corr_k;
+        L.patch_rows_only = 0;
+        for (int h0 = 0; h0 < g.H; h0 += saf::kMaxWork) {
+            L.nwork = 0;
+            for (int h = h0; h < std::min(g.H, h0 + saf::kMaxWork); ++h) {
+                saf::HeadWork &w = L.work[L.nwork++];
+                w = saf::HeadWork{};
+                w.head = h;
+                w.role = plan[h].role;
+                w.budget = plan[h].budget;
+                w.anchor = plan[h].anchor_frame;
+                w.list = vlist[h];
+                w.list_len = plan[h].role == SAF_VERTICAL ? (int32_t)std::min<int64_t>(plan[h].budget, g.N) : 0;
+                w.nsplit = 1;
+            }
+            hipError_t e = saf::launch_valu_attention(L, g.N, s);
+            if (e != hipSuccess) return hip_fail(c, e, "attention kernel (fp32)");
+        }
+        return SAF_OK;
+    }
+
+    // 2. bf16: shared-key heads on the matrix cores, ordered by key-set size
+    struct Item {
+        saf::HeadWork w;
+        int64_t tiles;
+        double cost;
+    };
+    std::vector<Item> items;
+    const int64_t tpf = (g.T + QT - 1) / QT;
+    const int64_t all_tiles = (g.N + QT - 1) / QT;
+    for (int h = 0; h < g.H; ++h) {
+        saf::HeadWork w{};
+        w.head = h;
+        w.role = plan[h].role;
+        w.budget = plan[h].budget;
+        w.anchor = plan[h].anchor_frame;
+        w.nsplit = 1;
+        Item it{};
+        switch (plan[h].role) {
+        case SAF_POSITION:
+            w.rows = saf::ROWS_FRAME;
+            it.tiles = (int64_t)g.S * tpf;
+            it.cost = (double)g.ns * g.S + 2.0 * g.P;
+            break;
+        case SAF_VERTICAL:
+            w.rows = saf::ROWS_ALL;
+            w.list = vlist[h];
+            w.list_len = (int32_t)std::min<int64_t>(plan[h].budget, g.N);
+            it.tiles = all_tiles;
+            it.cost = w.list_len;
+            break;
+        case SAF_SCANNING:
+            w.rows = saf::ROWS_ALL;
+            it.tiles = all_tiles;
+            it.cost = (double)((g.N + w.budget - 1) / w.budget) + (double)g.ns * g.S;
+            break;
+        case SAF_DENSE:
+            w.rows = saf::ROWS_ALL;
+            it.tiles = all_tiles;
+            it.cost = (double)g.N;
+            break;
+        case SAF_CORRESPONDENCE:
+            if (g.ns == 0) continue;
+            w.role = saf::DENSE;  // special-token rows attend to every key
+            w.rows = saf::ROWS_SPECIALS;
+            w.nsplit = pi.corr_splits;
+            it.tiles = ((int64_t)g.ns * g.S + QT - 1) / QT;
+            it.cost = (double)g.N / w.nsplit;
+            break;
+        }
+        it.w = w;
+        items.push_back(it);
+    }
+    std::stable_sort(items.begin(), items.end(), [](const Item &a, const Item &b) { return a.cost > b.cost; });
+    saf::MfmaLaunch M{};
+    M.g = g;
+    M.q = q;
+    M.k = k;
+    M.v = v;
+    M.o = o;
+    M.head_stride = lay.head_stride;
+    M.token_stride = lay.token_stride;
+    for (size_t i0 = 0; i0 < items.size(); i0 += saf::kMaxWork) {
+        M.nwork = 0;
+        int64_t blocks = 0;
+        for (size_t i = i0; i < std::min(items.size(), i0 + saf::kMaxWork); ++i) {
+            saf::HeadWork w = items[i].w;
+            if (w.nsplit > 1) {
+                w.part = (float *)wp;
+                wp += split_part_bytes(g, w.nsplit);
+            }
+            w.block0 = (int32_t)blocks;
+            blocks += items[i].tiles * w.nsplit;
+            M.work[M.nwork++] = w;
+        }
+        if (blocks >= ((int64_t)1 << 31)) return fail(c, SAF_EINVAL, "launch too large");
+        M.total_blocks = (int32_t)blocks;
+        hipError_t e = saf::launch_mfma_attention(M, s);
+        if (e != hipSuccess) return hip_fail(c, e, "matrix-core attention kernel");
+        e = saf::launch_split_combine(M, s);
+        if (e != hipSuccess) return hip_fail(c, e, "split combine kernel");
+    }
+
+    // 3. bf16: correspondence heads' patch rows on the gather path
+    if (pi.ncorr) {
+        saf::ValuLaunch L{};
+        L.g = g;
+        L.q = q;
+        L.k = k;
+        L.v = v;
+        L.o = o;
+        L.head_stride = lay.head_stride;
+        L.token_stride = lay.token_stride;
+        L.corr_idx = c->corr_idx;
+        L.corr_k = c->corr_k;
+        L.patch_rows_only = 1;
+        L.nwork = 0;
+        for (int h = 0; h < g.H; ++h) {
+            if (plan[h].role != SAF_CORRESPONDENCE) continue;
+            if (L.nwork == saf::kMaxWork) {
+                hipError_t e = saf::launch_valu_attention(L, g.Np, s);
+                if (e != hipSuccess) return hip_fail(c, e, "gather attention kernel");
+                L.nwork = 0;
+            }
+            saf::HeadWork &w = L.work[L.nwork++];
+            w = saf::HeadWork{};
+            w.head = h;
+            w.role = SAF_CORRESPONDENCE;
+            w.nsplit = 1;
+        }
+        hipError_t e = saf::launch_valu_attention(L, g.Np, s);
+        if (e != hipSuccess) return hip_fail(c, e, "gather attention kernel");
+    }
+    return SAF_OK;
+}
+
+saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, const void *v, void *o,
+                                 saf_layout_t lay, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!c) return SAF_EINVAL;
+    const saf::Geom &g = c->g;
+    saf_status_t st;
+    if ((st = check_tensors(c, q, k, v, o)) != SAF_OK) return st;
+    if ((st = check_layout(c, lay)) != SAF_OK) return st;
+    hipStream_t s = as_stream(stream);
+    if (g.dtype == saf::F32) {
+        saf::ValuLaunch L{};
+        L.g = g;
+        L.q = q;
+        L.k = k;
+        L.v = v;
+        L.o = o;
+        L.head_stride = lay.head_stride;
+        L.token_stride = lay.token_stride;
+        for (int h0 = 0; h0 < g.H; h0 += saf::kMaxWork) {
+            L.nwork = 0;
+            for (int h = h0; h < std::min(g.H, h0 + saf::kMaxWork); ++h) {
+                saf::HeadWork &w = L.work[L.nwork++];
+                w = saf::HeadWork{};
+                w.head = h;
+                w.role = saf::DENSE;
+                w.nsplit = 1;
+            }
+            hipError_t e = saf::launch_valu_attention(L, g.N, s);
+            if (e != hipSuccess) return hip_fail(c, e, "dense attention kernel (fp32)");
+        }
+        return SAF_OK;
+    }
+    saf::MfmaLaunch M{};
+    M.g = g;
+    M.q = q;
+    M.k = k;
+    M.v = v;
+    M.o = o;
+    M.head_stride = lay.head_stride;
+    M.token_stride = lay.token_stride;
+    const int64_t all_tiles = (g.N + QT - 1) / QT;
+    for (int h0 = 0; h0 < g.H; h0 += saf::kMaxWork) {
+        M.nwork = 0;
+        int64_t blocks = 0;
+        for (int h = h0; h < std::min(g.H, h0 + saf::kMaxWork); ++h) {
+            saf::HeadWork w{};
+            w.head = h;
+            w.role = saf::DENSE;
+            w.rows = saf::ROWS_ALL;
+            w.nsplit = 1;
+            w.block0 = (int32_t)blocks;
+            blocks += all_tiles;
+            M.work[M.nwork++] = w;
+        }
+        M.total_blocks = (int32_t)blocks;
+        hipError_t e = saf::launch_mfma_attention(M, s);
+        if (e != hipSuccess) return hip_fail(c, e, "dense attention kernel");
+    }
+    return SAF_OK;
+}
+
+}  // extern "C"

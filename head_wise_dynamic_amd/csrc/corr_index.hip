@@ -1,0 +1,461 @@
+// Correspondence index build (SAF3R Sec. 4.1 "DINO Top-K Kernel", Sec. 4.3):
+// for every patch u, the K patches v of other frames with the largest cosine
+// c_uv = f_u . f_v / (|f_u| |f_v|), ties to the lower token, stored as global
+// token indices in ascending order.  Built once per sequence and cached.
+//
+// bf16 features (the fast engine):
+//   * inverse norms 1/|f_u| in fp32;
+//   * the cosine matrix is never stored.  Columns are visited in doubling
+//     phases of patches [0,P), [P,2P), [2P,4P), ...; each phase is one MFMA
+//     GEMM (128 x 128 tiles, v_mfma_f32_32x32x16_bf16, fp32 accumulate,
+//     normalised after the dot) whose epilogue keeps only c >= theta_u, the
+//     row's current lower bound of its K-th best score, appending survivors
+//     to a per-row candidate buffer (wave ballot + one atomic per half-wave);
+//   * after each phase a compaction wave per row keeps the exact top-K of its
+//     buffer and raises theta_u to the K-th score.  Because theta_u is the
+//     K-th best of actual candidates it never exceeds the true K-th score, so
+//     no member of the final top-K is ever filtered out;
+//   * a final wave per row selects the top-K, sorts it by token and writes it.
+//   Expected survivors per phase are ~K (the K-th best of X candidates
+//   admits ~K of the next X), so buffers of max(P + 2K, 8K) entries suffice;
+//   a row whose buffer overflows anyway is flagged and recomputed exactly by
+//   the per-row engine below.
+// fp32 features (and flagged rows): one 1024-thread block per row computes
+//   every cosine with VALU FMAs into a scratch row and runs an exact block
+//   top-K (radix select + ordered compaction).
+#include "device_util.h"
+#include "topk_block.h"
+
+namespace saf {
+namespace {
+
+constexpr int GT = 128;       // GEMM tile (rows and columns)
+constexpr int GK = 32;        // k per LDS stage
+constexpr int GROW = GK + 8;  // padded LDS row (bf16)
+constexpr int kRowWaves = 4;  // rows per block in the per-row wave kernels
+constexpr int kFallbackBlocks = 256;
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Scratch {
+    float *invn;      // [Np]
+    float *theta;     // [Np]
+    uint32_t *cnt;    // [Np]
+    uint32_t *over;   // [Np] row needs the exact per-row engine
+    float2 *cand;     // [Np * cap] (score, patch index as float bits)
+    float *rowbuf;    // [kFallbackBlocks * Np] fallback scores
+};
+
+__host__ __device__ inline Scratch carve(void *base, int64_t Np, int32_t cap) {
+    char *p = (char *)base;
+    Scratch s;
+    s.invn = (float *)p;
+    p += align256(sizeof(float) * Np);
+    s.theta = (float *)p;
+    p += align256(sizeof(float) * Np);
+    s.cnt = (uint32_t *)p;
+    p += align256(sizeof(uint32_t) * Np);
+    s.over = (uint32_t *)p;
+    p += align256(sizeof(uint32_t) * Np);
+    s.cand = (float2 *)p;
+    p += align256(sizeof(float2) * (size_t)Np * cap);
+    s.rowbuf = (float *)p;
+    return s;
+}
+
+struct Args {
+    Geom g;
+    const void *F;
+    int64_t stride;
+    int32_t Df, K, cap;
+    int32_t all_rows_fallback;
+    int32_t *idx_out;
+    Scratch s;
+    int64_t col_lo, col_hi;  // current phase
+};
+
+template <typename T> __device__ inline float ldf(const T *p, int64_t i);
+template <> __device__ inline float ldf<float>(const float *p, int64_t i) { return p[i]; }
+template <> __device__ inline float ldf<uint16_t>(const uint16_t *p, int64_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+// ---- init: inverse norms, theta = -inf, counts and flags = 0 (one wave per row)
+template <typename T> __global__ __launch_bounds__(256) void init_rows(const Args A) {
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (u >= A.g.Np) return;
+    const T *f = (const T *)A.F + u * A.stride;
+    float acc = 0.f;
+    for (int c = lane; c < A.Df; c += 64) {
+        const float x = ldf<T>(f, c);
+        acc = fmaf(x, x, acc);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) {
+        A.s.invn[u] = acc > 0.f ? 1.f / sqrtf(acc) : 0.f;
+        A.s.theta[u] = -INFINITY;
+        A.s.cnt[u] = 0u;
+        A.s.over[u] = A.all_rows_fallback ? 1u : 0u;
+    }
+}
+
+// ---- one phase of the cosine GEMM with threshold filtering
+// grid (col tiles of the phase, row tiles), 256 threads = 2 x 2 waves of 64 x 64
+__global__ __launch_bounds__(256) void cos_phase(const Args A) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][GT * GROW];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GT * GROW];
+    __shared__ float r_invn[GT], r_theta[GT];
+    __shared__ int32_t r_frame[GT];
+
+    const Geom &g = A.g;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+    const int n = lane & 31, gq = lane >> 5;
+    const int64_t row0 = (int64_t)blockIdx.y * GT;
+    const int64_t col0 = A.col_lo + (int64_t)blockIdx.x * GT;
+    const uint16_t *F = (const uint16_t *)A.F;
+
+    if (tid < GT) {
+        const int64_t u = row0 + tid;
+        r_invn[tid] = u < g.Np ? A.s.invn[u] : 0.f;
+        r_theta[tid] = u < g.Np ? A.s.theta[u] : INFINITY;
+        r_frame[tid] = u < g.Np ? (int32_t)(u / g.P) : -1;
+    }
+
+    // loader: 512 chunks of 16 B per operand tile, 2 per thread
+    u32x4 ar[2], br[2];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i, row = c >> 2, seg = c & 3;
+            const int64_t u = row0 + row, v = col0 + row;
+            ar[i] = u < g.Np ? *(const u32x4 *)(F + u * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            br[i] = v < A.col_hi ? *(const u32x4 *)(F + v * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = tid + 256 * i, row = c >> 2, seg = c & 3;
+            *(u32x4 *)(&As[buf][row * GROW + 8 * seg]) = ar[i];
+            *(u32x4 *)(&Bs[buf][row * GROW + 8 * seg]) = br[i];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
+
+    const int nk = A.Df / GK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nk) load((t + 1) * GK);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 a[2], b[2];
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+                a[bi] = *(const bf16x8 *)(&As[buf][(64 * wr + 32 * bi + n) * GROW + 16 * kk + 8 * gq]);
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+                b[bj] = *(const bf16x8 *)(&Bs[buf][(64 * wc + 32 * bj + n) * GROW + 16 * kk + 8 * gq]);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 2; ++bj)
+                    acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
+        }
+        if (t + 1 < nk) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: C[row][col] with col = lane%32 of the block, rows per register
+    const uint64_t half = gq ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+        const int64_t v = col0 + 64 * wc + 32 * bj + n;
+        const bool vok = v < A.col_hi;
+        const float iv = vok ? A.s.invn[v] : 0.f;
+        const int32_t fv = vok ? (int32_t)(v / g.P) : -2;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+                const float c = acc[bi][bj][r] * r_invn[lr] * iv;
+                const bool keep = vok && r_frame[lr] >= 0 && r_frame[lr] != fv && c >= r_theta[lr];
+                const uint64_t m = __ballot(keep) & half;
+                if (m == 0ull) continue;
+                const int64_t u = row0 + lr;
+                uint32_t base = 0;
+                const int leader = __ffsll((unsigned long long)m) - 1;
+                if (lane == leader) base = atomicAdd(&A.s.cnt[u], (uint32_t)__popcll(m));
+                base = __shfl(base, leader);
+                if (keep) {
+                    const uint32_t slot = base + (uint32_t)__popcll(m & below);
+                    if (slot < (uint32_t)A.cap)
+                        A.s.cand[u * A.cap + slot] = make_float2(c, __int_as_float((int32_t)v));
+                }
+            }
+        }
+    }
+}
+
+// ---- per-row exact selection inside one wave.
+// Loads the row's n buffered candidates (n <= 64 * MAXE) into registers and
+// finds the K-th largest (score, then lower index) with bitwise searches.
+template <int MAXE> struct RowSel {
+    float sc[MAXE];
+    int32_t id[MAXE];
+    uint32_t key[MAXE];
+    int n;
+    uint32_t thr;      // K-th largest key
+    int32_t ithr;      // largest index kept among keys == thr
+    __device__ void load(const float2 *buf, int nn, int lane) {
+        n = nn;
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) {
+            const int i = e * 64 + lane;
+            if (i < n) {
+                const float2 x = buf[i];
+                sc[e] = x.x;
+                id[e] = __float_as_int(x.y);
+                key[e] = order_key(x.x);
+            } else {
+                sc[e] = -INFINITY;
+                id[e] = INT32_MAX;
+                key[e] = 0u;
+            }
+        }
+    }
+    __device__ static uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+        return x;
+    }
+    __device__ bool valid(int e, int lane) const { return e * 64 + lane < n; }
+    // Select K (<= n) entries.
+    __device__ void select(int K, int lane) {
+        uint32_t prefix = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = prefix | (1u << bit);
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < MAXE; ++e) c += (valid(e, lane) && key[e] >= cand) ? 1u : 0u;
+            if (wave_sum(c) >= (uint32_t)K) prefix = cand;
+        }
+        thr = prefix;
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) {
+            gt += (valid(e, lane) && key[e] > thr) ? 1u : 0u;
+            eq += (valid(e, lane) && key[e] == thr) ? 1u : 0u;
+        }
+        gt = wave_sum(gt);
+        eq = wave_sum(eq);
+        const uint32_t need = (uint32_t)K - gt;
+        if (eq == need) {
+            ithr = INT32_MAX;
+            return;
+        }
+        // largest x with #(key == thr && id < x) < need  ->  the need-th smallest id
+        uint32_t lo = 0;
+        for (int bit = 30; bit >= 0; --bit) {
+            const uint32_t cand = lo | (1u << bit);
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < MAXE; ++e)
+                c += (valid(e, lane) && key[e] == thr && (uint32_t)id[e] < cand) ? 1u : 0u;
+            if (wave_sum(c) < need) lo = cand;
+        }
+        ithr = (int32_t)lo;
+    }
+    __device__ bool kept(int e, int lane) const {
+        return valid(e, lane) && (key[e] > thr || (key[e] == thr && id[e] <= ithr));
+    }
+};
+
+template <int MAXE> __global__ __launch_bounds__(256) void compact_rows(const Args A) {
+    const int64_t u = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (u >= A.g.Np) return;
+    const uint32_t c = A.s.cnt[u];
+    if (c > (uint32_t)A.cap) {
+        if (lane == 0) A.s.over[u] = 1u;
+    }
+    const int nn = (int)min<uint32_t>(c, (uint32_t)A.cap);
+    if (nn <= A.K) return;
+    float2 *buf = A.s.cand + u * A.cap;
+    RowSel<MAXE> R;
+    R.load(buf, nn, lane);
+    R.select(A.K, lane);
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) mine += R.kept(e, lane) ? 1u : 0u;
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    uint32_t pos = incl - mine;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e)
+        if (R.kept(e, lane)) buf[pos++] = make_float2(R.sc[e], __int_as_float(R.id[e]));
+    if (lane == 0) {
+        A.s.cnt[u] = (uint32_t)A.K;
+        A.s.theta[u] = order_key_to_float(R.thr);
+    }
+}
+
+template <int MAXE> __global__ __launch_bounds__(256) void finalize_rows(const Args A) {
+    __shared__ int32_t sel[kRowWaves][1024];
+    const int wv = threadIdx.x >> 6;
+    const int64_t u = (int64_t)blockIdx.x * kRowWaves + wv;
+    const int lane = threadIdx.x & 63;
+    if (u >= A.g.Np) return;
+    if (A.s.over[u] || A.s.cnt[u] > (uint32_t)A.cap) return;  // exact per-row engine
+    const int nn = (int)A.s.cnt[u];
+    if (nn < A.K) {  // cannot happen without an overflow; recompute exactly
+        if (lane == 0) A.s.over[u] = 1u;
+        return;
+    }
+    const float2 *buf = A.s.cand + u * A.cap;
+    RowSel<MAXE> R;
+    R.load(buf, nn, lane);
+    R.select(A.K, lane);
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) mine += R.kept(e, lane) ? 1u : 0u;
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    uint32_t pos = incl - mine;
+    int32_t *s = sel[wv];
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e)
+        if (R.kept(e, lane)) s[pos++] = R.id[e];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    int32_t *out = A.idx_out + u * A.K;
+    const Geom &g = A.g;
+    for (int i = lane; i < A.K; i += 64) {
+        const int32_t v = s[i];
+        int rank = 0;
+        for (int j = 0; j < A.K; ++j) rank += s[j] < v ? 1 : 0;
+        out[rank] = (int32_t)((v / g.P) * g.T + g.ns + (v % g.P));
+    }
+}
+
+// ---- exact per-row engine: one 1024-thread block per flagged row
+template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(const Args A) {
+    __shared__ float fu[4096];
+    const Geom &g = A.g;
+    float *row = A.s.rowbuf + (int64_t)blockIdx.x * g.Np;
+    const T *F = (const T *)A.F;
+    for (int64_t u = blockIdx.x; u < g.Np; u += gridDim.x) {
+        if (!A.s.over[u]) continue;
+        __syncthreads();
+        for (int c = threadIdx.x; c < A.Df; c += 1024) fu[c] = ldf<T>(F + u * A.stride, c);
+        __syncthreads();
+        const float iu = A.s.invn[u];
+        const int64_t fr = u / g.P;
+        for (int64_t v = threadIdx.x; v < g.Np; v += 1024) {
+            float acc = 0.f;
+            const T *fv = F + v * A.stride;
+            for (int c = 0; c < A.Df; ++c) acc = fmaf(fu[c], ldf<T>(fv, c), acc);
+            // own-frame patches can never be selected: the candidate count
+            // (S-1)P is >= K, so they are given the lowest possible score
+            row[v] = (v / g.P == fr) ? -INFINITY : acc * iu * A.s.invn[v];
+        }
+        __syncthreads();
+        int32_t *out = A.idx_out + u * A.K;
+        block_topk_ascending(row, g.Np, A.K, [&](int64_t pos, int64_t v) {
+            out[pos] = (int32_t)((v / g.P) * g.T + g.ns + (v % g.P));
+        });
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+int32_t corr_capacity(const Geom &g, int32_t K) {
+    int64_t cap = std::max<int64_t>((int64_t)g.P + 2 * (int64_t)K, 8 * (int64_t)K);
+    cap = (cap + 63) / 64 * 64;
+    return (int32_t)cap;
+}
+
+size_t corr_scratch_bytes(const Geom &g, int32_t K, int32_t cap) {
+    (void)K;
+    const int64_t Np = g.Np;
+    return align256(sizeof(float) * Np) * 2 + align256(sizeof(uint32_t) * Np) * 2 +
+           align256(sizeof(float2) * (size_t)Np * cap) + align256(sizeof(float) * (size_t)kFallbackBlocks * Np);
+}
+
+hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
+    Args A{};
+    A.g = B.g;
+    A.F = B.dino;
+    A.stride = B.row_stride;
+    A.Df = B.Df;
+    A.K = B.K;
+    A.cap = B.cap;
+    A.idx_out = B.idx_out;
+    const bool gemm = B.dino_dtype == BF16 && (B.Df % GK) == 0 && B.cap <= 64 * 64 && B.K <= 1024;
+    A.all_rows_fallback = gemm ? 0 : 1;
+    A.s = carve(B.scratch, B.g.Np, B.cap);
+    const int64_t Np = B.g.Np;
+    const unsigned rb = (unsigned)((Np + 3) / 4);
+    if (B.dino_dtype == BF16)
+        hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
+    else
+        hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
+    if (gemm) {
+        const unsigned row_tiles = (unsigned)((Np + GT - 1) / GT);
+        int64_t lo = 0, hi = B.g.P;
+        while (lo < Np) {
+            hi = std::min<int64_t>(hi, Np);
+            A.col_lo = lo;
+            A.col_hi = hi;
+            const unsigned col_tiles = (unsigned)((hi - lo + GT - 1) / GT);
+            hipLaunchKernelGGL(cos_phase, dim3(col_tiles, row_tiles), dim3(256), 0, stream, A);
+            const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
+            if (A.cap <= 16 * 64)
+                hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A);
+            else if (A.cap <= 32 * 64)
+                hipLaunchKernelGGL(compact_rows<32>, dim3(cb), dim3(256), 0, stream, A);
+            else
+                hipLaunchKernelGGL(compact_rows<64>, dim3(cb), dim3(256), 0, stream, A);
+            lo = hi;
+            hi = 2 * hi;
+        }
+        const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
+        if (A.cap <= 16 * 64)
+            hipLaunchKernelGGL(finalize_rows<16>, dim3(cb), dim3(256), 0, stream, A);
+        else if (A.cap <= 32 * 64)
+            hipLaunchKernelGGL(finalize_rows<32>, dim3(cb), dim3(256), 0, stream, A);
+        else
+            hipLaunchKernelGGL(finalize_rows<64>, dim3(cb), dim3(256), 0, stream, A);
+    }
+    const unsigned fb = (unsigned)std::min<int64_t>(kFallbackBlocks, Np);
+    if (B.dino_dtype == BF16)
+        hipLaunchKernelGGL(fallback_rows<uint16_t>, dim3(fb), dim3(1024), 0, stream, A);
+    else
+        hipLaunchKernelGGL(fallback_rows<float>, dim3(fb), dim3(1024), 0, stream, A);
+    return hipGetLastError();
+}
+
+}  // namespace saf

@@ -1,0 +1,106 @@
+// Internal declarations shared by the host API (api.cpp) and the HIP kernels.
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saf {
+
+enum Role : int32_t { POSITION = 0, VERTICAL = 1, CORRESPONDENCE = 2, SCANNING = 3, DENSE = 4 };
+enum Dtype : int32_t { F32 = 0, BF16 = 1 };
+
+// Geometry with derived sizes.  Token j = f * T + t; special iff t < ns.
+struct Geom {
+    int32_t S, ns, P, T, H, d;
+    int64_t N, Np;
+    int32_t dtype;
+};
+
+// Query rows a piece of work covers:
+//   FRAME    -- rows f*T .. f*T+T-1 for every frame f (position heads: the key
+//               set depends on the query frame, so tiles never cross frames)
+//   ALL      -- rows 0 .. N-1
+//   SPECIALS -- the ns*S special-token rows, m -> (m / ns) * T + m % ns
+enum RowSpace : int32_t { ROWS_FRAME = 0, ROWS_ALL = 1, ROWS_SPECIALS = 2 };
+
+// One head's key-set description as the attention kernels see it.
+//   POSITION: specials (ns*S) ++ anchor-frame patches (P) ++ own-frame
+//             patches (P, only when the query frame is not the anchor)
+//   SCANNING: tokens m*stride for m < ceil(N/stride) ++ specials, where a
+//             special that already lies on the stride is a masked slot
+//   VERTICAL: list[0 .. list_len)
+//   DENSE:    every token (also the special rows of correspondence heads)
+struct HeadWork {
+    int32_t head;       // head index (pointer offsets)
+    int32_t role;       // key-set rule, see above
+    int32_t budget;     // stride for SCANNING
+    int32_t anchor;     // anchor frame for POSITION
+    int32_t rows;       // RowSpace
+    int32_t list_len;   // VERTICAL
+    int32_t nsplit;     // key splits per query tile (1 = no split)
+    int32_t block0;     // first work-group of this head in the launch
+    const int32_t *list;// VERTICAL key list (device, ascending)
+    float *part;        // split partials (nsplit > 1): [tiles*QT rows][nsplit] x (m, l, o[64])
+};
+
+constexpr int kMaxWork = 24;
+
+struct MfmaLaunch {
+    Geom g;
+    const void *q, *k, *v;
+    void *o;
+    int64_t head_stride, token_stride;
+    int32_t nwork;
+    int32_t total_blocks;
+    HeadWork work[kMaxWork];
+};
+
+// VALU row kernel: one wave per query row, looping over every listed head.
+//   rows = ROWS_ALL: every token row; rows = patch rows only when
+//   patch_rows_only (correspondence heads of the bf16 path).
+struct ValuLaunch {
+    Geom g;
+    const void *q, *k, *v;
+    void *o;
+    int64_t head_stride, token_stride;
+    const int32_t *corr_idx;   // [Np, corr_k] global token ids
+    int32_t corr_k;
+    int32_t patch_rows_only;
+    int32_t nwork;
+    HeadWork work[kMaxWork];
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns the hipError_t of its launch.
+hipError_t launch_mfma_attention(const MfmaLaunch &L, hipStream_t stream);
+hipError_t launch_split_combine(const MfmaLaunch &L, hipStream_t stream);
+hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t stream);
+
+// Vertical probe: qbar (fp32) of one head, probe scores, exact top-K.
+//   ws layout per head: partial sums [kProbeBlocks][64] f32, qbar [64] f32,
+//   scores [N] f32, histogram/scratch [kTopkScratch] u32.
+constexpr int kProbeBlocks = 256;
+constexpr int kTopkScratch = 4096;
+size_t vertical_ws_bytes(int64_t N);
+hipError_t launch_vertical_index(const Geom &g, const void *q, const void *k, int64_t head_stride,
+                                 int64_t token_stride, int32_t head, int32_t K, int32_t *idx_out,
+                                 void *ws, hipStream_t stream);
+
+// Correspondence index build (cosine top-K over other frames).
+struct CorrBuild {
+    Geom g;
+    const void *dino;
+    int32_t dino_dtype;
+    int32_t Df;
+    int64_t row_stride;
+    int32_t K;      // kept per row (already clamped)
+    int32_t cap;    // candidate capacity per row
+    int32_t *idx_out;   // [Np, K]
+    void *scratch;      // corr_scratch_bytes()
+};
+size_t corr_scratch_bytes(const Geom &g, int32_t K, int32_t cap);
+int32_t corr_capacity(const Geom &g, int32_t K);
+hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream);
+
+}  // namespace saf

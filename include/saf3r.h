@@ -1,0 +1,184 @@
+/*
+ * saf3r.h -- C ABI of the MI355X (gfx950) head-wise dynamic sparse global
+ * attention library (libsaf3r.so).
+ *
+ * The operation is the one described in "SAF3R: Dynamic Sparse Attention for
+ * Feed-Forward 3D Reconstruction Transformers" (arXiv 2607.03612): every head
+ * of a cross-view global attention layer is given a role, each role selects
+ * a key/value set per query, and attention is computed exactly over that set
+ * (softmax over the selected logits, scale 1/sqrt(d)):
+ *
+ *   O[h, i] = sum_{j in K_h(i)} softmax_j(q_i . k_j / sqrt(d)) v_j
+ *
+ * Roles (Sec. 3 Observation #2; Sec. 4.1 "Tailored Sparse Attention Kernels"):
+ *   SAF_POSITION       static set: every special token, every token of the
+ *                      anchor frame and every token of the query's own frame.
+ *   SAF_VERTICAL       one set shared by all queries: the top-`budget` keys of
+ *                      the mean-query probe qbar K^T / sqrt(d), where qbar is
+ *                      the mean of all N queries (Sec. 4.3, "Query-Probe
+ *                      Top-K Kernel").  Ties go to the lower token index.
+ *   SAF_CORRESPONDENCE per-query set: the cached DINO cosine top-K of the
+ *                      query's patch against the patches of the other frames
+ *                      (Sec. 4.1 "DINO Top-K Kernel", Sec. 4.3).  Special
+ *                      tokens carry no DINO feature; their queries attend to
+ *                      every key.
+ *   SAF_SCANNING       keys on a fixed stride `budget` of the global token
+ *                      index (phase 0) plus every special token (Sec. 4.1
+ *                      "Uniform Sampling Kernel").
+ *   SAF_DENSE          every key (full global attention).
+ *
+ * Token layout: frame f holds T = ns + P tokens, the ns special tokens
+ * (camera, registers) first, then P patch tokens; token j = f * T + t.  Patch
+ * number u = f * P + p is token f * T + ns + p.  Key sets are sets: a token
+ * is never counted twice.
+ *
+ * Conventions for every call:
+ *   - Pointers named dev_* / q / k / v / o / ws / dino are device pointers;
+ *     the caller owns them.  The context owns only the correspondence index
+ *     cache and small internal buffers.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns without waiting.  Argument errors are detected on the
+ *     host, before anything is enqueued, and returned synchronously; faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - No call throws.  On error the status is returned and a message is kept
+ *     in the context (saf_last_error).  A context is not thread-safe; separate
+ *     contexts are independent.
+ *   - Q, K, V and O share one element type (geometry.dtype) and one layout:
+ *     element (h, j, c) sits at h * head_stride + j * token_stride + c, with
+ *     the d channels contiguous.  [H, N, d] and [N, H, d] are both covered.
+ *     Rows must be 16-byte aligned (head_stride, token_stride multiples of 8
+ *     for bf16 and 4 for fp32; base pointers 16-byte aligned).
+ *   - head_dim must be 64.
+ */
+#ifndef SAF3R_H
+#define SAF3R_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SAF_OK = 0,
+    SAF_EINVAL = -1,        /* bad argument (null pointer, size, role, budget, layout) */
+    SAF_ENOMEM = -2,        /* device or host allocation failed */
+    SAF_EHIP = -3,          /* the HIP runtime reported an error */
+    SAF_EUNSUPPORTED = -4,  /* valid request outside what this build implements */
+    SAF_ESTATE = -5         /* call out of order (e.g. no correspondence index yet) */
+} saf_status_t;
+
+typedef enum { SAF_F32 = 0, SAF_BF16 = 1 } saf_dtype_t;
+
+typedef enum {
+    SAF_POSITION = 0,
+    SAF_VERTICAL = 1,
+    SAF_CORRESPONDENCE = 2,
+    SAF_SCANNING = 3,
+    SAF_DENSE = 4
+} saf_role_t;
+
+/* Correspondence top-K per query: over all other frames together, or K per
+ * other frame. */
+typedef enum { SAF_CORR_TOTAL = 0, SAF_CORR_PER_FRAME = 1 } saf_corr_mode_t;
+
+typedef struct {
+    int32_t num_frames;          /* S >= 1 */
+    int32_t specials_per_frame;  /* ns >= 0 (5 for VGGT: 1 camera + 4 register) */
+    int32_t patches_per_frame;   /* P >= 1 */
+    int32_t num_heads;           /* H, 1..64 */
+    int32_t head_dim;            /* d, must be 64 */
+    int32_t dtype;               /* saf_dtype_t of Q, K, V, O */
+} saf_geometry_t;
+
+typedef struct {
+    int64_t head_stride;   /* elements between heads */
+    int64_t token_stride;  /* elements between tokens */
+} saf_layout_t;
+
+typedef struct {
+    int32_t role;          /* saf_role_t */
+    int32_t budget;        /* VERTICAL: K >= 1 (clamped to N); SCANNING: stride >= 1;
+                              CORRESPONDENCE: 0 or the cached index's K; others: 0 */
+    int32_t anchor_frame;  /* POSITION: anchor frame in [0, S); others ignored */
+    int32_t flags;         /* must be 0 */
+} saf_head_plan_t;
+
+typedef struct saf_ctx saf_ctx_t;
+
+/* Create a context for one geometry.  Touches no device.  *out receives the
+ * context; NULL on failure.  Errors: SAF_EINVAL (bad geometry),
+ * SAF_EUNSUPPORTED (head_dim != 64), SAF_ENOMEM. */
+saf_status_t saf_create(const saf_geometry_t *geometry, saf_ctx_t **out);
+
+/* Release the context and its device memory (waits for the device). NULL ok. */
+void saf_destroy(saf_ctx_t *ctx);
+
+/* Message of the last failing call on this context ("" if none).  Valid until
+ * the next call on the context.  With ctx == NULL: the last saf_create error. */
+const char *saf_last_error(const saf_ctx_t *ctx);
+
+/* Bytes of device workspace that saf_sparse_attention / saf_dense_attention /
+ * saf_build_vertical_index need for this plan (plan: H entries, host memory;
+ * NULL = the dense call).  The workspace needs no initialisation. */
+saf_status_t saf_workspace_size(const saf_ctx_t *ctx, const saf_head_plan_t *plan, size_t *bytes);
+
+/* Build the correspondence index (Sec. 4.3, "DINO Top-K Kernel") from DINO
+ * features of the S*P patches (row u = patch number u, Df channels contiguous,
+ * rows dino_row_stride elements apart, dtype dino_dtype).  For every patch u:
+ * cosine c_uv = f_u.f_v / (|f_u||f_v|) (0 when a norm is 0) against the
+ * patches v of the other frames; the first K by (c desc, token asc) (TOTAL;
+ * clamped to (S-1)P) are stored as global token indices, ascending.  The
+ * index is kept in the context and reused by every later
+ * saf_sparse_attention call (the cache of Sec. 4.3) until rebuilt.
+ * Errors: SAF_EINVAL (S < 2, K < 1, Df < 1, bad stride/pointer),
+ * SAF_EUNSUPPORTED (PER_FRAME mode, Df not a multiple of 32), SAF_ENOMEM. */
+saf_status_t saf_build_corr_index(saf_ctx_t *ctx, const void *dino, int32_t dino_dtype,
+                                  int32_t Df, int64_t dino_row_stride, int32_t K,
+                                  int32_t mode, void *stream);
+
+/* Replace the cached index with caller data: dev_idx holds S*P rows of Kc
+ * global token indices (int32, device memory), each row a set of distinct
+ * patch tokens of other frames.  The data is copied (stream-ordered).
+ * Errors: SAF_EINVAL (S < 2, Kc < 1, Kc > (S-1)P, null pointer), SAF_ENOMEM. */
+saf_status_t saf_set_corr_index(saf_ctx_t *ctx, const int32_t *dev_idx, int32_t Kc, void *stream);
+
+/* Copy the cached index ([S*P, Kc] int32, rows ascending) to dev_out (may be
+ * NULL to query Kc only).  Errors: SAF_ESTATE (no index), SAF_EINVAL. */
+saf_status_t saf_get_corr_index(const saf_ctx_t *ctx, int32_t *dev_out, int32_t *Kc, void *stream);
+
+/* Vertical-line key set of one head (Sec. 4.3): qbar = mean of the N query
+ * rows of head `head` (fp32), r_j = qbar . k_j / sqrt(d) (fp32), the top
+ * min(K, N) by (r desc, j asc), written ascending to dev_idx_out (int32).
+ * ws: workspace of at least saf_workspace_size() for a plan holding this
+ * head as VERTICAL with budget K.  Errors: SAF_EINVAL. */
+saf_status_t saf_build_vertical_index(saf_ctx_t *ctx, const void *q, const void *k,
+                                      saf_layout_t layout, int32_t head, int32_t K,
+                                      int32_t *dev_idx_out, void *ws, size_t ws_bytes,
+                                      void *stream);
+
+/* One sparse global-attention layer: every head h by plan[h] (H entries, host
+ * memory).  Vertical heads build their key set in this call unless vert_idx
+ * is given: then vert_idx + h * vert_ld holds head h's min(K, N) key indices
+ * (int32, device, ascending) for every vertical head h.  Correspondence heads
+ * use the cached index.  O gets the input element type.
+ * Errors: SAF_EINVAL (bad plan/layout/pointer, workspace too small),
+ * SAF_ESTATE (a correspondence head and no cached index, or a budget that
+ * differs from the index's K), SAF_EHIP. */
+saf_status_t saf_sparse_attention(saf_ctx_t *ctx, const saf_head_plan_t *plan, const void *q,
+                                  const void *k, const void *v, void *o, saf_layout_t layout,
+                                  const int32_t *vert_idx, int64_t vert_ld, void *ws,
+                                  size_t ws_bytes, void *stream);
+
+/* Dense global attention over every key (the speedup baseline), all heads.
+ * Errors: SAF_EINVAL, SAF_EHIP. */
+saf_status_t saf_dense_attention(saf_ctx_t *ctx, const void *q, const void *k, const void *v,
+                                 void *o, saf_layout_t layout, void *ws, size_t ws_bytes,
+                                 void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAF3R_H */
