@@ -65,6 +65,9 @@ _PROTOS = {
     "saf_build_vertical_index": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _VP, _VP, _SZ, _VP]),
     "saf_sparse_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _I64, _VP, _SZ, _VP]),
     "saf_dense_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _SZ, _VP]),
+    "saf_set_kernel_timing": (C.c_int, [_VP, _I32]),
+    "saf_read_kernel_timing": (C.c_int, [_VP, _I32, C.POINTER(C.c_char_p), C.POINTER(C.c_float),
+                                         C.POINTER(_I32)]),
 }
 
 
@@ -127,6 +130,14 @@ def saf_sparse_attention(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, ws, w
 
 def saf_dense_attention(ctx, q, k, v, o, layout, ws, ws_bytes, stream) -> int:
     return lib().saf_dense_attention(ctx, q, k, v, o, layout, ws, ws_bytes, stream)
+
+
+def saf_set_kernel_timing(ctx, enable) -> int:
+    return lib().saf_set_kernel_timing(ctx, enable)
+
+
+def saf_read_kernel_timing(ctx, max_entries, names, ms, count: C.c_int32) -> int:
+    return lib().saf_read_kernel_timing(ctx, max_entries, names, ms, C.byref(count))
 
 
 # ---------------------------------------------------------------------------
@@ -249,6 +260,17 @@ class Context:
                                          C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), lay, vptr, vld,
                                          C.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
         return o
+
+    def set_kernel_timing(self, enable: bool = True):
+        self._check(saf_set_kernel_timing(self._ctx, 1 if enable else 0))
+
+    def read_kernel_timing(self, max_entries: int = 4096):
+        """[(launch group name, ms)] recorded since the last read (after a sync)."""
+        names = (C.c_char_p * max_entries)()
+        ms = (C.c_float * max_entries)()
+        cnt = C.c_int32()
+        self._check(saf_read_kernel_timing(self._ctx, max_entries, names, ms, cnt))
+        return [(names[i].decode(), float(ms[i])) for i in range(min(cnt.value, max_entries))]
 
     def dense_attention(self, q, k, v, o=None, stream=None) -> torch.Tensor:
         lay = self.layout_of(q)

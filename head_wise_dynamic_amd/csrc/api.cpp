@@ -25,7 +25,48 @@ struct saf_ctx {
     size_t corr_bytes = 0;
     void *corr_scratch = nullptr;
     size_t corr_scratch_bytes = 0;
+    // per-launch timing
+    bool timing = false;
+    struct Rec {
+        const char *name;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;
 };
+
+namespace {
+
+// Brackets one launch group with events when the context records timings.
+struct Timed {
+    saf_ctx *c;
+    hipStream_t s;
+    const char *name;
+    hipEvent_t a = nullptr, b = nullptr;
+    Timed(saf_ctx *c_, hipStream_t s_, const char *n) : c(c_), s(s_), name(n) {
+        if (!c->timing) return;
+        a = take();
+        b = take();
+        if (a && b) (void)hipEventRecord(a, s);
+    }
+    hipEvent_t take() {
+        hipEvent_t e = nullptr;
+        if (!c->pool.empty()) {
+            e = c->pool.back();
+            c->pool.pop_back();
+        } else if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+        }
+        return e;
+    }
+    ~Timed() {
+        if (!c->timing || !a || !b) return;
+        (void)hipEventRecord(b, s);
+        c->recs.push_back({name, a, b});
+    }
+};
+
+}  // namespace
 
 namespace {
 
@@ -173,6 +214,11 @@ saf_status_t saf_create(const saf_geometry_t *geom, saf_ctx_t **out) {
 
 void saf_destroy(saf_ctx_t *c) {
     if (!c) return;
+    for (auto &r : c->recs) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
     if (c->corr_idx || c->corr_scratch) {
         (void)hipDeviceSynchronize();
         if (c->corr_idx) (void)hipFree(c->corr_idx);
@@ -264,7 +310,11 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     B.cap = cap;
     B.idx_out = c->corr_idx;
     B.scratch = c->corr_scratch;
-    hipError_t e = saf::launch_corr_build(B, as_stream(stream));
+    hipError_t e;
+    {
+        Timed tm(c, as_stream(stream), "corr_index");
+        e = saf::launch_corr_build(B, as_stream(stream));
+    }
     if (e != hipSuccess) return hip_fail(c, e, "correspondence index kernels");
     c->corr_k = Kc;
     return SAF_OK;
@@ -307,8 +357,12 @@ saf_status_t saf_build_vertical_index(saf_ctx_t *c, const void *q, const void *k
     if (!aligned16(q) || !aligned16(k)) return fail(c, SAF_EINVAL, "q/k must be 16-byte aligned");
     const size_t need = saf::vertical_ws_bytes(c->g.N);
     if (ws_bytes < need) return fail(c, SAF_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
-    hipError_t e = saf::launch_vertical_index(c->g, q, k, lay.head_stride, lay.token_stride, head, K,
-                                              dev_idx_out, ws, as_stream(stream));
+    hipError_t e;
+    {
+        Timed tm(c, as_stream(stream), "vertical_index");
+        e = saf::launch_vertical_index(c->g, q, k, lay.head_stride, lay.token_stride, head, K, dev_idx_out, ws,
+                                       as_stream(stream));
+    }
     if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
     return SAF_OK;
 }
@@ -355,8 +409,12 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         wp += align256(sizeof(int32_t) * g.N);
         void *vws = wp;
         wp += align256(saf::vertical_ws_bytes(g.N));
-        hipError_t e = saf::launch_vertical_index(g, q, k, lay.head_stride, lay.token_stride, h,
-                                                  plan[h].budget, idx, vws, s);
+        hipError_t e;
+        {
+            Timed tm(c, s, "vertical_index");
+            e = saf::launch_vertical_index(g, q, k, lay.head_stride, lay.token_stride, h, plan[h].budget, idx,
+                                           vws, s);
+        }
         if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
         vlist[h] = idx;
     }
@@ -387,7 +445,11 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
                 w.list_len = plan[h].role == SAF_VERTICAL ? (int32_t)std::min<int64_t>(plan[h].budget, g.N) : 0;
                 w.nsplit = 1;
             }
-            hipError_t e = saf::launch_valu_attention(L, g.N, s);
+            hipError_t e;
+            {
+                Timed tm(c, s, "valu_attention");
+                e = saf::launch_valu_attention(L, g.N, s);
+            }
             if (e != hipSuccess) return hip_fail(c, e, "attention kernel (fp32)");
         }
         return SAF_OK;
@@ -469,9 +531,16 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         }
         if (blocks >= ((int64_t)1 << 31)) return fail(c, SAF_EINVAL, "launch too large");
         M.total_blocks = (int32_t)blocks;
-        hipError_t e = saf::launch_mfma_attention(M, s);
+        hipError_t e;
+        {
+            Timed tm(c, s, "shared_attention");
+            e = saf::launch_mfma_attention(M, s);
+        }
         if (e != hipSuccess) return hip_fail(c, e, "matrix-core attention kernel");
-        e = saf::launch_split_combine(M, s);
+        {
+            Timed tm(c, s, "split_combine");
+            e = saf::launch_split_combine(M, s);
+        }
         if (e != hipSuccess) return hip_fail(c, e, "split combine kernel");
     }
 
@@ -492,7 +561,11 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         for (int h = 0; h < g.H; ++h) {
             if (plan[h].role != SAF_CORRESPONDENCE) continue;
             if (L.nwork == saf::kMaxWork) {
-                hipError_t e = saf::launch_valu_attention(L, g.Np, s);
+                hipError_t e;
+                {
+                    Timed tm(c, s, "gather_attention");
+                    e = saf::launch_valu_attention(L, g.Np, s);
+                }
                 if (e != hipSuccess) return hip_fail(c, e, "gather attention kernel");
                 L.nwork = 0;
             }
@@ -502,7 +575,11 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
             w.role = SAF_CORRESPONDENCE;
             w.nsplit = 1;
         }
-        hipError_t e = saf::launch_valu_attention(L, g.Np, s);
+        hipError_t e;
+        {
+            Timed tm(c, s, "gather_attention");
+            e = saf::launch_valu_attention(L, g.Np, s);
+        }
         if (e != hipSuccess) return hip_fail(c, e, "gather attention kernel");
     }
     return SAF_OK;
@@ -536,7 +613,11 @@ saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, con
                 w.role = saf::DENSE;
                 w.nsplit = 1;
             }
-            hipError_t e = saf::launch_valu_attention(L, g.N, s);
+            hipError_t e;
+            {
+                Timed tm(c, s, "dense_attention");
+                e = saf::launch_valu_attention(L, g.N, s);
+            }
             if (e != hipSuccess) return hip_fail(c, e, "dense attention kernel (fp32)");
         }
         return SAF_OK;
@@ -564,10 +645,42 @@ saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, con
             M.work[M.nwork++] = w;
         }
         M.total_blocks = (int32_t)blocks;
-        hipError_t e = saf::launch_mfma_attention(M, s);
+        hipError_t e;
+        {
+            Timed tm(c, s, "dense_attention");
+            e = saf::launch_mfma_attention(M, s);
+        }
         if (e != hipSuccess) return hip_fail(c, e, "dense attention kernel");
     }
     return SAF_OK;
+}
+
+saf_status_t saf_set_kernel_timing(saf_ctx_t *c, int32_t enable) {
+    if (!c) return SAF_EINVAL;
+    c->timing = enable != 0;
+    return SAF_OK;
+}
+
+saf_status_t saf_read_kernel_timing(saf_ctx_t *c, int32_t max, const char **names, float *ms, int32_t *count) {
+    if (!c || !count) return SAF_EINVAL;
+    if (max > 0 && (!names || !ms)) return fail(c, SAF_EINVAL, "null names/ms with max > 0");
+    saf_status_t st = SAF_OK;
+    int32_t i = 0;
+    for (auto &r : c->recs) {
+        if (i < max) {
+            float t = 0.f;
+            hipError_t e = hipEventElapsedTime(&t, r.a, r.b);
+            if (e != hipSuccess && st == SAF_OK) st = hip_fail(c, e, "hipEventElapsedTime");
+            names[i] = r.name;
+            ms[i] = t;
+        }
+        ++i;
+        c->pool.push_back(r.a);
+        c->pool.push_back(r.b);
+    }
+    c->recs.clear();
+    *count = i;
+    return st;
 }
 
 }  // extern "C"

@@ -177,6 +177,21 @@ saf_status_t saf_dense_attention(saf_ctx_t *ctx, const void *q, const void *k, c
                                  void *o, saf_layout_t layout, void *ws, size_t ws_bytes,
                                  void *stream);
 
+/* Per-launch timing (tracing).  With enable != 0 every kernel launch group
+ * the context enqueues (one entry per group: "shared_attention",
+ * "gather_attention", "split_combine", "vertical_index", "corr_index",
+ * "dense_attention") is bracketed by two HIP events on the call's stream.
+ * Timing adds two event records per launch group and nothing else; it is
+ * off by default.  Errors: SAF_EINVAL. */
+saf_status_t saf_set_kernel_timing(saf_ctx_t *ctx, int32_t enable);
+
+/* Read and clear the recorded launches.  Call after the streams involved
+ * have been synchronised.  Writes up to max entries (names: static strings,
+ * ms: elapsed milliseconds) and the total number recorded to *count.
+ * Errors: SAF_EINVAL (null ctx/count), SAF_EHIP (an event is not complete). */
+saf_status_t saf_read_kernel_timing(saf_ctx_t *ctx, int32_t max, const char **names, float *ms,
+                                    int32_t *count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,8 @@ def lib():
         L = C.CDLL(_LIB)
         P = C.c_void_p
         i32, i64, dbl = C.c_int32, C.c_int64, C.c_double
+        L.oracle_num_threads.restype = C.c_int
+        L.oracle_num_threads.argtypes = []
         L.oracle_position_set.restype = i64
         L.oracle_position_set.argtypes = [i32, i32, i32, i32, i32, P]
         L.oracle_scan_set.restype = i64
@@ -95,6 +97,10 @@ def _p(a: Optional[np.ndarray]):
 
 def _i64(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 # ---------------------------------------------------------------------------

@@ -21,12 +21,16 @@
  * Element type codes: 0 = float32, 1 = bfloat16 (raw 16-bit patterns).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+
+/* Threads the OpenMP loops below use (reported with CPU timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 static double load_elem(const void *base, int dtype, int64_t i)
 {
