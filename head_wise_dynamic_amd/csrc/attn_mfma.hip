@@ -119,20 +119,22 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-    // ---- tile loader: thread handles chunks tid and tid+256 (row = c>>3, seg = c&7)
+    // ---- tile loader: thread handles key rows 2p and 2p+1 (p = tid / 8) at
+    // channel segment seg = tid % 8, so V^T can be written two keys per
+    // 32-bit LDS store
     u32x4 kreg[2], vreg[2];
     bool kval[2];
+    const int lp = tid >> 3, lseg = tid & 7;
     auto load_tile = [&](int64_t kt) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
-            const int64_t m = kt + row;
+            const int64_t m = kt + 2 * lp + i;
             int64_t tok = -1;
             if (m < kend) tok = key_token(w, g, m, rm.qframe);
             kval[i] = tok >= 0;
             if (tok >= 0) {
-                kreg[i] = *(const u32x4 *)(K + tok * ts + 8 * seg);
-                vreg[i] = *(const u32x4 *)(V + tok * ts + 8 * seg);
+                kreg[i] = *(const u32x4 *)(K + tok * ts + 8 * lseg);
+                vreg[i] = *(const u32x4 *)(V + tok * ts + 8 * lseg);
             } else {
                 kreg[i] = u32x4{0u, 0u, 0u, 0u};
                 vreg[i] = u32x4{0u, 0u, 0u, 0u};
@@ -141,16 +143,17 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
-            *(u32x4 *)(&Ks[buf][row * KROW + 8 * seg]) = kreg[i];
-            uint16_t *vt = &Vt[buf][(8 * seg) * VROW + row];
+        for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * lseg]) = kreg[i];
+        uint32_t *vt = (uint32_t *)&Vt[buf][(8 * lseg) * VROW + 2 * lp];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vt[(2 * e) * VROW] = (uint16_t)(vreg[i][e] & 0xFFFFu);
-                vt[(2 * e + 1) * VROW] = (uint16_t)(vreg[i][e] >> 16);
-            }
-            if (seg == 0) kbias[buf][row] = kval[i] ? 0.f : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+            // channels 2e and 2e+1 of the two keys
+            vt[(2 * e) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[1][e], vreg[0][e], 0x05040100u);
+            vt[(2 * e + 1) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[1][e], vreg[0][e], 0x07060302u);
+        }
+        if (lseg == 0) {
+            kbias[buf][2 * lp] = kval[0] ? 0.f : -INFINITY;
+            kbias[buf][2 * lp + 1] = kval[1] ? 0.f : -INFINITY;
         }
     };
 
@@ -187,31 +190,36 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
                 for (int r = 0; r < 16; ++r)
                     s[bb][r] += kbias[buf][32 * bb + 16 * (r >> 3) + 8 * gq + (r & 7)];
         }
-        // online softmax (log2 domain)
+        // online softmax (log2 domain).  The running max is only raised when
+        // a logit exceeds it by more than 8 (weights stay <= 2^8), so the
+        // O rescale is skipped on most tiles.
         float mx = s[0][0];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * sc);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+        if (__any(mx > m_run + 8.f)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float lsum = 0.f;
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(fmaf(s[bb][r], sc, -m_use));
+                const float p = fast_exp2(fmaf(s[bb][r], sc, -m_use));
                 s[bb][r] = p;
                 lsum += p;
             }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        l_run += lsum;
 
         // O^T += V^T P^T, four k-steps of 16 keys
 #pragma unroll
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const MfmaLaunch L) 
             const float Mu = (M == -INFINITY) ? 0.f : M;
             float l = 0.f, o = 0.f;
             for (int s = 0; s < w.nsplit; ++s) {
-                const float f = exp2f(rec[s * PSTRIDE] - Mu);
+                const float f = fast_exp2(rec[s * PSTRIDE] - Mu);
                 l += rec[s * PSTRIDE + 1] * f;
                 o += rec[s * PSTRIDE + 2 + lane] * f;
             }

@@ -102,11 +102,11 @@ __device__ void attend_row(const ValuLaunch &L, const HeadWork &w, int64_t qtok,
         for (int x = LPR; x < 64; x <<= 1) cm = fmaxf(cm, __shfl_xor(cm, x));
         if (cm == -INFINITY) continue;  // wave-uniform: every slot masked
         const float m_new = fmaxf(m_run, cm);
-        const float alpha = exp2f(m_run - m_new);
+        const float alpha = fast_exp2(m_run - m_new);
         float lsum = 0.f;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            s[p] = exp2f(s[p] - m_new);
+            s[p] = fast_exp2(s[p] - m_new);
             lsum += s[p];
         }
         l_run = l_run * alpha + lsum;

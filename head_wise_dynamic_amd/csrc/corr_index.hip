@@ -29,9 +29,6 @@
 namespace saf {
 namespace {
 
-constexpr int GT = 128;       // GEMM tile (rows and columns)
-constexpr int GK = 32;        // k per LDS stage
-constexpr int GROW = GK + 8;  // padded LDS row (bf16)
 constexpr int kRowWaves = 4;  // rows per block in the per-row wave kernels
 constexpr int kFallbackBlocks = 256;
 
@@ -101,35 +98,80 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
     }
 }
 
-// ---- one phase of the cosine GEMM with threshold filtering
-// grid (col tiles of the phase, row tiles), 256 threads = 2 x 2 waves of 64 x 64
-__global__ __launch_bounds__(256) void cos_phase(const Args A) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][GT * GROW];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GT * GROW];
-    __shared__ float r_invn[GT], r_theta[GT];
-    __shared__ int32_t r_frame[GT];
+// ---- one phase of the cosine GEMM with threshold filtering.
+// Tile 256 x 256 per work-group of 4 waves (2 x 2); each wave owns 128 x 128
+// as 4 x 4 blocks of 32 x 32 (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
+// Channels are staged through LDS 64 at a time, double buffered, with the
+// next stage prefetched into registers while the current one is multiplied.
+// Work-groups are mapped XCD by XCD (blockIdx % 8 selects the XCD): each XCD
+// sweeps a contiguous, row-grouped range of tiles so that its L2 serves the
+// operand panels its work-groups share.
+constexpr int CT = 256;
+constexpr int CK = 64;
+constexpr int CROW = CK + 8;   // padded LDS row: 144 B, conflict-free 16-byte reads
+constexpr int kGroupRows = 4;  // row tiles per group in the tile order
+
+__global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][CT * CROW];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][CT * CROW];
+    __shared__ float r_thr[CT], r_iu[CT];
+    __shared__ int32_t r_frame[CT];
 
     const Geom &g = A.g;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 1, wc = wave & 1;
     const int n = lane & 31, gq = lane >> 5;
-    const int64_t row0 = (int64_t)blockIdx.y * GT;
-    const int64_t col0 = A.col_lo + (int64_t)blockIdx.x * GT;
+
+    // ---- tile of this work-group
+    const int nrow = (int)((g.Np + CT - 1) / CT);
+    const int ncol = (int)((A.col_hi - A.col_lo + CT - 1) / CT);
+    const int total = nrow * ncol;
+    const int per_xcd = (total + 7) / 8;
+    const int tix = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (tix >= total) return;
+    const int gsize = kGroupRows * ncol;
+    const int grp = tix / gsize, rem = tix % gsize;
+    const int rows_in_grp = min(kGroupRows, nrow - grp * kGroupRows);
+    const int rt = grp * kGroupRows + rem % rows_in_grp;
+    const int ct = rem / rows_in_grp;
+    const int64_t row0 = (int64_t)rt * CT;
+    const int64_t col0 = A.col_lo + (int64_t)ct * CT;
     const uint16_t *F = (const uint16_t *)A.F;
 
-    if (tid < GT) {
+    // row thresholds in units of acc * inv|f_v|, lowered by 2^-20 relative so
+    // that the filter never drops a value the exact comparison would keep
+    {
         const int64_t u = row0 + tid;
-        r_invn[tid] = u < g.Np ? A.s.invn[u] : 0.f;
-        r_theta[tid] = u < g.Np ? A.s.theta[u] : INFINITY;
-        r_frame[tid] = u < g.Np ? (int32_t)(u / g.P) : -1;
+        float thr = INFINITY, iu = 0.f;
+        int32_t fr = -1;
+        if (u < g.Np) {
+            const float th = A.s.theta[u];
+            iu = A.s.invn[u];
+            fr = (int32_t)(u / g.P);
+            if (th == -INFINITY) {
+                thr = -INFINITY;
+            } else if (iu > 0.f) {
+                const float t = th / iu;
+                thr = t > 0.f ? t * (1.f - 0x1p-20f) : (t < 0.f ? t * (1.f + 0x1p-20f) : -1e-30f);
+            } else {
+                thr = th <= 0.f ? -INFINITY : INFINITY;
+            }
+        }
+        r_thr[tid] = thr;
+        r_iu[tid] = iu;
+        r_frame[tid] = fr;
     }
+    const int32_t f_row_lo = (int32_t)(row0 / g.P);
+    const int32_t f_row_hi = (int32_t)((min<int64_t>(row0 + CT, g.Np) - 1) / g.P);
+    const int32_t f_col_lo = (int32_t)(col0 / g.P);
+    const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, A.col_hi) - 1) / g.P);
+    const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
-    // loader: 512 chunks of 16 B per operand tile, 2 per thread
-    u32x4 ar[2], br[2];
+    u32x4 ar[8], br[8];
     auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i, row = c >> 2, seg = c & 3;
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
             const int64_t u = row0 + row, v = col0 + row;
             ar[i] = u < g.Np ? *(const u32x4 *)(F + u * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
             br[i] = v < A.col_hi ? *(const u32x4 *)(F + v * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
@@ -137,63 +179,72 @@ __global__ __launch_bounds__(256) void cos_phase(const Args A) {
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int c = tid + 256 * i, row = c >> 2, seg = c & 3;
-            *(u32x4 *)(&As[buf][row * GROW + 8 * seg]) = ar[i];
-            *(u32x4 *)(&Bs[buf][row * GROW + 8 * seg]) = br[i];
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
+            *(u32x4 *)(&As[buf][row * CROW + 8 * seg]) = ar[i];
+            *(u32x4 *)(&Bs[buf][row * CROW + 8 * seg]) = br[i];
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
 
-    const int nk = A.Df / GK;
+    const int nk = A.Df / CK;
     load(0);
     store(0);
     __syncthreads();
     for (int t = 0; t < nk; ++t) {
         const int buf = t & 1;
-        if (t + 1 < nk) load((t + 1) * GK);
+        if (t + 1 < nk) load((t + 1) * CK);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 a[2], b[2];
+        for (int kk = 0; kk < CK / 16; ++kk) {
+            bf16x8 a[4], b[4];
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-                a[bi] = *(const bf16x8 *)(&As[buf][(64 * wr + 32 * bi + n) * GROW + 16 * kk + 8 * gq]);
+            for (int bi = 0; bi < 4; ++bi)
+                a[bi] = *(const bf16x8 *)(&As[buf][(128 * wr + 32 * bi + n) * CROW + 16 * kk + 8 * gq]);
 #pragma unroll
-            for (int bj = 0; bj < 2; ++bj)
-                b[bj] = *(const bf16x8 *)(&Bs[buf][(64 * wc + 32 * bj + n) * GROW + 16 * kk + 8 * gq]);
+            for (int bj = 0; bj < 4; ++bj)
+                b[bj] = *(const bf16x8 *)(&Bs[buf][(128 * wc + 32 * bj + n) * CROW + 16 * kk + 8 * gq]);
 #pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
+            for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-                for (int bj = 0; bj < 2; ++bj)
+                for (int bj = 0; bj < 4; ++bj)
                     acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
         }
         if (t + 1 < nk) store(buf ^ 1);
         __syncthreads();
     }
 
-    // epilogue: C[row][col] with col = lane%32 of the block, rows per register
+    // ---- epilogue: lane holds column n of each block, rows per register
+    float iv[4];
+    int32_t fv[4];
+    bool vok[4];
+    int64_t vcol[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        vcol[bj] = col0 + 128 * wc + 32 * bj + n;
+        vok[bj] = vcol[bj] < A.col_hi;
+        iv[bj] = vok[bj] ? A.s.invn[vcol[bj]] : 0.f;
+        fv[bj] = vok[bj] ? (int32_t)(vcol[bj] / g.P) : -2;
+    }
     const uint64_t half = gq ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) {
-        const int64_t v = col0 + 64 * wc + 32 * bj + n;
-        const bool vok = v < A.col_hi;
-        const float iv = vok ? A.s.invn[v] : 0.f;
-        const int32_t fv = vok ? (int32_t)(v / g.P) : -2;
+    for (int bi = 0; bi < 4; ++bi) {
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) {
+        for (int r = 0; r < 16; ++r) {
+            const int lr = 128 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+            const float thr = r_thr[lr];
+            const int32_t fr = r_frame[lr];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
-                const float c = acc[bi][bj][r] * r_invn[lr] * iv;
-                const bool keep = vok && r_frame[lr] >= 0 && r_frame[lr] != fv && c >= r_theta[lr];
+            for (int bj = 0; bj < 4; ++bj) {
+                const float x = acc[bi][bj][r] * iv[bj];
+                const bool keep = vok[bj] && x >= thr && (!overlap || fr != fv[bj]);
                 const uint64_t m = __ballot(keep) & half;
                 if (m == 0ull) continue;
                 const int64_t u = row0 + lr;
@@ -204,7 +255,8 @@ __global__ __launch_bounds__(256) void cos_phase(const Args A) {
                 if (keep) {
                     const uint32_t slot = base + (uint32_t)__popcll(m & below);
                     if (slot < (uint32_t)A.cap)
-                        A.s.cand[u * A.cap + slot] = make_float2(c, __int_as_float((int32_t)v));
+                        A.s.cand[u * A.cap + slot] =
+                            make_float2(x * r_iu[lr], __int_as_float((int32_t)vcol[bj]));
                 }
             }
         }
@@ -218,23 +270,25 @@ template <int MAXE> struct RowSel {
     float sc[MAXE];
     int32_t id[MAXE];
     uint32_t key[MAXE];
-    int n;
+    int n, ne;         // entries, and register slots in use (ceil(n / 64))
     uint32_t thr;      // K-th largest key
     int32_t ithr;      // largest index kept among keys == thr
     __device__ void load(const float2 *buf, int nn, int lane) {
         n = nn;
+        ne = (nn + 63) / 64;
 #pragma unroll
         for (int e = 0; e < MAXE; ++e) {
-            const int i = e * 64 + lane;
-            if (i < n) {
-                const float2 x = buf[i];
-                sc[e] = x.x;
-                id[e] = __float_as_int(x.y);
-                key[e] = order_key(x.x);
-            } else {
-                sc[e] = -INFINITY;
-                id[e] = INT32_MAX;
-                key[e] = 0u;
+            sc[e] = -INFINITY;
+            id[e] = INT32_MAX;
+            key[e] = 0u;
+            if (e < ne) {
+                const int i = e * 64 + lane;
+                if (i < n) {
+                    const float2 x = buf[i];
+                    sc[e] = x.x;
+                    id[e] = __float_as_int(x.y);
+                    key[e] = order_key(x.x);
+                }
             }
         }
     }
@@ -244,22 +298,29 @@ template <int MAXE> struct RowSel {
         return x;
     }
     __device__ bool valid(int e, int lane) const { return e * 64 + lane < n; }
-    // Select K (<= n) entries.
+    // count of valid entries with key >= k (per lane)
+    __device__ uint32_t count_ge(uint32_t k, int lane) const {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e)
+            if (e < ne) c += (valid(e, lane) && key[e] >= k) ? 1u : 0u;
+        return c;
+    }
+    // Select K (<= n) entries by (key desc, id asc).
     __device__ void select(int K, int lane) {
         uint32_t prefix = 0;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t cand = prefix | (1u << bit);
-            uint32_t c = 0;
-#pragma unroll
-            for (int e = 0; e < MAXE; ++e) c += (valid(e, lane) && key[e] >= cand) ? 1u : 0u;
-            if (wave_sum(c) >= (uint32_t)K) prefix = cand;
+            if (wave_sum(count_ge(cand, lane)) >= (uint32_t)K) prefix = cand;
         }
         thr = prefix;
         uint32_t gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < MAXE; ++e) {
-            gt += (valid(e, lane) && key[e] > thr) ? 1u : 0u;
-            eq += (valid(e, lane) && key[e] == thr) ? 1u : 0u;
+            if (e < ne) {
+                gt += (valid(e, lane) && key[e] > thr) ? 1u : 0u;
+                eq += (valid(e, lane) && key[e] == thr) ? 1u : 0u;
+            }
         }
         gt = wave_sum(gt);
         eq = wave_sum(eq);
@@ -275,13 +336,13 @@ template <int MAXE> struct RowSel {
             uint32_t c = 0;
 #pragma unroll
             for (int e = 0; e < MAXE; ++e)
-                c += (valid(e, lane) && key[e] == thr && (uint32_t)id[e] < cand) ? 1u : 0u;
+                if (e < ne) c += (valid(e, lane) && key[e] == thr && (uint32_t)id[e] < cand) ? 1u : 0u;
             if (wave_sum(c) < need) lo = cand;
         }
         ithr = (int32_t)lo;
     }
     __device__ bool kept(int e, int lane) const {
-        return valid(e, lane) && (key[e] > thr || (key[e] == thr && id[e] <= ithr));
+        return e < ne && valid(e, lane) && (key[e] > thr || (key[e] == thr && id[e] <= ithr));
     }
 };
 
@@ -414,7 +475,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.K = B.K;
     A.cap = B.cap;
     A.idx_out = B.idx_out;
-    const bool gemm = B.dino_dtype == BF16 && (B.Df % GK) == 0 && B.cap <= 64 * 64 && B.K <= 1024;
+    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.cap <= 64 * 64 && B.K <= 1024;
     A.all_rows_fallback = gemm ? 0 : 1;
     A.s = carve(B.scratch, B.g.Np, B.cap);
     const int64_t Np = B.g.Np;
@@ -424,14 +485,14 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     else
         hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
     if (gemm) {
-        const unsigned row_tiles = (unsigned)((Np + GT - 1) / GT);
         int64_t lo = 0, hi = B.g.P;
         while (lo < Np) {
             hi = std::min<int64_t>(hi, Np);
             A.col_lo = lo;
             A.col_hi = hi;
-            const unsigned col_tiles = (unsigned)((hi - lo + GT - 1) / GT);
-            hipLaunchKernelGGL(cos_phase, dim3(col_tiles, row_tiles), dim3(256), 0, stream, A);
+            const int64_t tiles = ((Np + CT - 1) / CT) * ((hi - lo + CT - 1) / CT);
+            const unsigned blocks = (unsigned)(8 * ((tiles + 7) / 8));
+            hipLaunchKernelGGL(cos_phase, dim3(blocks), dim3(256), 0, stream, A);
             const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
             if (A.cap <= 16 * 64)
                 hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A);
