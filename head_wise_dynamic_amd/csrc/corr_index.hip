@@ -69,6 +69,7 @@ struct Args {
     int32_t *idx_out;
     Scratch s;
     int64_t col_lo, col_hi;  // current phase
+    int64_t seed_cols;       // columns of the seed phase (whole frames)
 };
 
 template <typename T> __device__ inline float ldf(const T *p, int64_t i);
@@ -93,14 +94,17 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
     if (lane == 0) {
         A.s.invn[u] = acc > 0.f ? 1.f / sqrtf(acc) : 0.f;
         A.s.theta[u] = -INFINITY;
-        A.s.cnt[u] = 0u;
+        // the seed phase fills slots [0, seed_cols minus the own frame)
+        const int64_t fr = u / A.g.P;
+        A.s.cnt[u] = A.all_rows_fallback ? 0u
+                                         : (uint32_t)(A.seed_cols - (fr < A.seed_cols / A.g.P ? A.g.P : 0));
         A.s.over[u] = A.all_rows_fallback ? 1u : 0u;
     }
 }
 
 // ---- one phase of the cosine GEMM with threshold filtering.
-// Tile 256 x 256 per work-group of 4 waves (2 x 2); each wave owns 128 x 128
-// as 4 x 4 blocks of 32 x 32 (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
+// Tile 256 x 256 per work-group of 8 waves (4 x 2); each wave owns 64 x 128
+// as 2 x 4 blocks of 32 x 32 (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
 // Channels are staged through LDS 64 at a time, double buffered, with the
 // next stage prefetched into registers while the current one is multiplied.
 // Work-groups are mapped XCD by XCD (blockIdx % 8 selects the XCD): each XCD
@@ -111,15 +115,26 @@ constexpr int CK = 64;
 constexpr int CROW = CK + 8;   // padded LDS row: 144 B, conflict-free 16-byte reads
 constexpr int kGroupRows = 4;  // row tiles per group in the tile order
 
-__global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][CT * CROW];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][CT * CROW];
+constexpr int kTileElems = CT * CROW;     // one operand tile in LDS (bf16)
+constexpr int kRowCap = 48;                // survivors staged per row per tile
+constexpr int kCosThreads = 512;           // 8 waves: 4 (rows) x 2 (columns) of 64 x 128
+
+// SEED: the first phase (frames [0, seed_frames)), every candidate kept and
+// written at a fixed slot; otherwise the threshold-filtered phase.
+template <bool SEED>
+__global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
+    // operand tiles: As[2], Bs[2]; after the k-loop the same memory stages
+    // the surviving candidates (128 KB) and per-lane score spills (16 KB)
+    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
+    uint16_t (*As)[kTileElems] = (uint16_t (*)[kTileElems])smem;
+    uint16_t (*Bs)[kTileElems] = (uint16_t (*)[kTileElems])(smem + 2 * kTileElems);
     __shared__ float r_thr[CT], r_iu[CT];
     __shared__ int32_t r_frame[CT];
+    __shared__ uint32_t r_cnt[CT];
 
     const Geom &g = A.g;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave >> 1, wc = wave & 1;  // wave rows [64 wr, +64), columns [128 wc, +128)
     const int n = lane & 31, gq = lane >> 5;
 
     // ---- tile of this work-group
@@ -140,7 +155,7 @@ __global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
 
     // row thresholds in units of acc * inv|f_v|, lowered by 2^-20 relative so
     // that the filter never drops a value the exact comparison would keep
-    {
+    if (tid < CT) {
         const int64_t u = row0 + tid;
         float thr = INFINITY, iu = 0.f;
         int32_t fr = -1;
@@ -160,6 +175,7 @@ __global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
         r_thr[tid] = thr;
         r_iu[tid] = iu;
         r_frame[tid] = fr;
+        r_cnt[tid] = 0u;
     }
     const int32_t f_row_lo = (int32_t)(row0 / g.P);
     const int32_t f_row_hi = (int32_t)((min<int64_t>(row0 + CT, g.Np) - 1) / g.P);
@@ -167,11 +183,11 @@ __global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
     const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, A.col_hi) - 1) / g.P);
     const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
-    u32x4 ar[8], br[8];
+    u32x4 ar[4], br[4];
     auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
             const int64_t u = row0 + row, v = col0 + row;
             ar[i] = u < g.Np ? *(const u32x4 *)(F + u * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
             br[i] = v < A.col_hi ? *(const u32x4 *)(F + v * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
@@ -179,16 +195,16 @@ __global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
     };
     auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * i, row = c >> 3, seg = c & 7;
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
             *(u32x4 *)(&As[buf][row * CROW + 8 * seg]) = ar[i];
             *(u32x4 *)(&Bs[buf][row * CROW + 8 * seg]) = br[i];
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi)
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
@@ -203,15 +219,16 @@ __global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
         if (t + 1 < nk) load((t + 1) * CK);
 #pragma unroll
         for (int kk = 0; kk < CK / 16; ++kk) {
-            bf16x8 a[4], b[4];
+            __builtin_amdgcn_iglp_opt(0);  // interleave LDS reads with the MFMA chain
+            bf16x8 a[2], b[4];
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
-                a[bi] = *(const bf16x8 *)(&As[buf][(128 * wr + 32 * bi + n) * CROW + 16 * kk + 8 * gq]);
+            for (int bi = 0; bi < 2; ++bi)
+                a[bi] = *(const bf16x8 *)(&As[buf][(64 * wr + 32 * bi + n) * CROW + 16 * kk + 8 * gq]);
 #pragma unroll
             for (int bj = 0; bj < 4; ++bj)
                 b[bj] = *(const bf16x8 *)(&Bs[buf][(128 * wc + 32 * bj + n) * CROW + 16 * kk + 8 * gq]);
 #pragma unroll
-            for (int bi = 0; bi < 4; ++bi)
+            for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
                 for (int bj = 0; bj < 4; ++bj)
                     acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
@@ -220,59 +237,100 @@ __global__ __launch_bounds__(256, 1) void cos_phase(const Args A) {
         __syncthreads();
     }
 
-    // ---- epilogue: lane holds column n of each block, rows per register
+    // ---- epilogue: lane holds column n of each block, rows per register.
     float iv[4];
     int32_t fv[4];
-    bool vok[4];
-    int64_t vcol[4];
+    const int32_t vcol0 = (int32_t)(col0 + 128 * wc + n);  // column of block bj: vcol0 + 32 bj
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-        vcol[bj] = col0 + 128 * wc + 32 * bj + n;
-        vok[bj] = vcol[bj] < A.col_hi;
-        iv[bj] = vok[bj] ? A.s.invn[vcol[bj]] : 0.f;
-        fv[bj] = vok[bj] ? (int32_t)(vcol[bj] / g.P) : -2;
+        const int64_t v = vcol0 + 32 * bj;
+        const bool vok = v < A.col_hi;
+        iv[bj] = vok ? A.s.invn[v] : __builtin_nanf("");  // NaN never passes a comparison
+        fv[bj] = vok ? (int32_t)(v / g.P) : -2;
     }
-    const uint64_t half = gq ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    if (SEED) {
+        // every candidate of the seed frames is kept; its slot in the row's
+        // buffer is fixed: the seed columns, own frame removed
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
+        for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int lr = 128 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
-            const float thr = r_thr[lr];
-            const int32_t fr = r_frame[lr];
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+                const int32_t fr = r_frame[lr];
+                const float iu = r_iu[lr];
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
-                const float x = acc[bi][bj][r] * iv[bj];
-                const bool keep = vok[bj] && x >= thr && (!overlap || fr != fv[bj]);
-                const uint64_t m = __ballot(keep) & half;
-                if (m == 0ull) continue;
-                const int64_t u = row0 + lr;
-                uint32_t base = 0;
-                const int leader = __ffsll((unsigned long long)m) - 1;
-                if (lane == leader) base = atomicAdd(&A.s.cnt[u], (uint32_t)__popcll(m));
-                base = __shfl(base, leader);
-                if (keep) {
-                    const uint32_t slot = base + (uint32_t)__popcll(m & below);
-                    if (slot < (uint32_t)A.cap)
-                        A.s.cand[u * A.cap + slot] =
-                            make_float2(x * r_iu[lr], __int_as_float((int32_t)vcol[bj]));
+                for (int bj = 0; bj < 4; ++bj) {
+                    const int32_t v = vcol0 + 32 * bj;
+                    if (fr >= 0 && fv[bj] >= 0 && fr != fv[bj]) {
+                        const int32_t slot = (fv[bj] > fr) ? v - g.P : v;
+                        const float c = acc[bi][bj][r] * iv[bj] * iu;
+                        A.s.cand[(row0 + lr) * A.cap + slot] = make_float2(c, __int_as_float(v));
+                    }
+                }
+            }
+        return;
+    }
+
+    // filtered phase.  Fast path per 32 x 32 block: a 16-bit mask of the
+    // lane's values that pass their row's threshold.  Lanes with a hit spill
+    // their 16 scores to LDS and stage each hit in its row's LDS list; one
+    // global atomic per row then reserves the row's buffer slots.
+    __syncthreads();  // operand tiles are no longer read: reuse them
+    float2 *stage = (float2 *)smem;                                  // [CT][kRowCap]
+    float *xl = (float *)((char *)smem + sizeof(float2) * CT * kRowCap) + (wave * 64 + lane) * 16;
+    const float *thr_base = r_thr + 64 * wr + 4 * gq;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+            uint32_t k = 0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                k |= (acc[bi][bj][r] * iv[bj] >= thr_base[32 * bi + 8 * (r >> 2) + (r & 3)]) ? (1u << r) : 0u;
+            if (k) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xl[r] = acc[bi][bj][r] * iv[bj];
+                const int32_t v = vcol0 + 32 * bj;
+                while (k) {
+                    const int r = __ffs(k) - 1;
+                    k &= k - 1;
+                    const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+                    if (overlap && r_frame[lr] == fv[bj]) continue;  // own frame
+                    const float2 e = make_float2(xl[r] * r_iu[lr], __int_as_float(v));
+                    const uint32_t slot = atomicAdd(&r_cnt[lr], 1u);
+                    if (slot < (uint32_t)kRowCap) {
+                        stage[lr * kRowCap + slot] = e;
+                    } else {  // rare: more than kRowCap hits of one row in one tile
+                        const uint32_t gs = atomicAdd(&A.s.cnt[row0 + lr], 1u);
+                        if (gs < (uint32_t)A.cap) A.s.cand[(row0 + lr) * A.cap + gs] = e;
+                    }
                 }
             }
         }
     }
+    __syncthreads();
+    if (tid < CT) {
+        const uint32_t nloc = min(r_cnt[tid], (uint32_t)kRowCap);
+        if (nloc) {
+            const int64_t u = row0 + tid;
+            const uint32_t base = atomicAdd(&A.s.cnt[u], nloc);
+            for (uint32_t i = 0; i < nloc; ++i)
+                if (base + i < (uint32_t)A.cap) A.s.cand[u * A.cap + base + i] = stage[tid * kRowCap + i];
+        }
+    }
 }
 
-// ---- per-row exact selection inside one wave.
-// Loads the row's n buffered candidates (n <= 64 * MAXE) into registers and
-// finds the K-th largest (score, then lower index) with bitwise searches.
+// ---- per-row selection inside one wave.
+// The row's n buffered candidates (n <= 64 * MAXE) are held in registers,
+// lane-strided.  Counts over the row use ballot + popcount, so the search
+// needs no cross-lane shuffles.
 template <int MAXE> struct RowSel {
     float sc[MAXE];
     int32_t id[MAXE];
-    uint32_t key[MAXE];
     int n, ne;         // entries, and register slots in use (ceil(n / 64))
-    uint32_t thr;      // K-th largest key
-    int32_t ithr;      // largest index kept among keys == thr
+    uint32_t thr;      // selection threshold (order key)
+    int32_t ithr;      // largest index kept among keys == thr (exact mode)
     __device__ void load(const float2 *buf, int nn, int lane) {
         n = nn;
         ne = (nn + 63) / 64;
@@ -280,50 +338,52 @@ template <int MAXE> struct RowSel {
         for (int e = 0; e < MAXE; ++e) {
             sc[e] = -INFINITY;
             id[e] = INT32_MAX;
-            key[e] = 0u;
             if (e < ne) {
                 const int i = e * 64 + lane;
                 if (i < n) {
                     const float2 x = buf[i];
                     sc[e] = x.x;
                     id[e] = __float_as_int(x.y);
-                    key[e] = order_key(x.x);
                 }
             }
         }
     }
-    __device__ static uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-        return x;
-    }
     __device__ bool valid(int e, int lane) const { return e * 64 + lane < n; }
-    // count of valid entries with key >= k (per lane)
     __device__ uint32_t count_ge(uint32_t k, int lane) const {
         uint32_t c = 0;
 #pragma unroll
         for (int e = 0; e < MAXE; ++e)
-            if (e < ne) c += (valid(e, lane) && key[e] >= k) ? 1u : 0u;
+            if (e < ne) c += (uint32_t)__popcll(__ballot(valid(e, lane) && order_key(sc[e]) >= k));
         return c;
     }
-    // Select K (<= n) entries by (key desc, id asc).
-    __device__ void select(int K, int lane) {
+    // Largest key prefix (the top `bits` bits resolved) with >= K entries at
+    // or above it.  With bits = 32 this is the K-th largest key exactly.
+    __device__ uint32_t prefix_search(int K, int lane, int bits) const {
         uint32_t prefix = 0;
-        for (int bit = 31; bit >= 0; --bit) {
+        for (int bit = 31; bit >= 32 - bits; --bit) {
             const uint32_t cand = prefix | (1u << bit);
-            if (wave_sum(count_ge(cand, lane)) >= (uint32_t)K) prefix = cand;
+            if (count_ge(cand, lane) >= (uint32_t)K) prefix = cand;
         }
-        thr = prefix;
+        return prefix;
+    }
+    // Approximate: keep every entry whose key is >= a 16-bit prefix bound of
+    // the K-th largest key (at least K entries, a few more near the bound).
+    __device__ void select_bound(int K, int lane) {
+        thr = prefix_search(K, lane, 16);
+        ithr = INT32_MAX;
+    }
+    // Exact: the K entries first by (score desc, index asc).
+    __device__ void select_exact(int K, int lane) {
+        thr = prefix_search(K, lane, 32);
         uint32_t gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < MAXE; ++e) {
             if (e < ne) {
-                gt += (valid(e, lane) && key[e] > thr) ? 1u : 0u;
-                eq += (valid(e, lane) && key[e] == thr) ? 1u : 0u;
+                const uint32_t key = order_key(sc[e]);
+                gt += (uint32_t)__popcll(__ballot(valid(e, lane) && key > thr));
+                eq += (uint32_t)__popcll(__ballot(valid(e, lane) && key == thr));
             }
         }
-        gt = wave_sum(gt);
-        eq = wave_sum(eq);
         const uint32_t need = (uint32_t)K - gt;
         if (eq == need) {
             ithr = INT32_MAX;
@@ -336,30 +396,36 @@ template <int MAXE> struct RowSel {
             uint32_t c = 0;
 #pragma unroll
             for (int e = 0; e < MAXE; ++e)
-                if (e < ne) c += (valid(e, lane) && key[e] == thr && (uint32_t)id[e] < cand) ? 1u : 0u;
-            if (wave_sum(c) < need) lo = cand;
+                if (e < ne)
+                    c += (uint32_t)__popcll(
+                        __ballot(valid(e, lane) && order_key(sc[e]) == thr && (uint32_t)id[e] < cand));
+            if (c < need) lo = cand;
         }
         ithr = (int32_t)lo;
     }
     __device__ bool kept(int e, int lane) const {
-        return e < ne && valid(e, lane) && (key[e] > thr || (key[e] == thr && id[e] <= ithr));
+        const uint32_t key = order_key(sc[e]);
+        return e < ne && valid(e, lane) && (key > thr || (key == thr && id[e] <= ithr));
     }
 };
 
-template <int MAXE> __global__ __launch_bounds__(256) void compact_rows(const Args A) {
+// Between phases: raise theta_u to a lower bound of the row's K-th best score
+// and drop the entries below it.  Rows with cnt outside (lo_cnt, hi_cnt] are
+// left to the other register-size variant.
+template <int MAXE>
+__global__ __launch_bounds__(256) void compact_rows(const Args A, uint32_t lo_cnt, uint32_t hi_cnt) {
     const int64_t u = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (u >= A.g.Np) return;
     const uint32_t c = A.s.cnt[u];
-    if (c > (uint32_t)A.cap) {
-        if (lane == 0) A.s.over[u] = 1u;
-    }
-    const int nn = (int)min<uint32_t>(c, (uint32_t)A.cap);
-    if (nn <= A.K) return;
+    const uint32_t nn = min(c, (uint32_t)A.cap);
+    if (nn <= lo_cnt || nn > hi_cnt) return;
+    if (c > (uint32_t)A.cap && lane == 0) A.s.over[u] = 1u;
+    if ((int)nn <= A.K) return;
     float2 *buf = A.s.cand + u * A.cap;
     RowSel<MAXE> R;
-    R.load(buf, nn, lane);
-    R.select(A.K, lane);
+    R.load(buf, (int)nn, lane);
+    R.select_bound(A.K, lane);
     uint32_t mine = 0;
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) mine += R.kept(e, lane) ? 1u : 0u;
@@ -369,24 +435,28 @@ template <int MAXE> __global__ __launch_bounds__(256) void compact_rows(const Ar
         const uint32_t y = __shfl_up(incl, o);
         if (lane >= o) incl += y;
     }
+    const uint32_t total = __shfl(incl, 63);
     uint32_t pos = incl - mine;
 #pragma unroll
     for (int e = 0; e < MAXE; ++e)
         if (R.kept(e, lane)) buf[pos++] = make_float2(R.sc[e], __int_as_float(R.id[e]));
     if (lane == 0) {
-        A.s.cnt[u] = (uint32_t)A.K;
+        A.s.cnt[u] = total;
         A.s.theta[u] = order_key_to_float(R.thr);
     }
 }
 
-template <int MAXE> __global__ __launch_bounds__(256) void finalize_rows(const Args A) {
+template <int MAXE>
+__global__ __launch_bounds__(256) void finalize_rows(const Args A, uint32_t lo_cnt, uint32_t hi_cnt) {
     __shared__ int32_t sel[kRowWaves][1024];
     const int wv = threadIdx.x >> 6;
     const int64_t u = (int64_t)blockIdx.x * kRowWaves + wv;
     const int lane = threadIdx.x & 63;
     if (u >= A.g.Np) return;
-    if (A.s.over[u] || A.s.cnt[u] > (uint32_t)A.cap) return;  // exact per-row engine
-    const int nn = (int)A.s.cnt[u];
+    const uint32_t c = A.s.cnt[u];
+    if (c <= lo_cnt || c > hi_cnt) return;
+    if (A.s.over[u] || c > (uint32_t)A.cap) return;  // exact per-row engine
+    const int nn = (int)c;
     if (nn < A.K) {  // cannot happen without an overflow; recompute exactly
         if (lane == 0) A.s.over[u] = 1u;
         return;
@@ -394,7 +464,7 @@ template <int MAXE> __global__ __launch_bounds__(256) void finalize_rows(const A
     const float2 *buf = A.s.cand + u * A.cap;
     RowSel<MAXE> R;
     R.load(buf, nn, lane);
-    R.select(A.K, lane);
+    R.select_exact(A.K, lane);
     uint32_t mine = 0;
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) mine += R.kept(e, lane) ? 1u : 0u;
@@ -454,7 +524,8 @@ template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(cons
 }  // namespace
 
 int32_t corr_capacity(const Geom &g, int32_t K) {
-    int64_t cap = std::max<int64_t>((int64_t)g.P + 2 * (int64_t)K, 8 * (int64_t)K);
+    // the seed phase stores two frames' candidates; later phases add ~K-2K
+    int64_t cap = std::max<int64_t>(2 * (int64_t)g.P, 8 * (int64_t)K);
     cap = (cap + 63) / 64 * 64;
     return (int32_t)cap;
 }
@@ -479,37 +550,45 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.all_rows_fallback = gemm ? 0 : 1;
     A.s = carve(B.scratch, B.g.Np, B.cap);
     const int64_t Np = B.g.Np;
+    A.seed_cols = std::min<int64_t>(Np, 2 * (int64_t)B.g.P);
     const unsigned rb = (unsigned)((Np + 3) / 4);
     if (B.dino_dtype == BF16)
         hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
     else
         hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
     if (gemm) {
-        int64_t lo = 0, hi = B.g.P;
+        const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
+        // rows with <= 1024 candidates use the 16-slot register variant, the
+        // rest (the seed phase, rare heavy rows) the 64-slot one
+        const uint32_t small = 16 * 64, big = 64 * 64;
+        auto compact = [&]() {
+            hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A, 0u, small);
+            if ((uint32_t)A.cap > small)
+                hipLaunchKernelGGL(compact_rows<64>, dim3(cb), dim3(256), 0, stream, A, small, big);
+        };
+        auto blocks_for = [&](int64_t lo, int64_t hi) {
+            const int64_t tiles = ((Np + CT - 1) / CT) * ((hi - lo + CT - 1) / CT);
+            return (unsigned)(8 * ((tiles + 7) / 8));
+        };
+        // seed phase: frames 0 and 1, every candidate kept
+        A.col_lo = 0;
+        A.col_hi = A.seed_cols;
+        hipLaunchKernelGGL(cos_phase<true>, dim3(blocks_for(0, A.seed_cols)), dim3(kCosThreads), 0, stream, A);
+        compact();
+        // doubling filtered phases
+        int64_t lo = A.seed_cols, hi = 2 * A.seed_cols;
         while (lo < Np) {
             hi = std::min<int64_t>(hi, Np);
             A.col_lo = lo;
             A.col_hi = hi;
-            const int64_t tiles = ((Np + CT - 1) / CT) * ((hi - lo + CT - 1) / CT);
-            const unsigned blocks = (unsigned)(8 * ((tiles + 7) / 8));
-            hipLaunchKernelGGL(cos_phase, dim3(blocks), dim3(256), 0, stream, A);
-            const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
-            if (A.cap <= 16 * 64)
-                hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A);
-            else if (A.cap <= 32 * 64)
-                hipLaunchKernelGGL(compact_rows<32>, dim3(cb), dim3(256), 0, stream, A);
-            else
-                hipLaunchKernelGGL(compact_rows<64>, dim3(cb), dim3(256), 0, stream, A);
+            hipLaunchKernelGGL(cos_phase<false>, dim3(blocks_for(lo, hi)), dim3(kCosThreads), 0, stream, A);
+            compact();
             lo = hi;
             hi = 2 * hi;
         }
-        const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
-        if (A.cap <= 16 * 64)
-            hipLaunchKernelGGL(finalize_rows<16>, dim3(cb), dim3(256), 0, stream, A);
-        else if (A.cap <= 32 * 64)
-            hipLaunchKernelGGL(finalize_rows<32>, dim3(cb), dim3(256), 0, stream, A);
-        else
-            hipLaunchKernelGGL(finalize_rows<64>, dim3(cb), dim3(256), 0, stream, A);
+        hipLaunchKernelGGL(finalize_rows<16>, dim3(cb), dim3(256), 0, stream, A, 0u, small);
+        if ((uint32_t)A.cap > small)
+            hipLaunchKernelGGL(finalize_rows<64>, dim3(cb), dim3(256), 0, stream, A, small, big);
     }
     const unsigned fb = (unsigned)std::min<int64_t>(kFallbackBlocks, Np);
     if (B.dino_dtype == BF16)
