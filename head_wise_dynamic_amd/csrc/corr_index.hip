@@ -410,39 +410,61 @@ template <int MAXE> struct RowSel {
 };
 
 // Between phases: raise theta_u to a lower bound of the row's K-th best score
-// and drop the entries below it.  Rows with cnt outside (lo_cnt, hi_cnt] are
-// left to the other register-size variant.
+// and drop the entries below it.  The bound comes from the first 64 * MAXE
+// entries (the K-th best of a subset never exceeds the K-th best of the row);
+// a longer row is then filtered by streaming over all its entries.
 template <int MAXE>
-__global__ __launch_bounds__(256) void compact_rows(const Args A, uint32_t lo_cnt, uint32_t hi_cnt) {
+__global__ __launch_bounds__(256) void compact_rows(const Args A) {
     const int64_t u = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (u >= A.g.Np) return;
     const uint32_t c = A.s.cnt[u];
     const uint32_t nn = min(c, (uint32_t)A.cap);
-    if (nn <= lo_cnt || nn > hi_cnt) return;
     if (c > (uint32_t)A.cap && lane == 0) A.s.over[u] = 1u;
     if ((int)nn <= A.K) return;
     float2 *buf = A.s.cand + u * A.cap;
-    RowSel<MAXE> R;
-    R.load(buf, (int)nn, lane);
-    R.select_bound(A.K, lane);
-    uint32_t mine = 0;
+    uint32_t total = nn, thr = 0;
+    for (int pass = 0; pass < 4 && (int)total > A.K; ++pass) {
+        const int nreg = (int)min<uint32_t>(total, 64u * MAXE);
+        RowSel<MAXE> R;
+        R.load(buf, nreg, lane);
+        R.select_bound(A.K, lane);
+        thr = R.thr;
+        if ((int)total == nreg) {
+            uint32_t mine = 0;
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) mine += R.kept(e, lane) ? 1u : 0u;
-    uint32_t incl = mine;
+            for (int e = 0; e < MAXE; ++e) mine += R.kept(e, lane) ? 1u : 0u;
+            uint32_t incl = mine;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            total = __shfl(incl, 63);
+            uint32_t pos = incl - mine;
+#pragma unroll
+            for (int e = 0; e < MAXE; ++e)
+                if (R.kept(e, lane)) buf[pos++] = make_float2(R.sc[e], __int_as_float(R.id[e]));
+            break;
+        }
+        // in-place ordered filter: the write position never passes the read one
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        uint32_t pos = 0;
+        for (uint32_t i0 = 0; i0 < total; i0 += 64) {
+            const uint32_t i = i0 + lane;
+            float2 x = make_float2(-INFINITY, 0.f);
+            if (i < total) x = buf[i];
+            const bool keep = i < total && order_key(x.x) >= thr;
+            const uint64_t m = __ballot(keep);
+            __builtin_amdgcn_wave_barrier();
+            if (keep) buf[pos + (uint32_t)__popcll(m & below)] = x;
+            pos += (uint32_t)__popcll(m);
+        }
+        total = pos;
     }
-    const uint32_t total = __shfl(incl, 63);
-    uint32_t pos = incl - mine;
-#pragma unroll
-    for (int e = 0; e < MAXE; ++e)
-        if (R.kept(e, lane)) buf[pos++] = make_float2(R.sc[e], __int_as_float(R.id[e]));
     if (lane == 0) {
         A.s.cnt[u] = total;
-        A.s.theta[u] = order_key_to_float(R.thr);
+        A.s.theta[u] = order_key_to_float(thr);
     }
 }
 
@@ -558,14 +580,8 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
         hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
     if (gemm) {
         const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
-        // rows with <= 1024 candidates use the 16-slot register variant, the
-        // rest (the seed phase, rare heavy rows) the 64-slot one
         const uint32_t small = 16 * 64, big = 64 * 64;
-        auto compact = [&]() {
-            hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A, 0u, small);
-            if ((uint32_t)A.cap > small)
-                hipLaunchKernelGGL(compact_rows<64>, dim3(cb), dim3(256), 0, stream, A, small, big);
-        };
+        auto compact = [&]() { hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A); };
         auto blocks_for = [&](int64_t lo, int64_t hi) {
             const int64_t tiles = ((Np + CT - 1) / CT) * ((hi - lo + CT - 1) / CT);
             return (unsigned)(8 * ((tiles + 7) / 8));
