@@ -129,6 +129,7 @@ def main():
         per = {}
         for name, ms in ctx.read_kernel_timing():
             per[name] = per.get(name, 0.0) + ms
+            per["launches:" + name] = per.get("launches:" + name, 0) + 1
         for name, ms in per.items():
             groups.setdefault(name, []).append(ms)
     launches = {}
@@ -138,7 +139,8 @@ def main():
         for name, ms in ctx.read_kernel_timing():
             launches.setdefault(name, []).append(ms)
     ctx.set_kernel_timing(False)
-    breakdown = {n: round(statistics.median(v), 4) for n, v in groups.items()}
+    launch_counts = {n.split(":", 1)[1]: int(v[0]) for n, v in groups.items() if n.startswith("launches:")}
+    breakdown = {n: round(statistics.median(v), 4) for n, v in groups.items() if not n.startswith("launches:")}
 
     # layer with the index cached (every layer after the first of a sequence)
     attn = []
@@ -197,11 +199,19 @@ def main():
         t = statistics.median(launches["gather_attention"])
         cand["gather_attention"] = dict(bound="hbm", achieved=gather_bytes / (t * 1e-3) / 1e9,
                                         peak=PEAK_HBM_GBS, unit="GB/s", ms=t)
+    if "cosine_gemm" in groups:
+        # the index build's GEMM phases: algorithmic work 2 (S P)^2 Df per
+        # step (every pair counted once per direction); the kernel computes the
+        # square part of the pair space once per unordered pair
+        t = statistics.median(groups["cosine_gemm"])
+        cand["cosine_gemm"] = dict(bound="mfma", achieved=2.0 * g.Np * g.Np * w.Df / (t * 1e-3) / 1e12,
+                                   peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", ms=t,
+                                   launches=launch_counts.get("cosine_gemm", 0))
     dom = max(cand, key=lambda n: cand[n]["ms"])
     r = cand[dom]
     roofline = {"kernel": dom, "bound": r["bound"], "achieved": round(r["achieved"], 2), "peak": r["peak"],
                 "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4), "traffic": None,
-                "kernel_ms": round(r["ms"], 4)}
+                "kernel_ms_per_step": round(r["ms"], 4), "launches_per_step": r.get("launches", 1)}
     others = {n: {"achieved": round(c["achieved"], 2), "unit": c["unit"], "peak": c["peak"],
                   "frac": round(c["achieved"] / c["peak"], 4), "kernel_ms": round(c["ms"], 4)}
               for n, c in cand.items() if n != dom}

@@ -66,6 +66,20 @@ struct Timed {
     }
 };
 
+// Tracing hook for launch groups that live inside one launcher (the cosine
+// GEMM phases of the index build): begin opens a Timed record, end closes it.
+void mark_launch(void *user, int begin, const char *name, hipStream_t s) {
+    saf_ctx *c = (saf_ctx *)user;
+    static thread_local Timed *open = nullptr;
+    if (!c->timing) return;
+    if (begin) {
+        open = new (std::nothrow) Timed(c, s, name);
+    } else if (open) {
+        delete open;
+        open = nullptr;
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -310,6 +324,8 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     B.cap = cap;
     B.idx_out = c->corr_idx;
     B.scratch = c->corr_scratch;
+    B.mark = mark_launch;
+    B.mark_user = c;
     hipError_t e;
     {
         Timed tm(c, as_stream(stream), "corr_index");

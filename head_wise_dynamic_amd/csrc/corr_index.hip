@@ -68,8 +68,10 @@ struct Args {
     int32_t all_rows_fallback;
     int32_t *idx_out;
     Scratch s;
-    int64_t col_lo, col_hi;  // current phase
+    int64_t col_lo, col_hi;  // current phase: columns
+    int64_t row_lo, row_hi;  // current phase: rows
     int64_t seed_cols;       // columns of the seed phase (whole frames)
+    int64_t sym_lo;          // start of the symmetric square [sym_lo, Np)^2
 };
 
 template <typename T> __device__ inline float ldf(const T *p, int64_t i);
@@ -110,27 +112,47 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
 // Work-groups are mapped XCD by XCD (blockIdx % 8 selects the XCD): each XCD
 // sweeps a contiguous, row-grouped range of tiles so that its L2 serves the
 // operand panels its work-groups share.
+//
+// Modes:
+//   SEED   rows [row_lo,row_hi) x the seed columns: every candidate is kept at
+//          a fixed slot (the seed columns with the own frame removed);
+//   FILTER rows [row_lo,row_hi) x columns [col_lo,col_hi): a value is kept if
+//          it reaches the row's threshold;
+//   SYM    the upper triangle of tiles of [sym_lo,Np) x [sym_lo,Np): cosine is
+//          symmetric, so each off-diagonal tile feeds its rows (forward) and,
+//          transposed, its columns' rows.
 constexpr int CT = 256;
 constexpr int CK = 64;
 constexpr int CROW = CK + 8;   // padded LDS row: 144 B, conflict-free 16-byte reads
 constexpr int kGroupRows = 4;  // row tiles per group in the tile order
 
 constexpr int kTileElems = CT * CROW;     // one operand tile in LDS (bf16)
-constexpr int kRowCap = 48;                // survivors staged per row per tile
 constexpr int kCosThreads = 512;           // 8 waves: 4 (rows) x 2 (columns) of 64 x 128
+enum CosMode { SEED = 0, FILTER = 1, SYM = 2 };
 
-// SEED: the first phase (frames [0, seed_frames)), every candidate kept and
-// written at a fixed slot; otherwise the threshold-filtered phase.
-template <bool SEED>
+// threshold of a row in units of acc * (inverse norm of the other side),
+// lowered by 2^-20 relative so that the filter never drops a value the exact
+// comparison would keep
+__device__ __forceinline__ float scaled_threshold(float th, float inv_self) {
+    if (th == -INFINITY) return -INFINITY;
+    if (inv_self > 0.f) {
+        const float t = th / inv_self;
+        return t > 0.f ? t * (1.f - 0x1p-20f) : (t < 0.f ? t * (1.f + 0x1p-20f) : -1e-30f);
+    }
+    return th <= 0.f ? -INFINITY : INFINITY;  // zero-norm row: every cosine is 0
+}
+
+template <int MODE>
 __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
-    // operand tiles: As[2], Bs[2]; after the k-loop the same memory stages
-    // the surviving candidates (128 KB) and per-lane score spills (16 KB)
+    constexpr int kRowCap = MODE == SYM ? 24 : 48;  // survivors staged per row per tile
+    // operand tiles: As[2], Bs[2]; after the k-loop the same memory stages the
+    // surviving candidates and per-lane accumulator spills
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
     uint16_t (*As)[kTileElems] = (uint16_t (*)[kTileElems])smem;
     uint16_t (*Bs)[kTileElems] = (uint16_t (*)[kTileElems])(smem + 2 * kTileElems);
-    __shared__ float r_thr[CT], r_iu[CT];
+    __shared__ float r_thr[CT], r_iu[CT], c_thr[CT];
     __shared__ int32_t r_frame[CT];
-    __shared__ uint32_t r_cnt[CT];
+    __shared__ uint32_t r_cnt[CT], c_cnt[CT];
 
     const Geom &g = A.g;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -138,49 +160,68 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     const int n = lane & 31, gq = lane >> 5;
 
     // ---- tile of this work-group
-    const int nrow = (int)((g.Np + CT - 1) / CT);
-    const int ncol = (int)((A.col_hi - A.col_lo + CT - 1) / CT);
-    const int total = nrow * ncol;
-    const int per_xcd = (total + 7) / 8;
-    const int tix = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (tix >= total) return;
-    const int gsize = kGroupRows * ncol;
-    const int grp = tix / gsize, rem = tix % gsize;
-    const int rows_in_grp = min(kGroupRows, nrow - grp * kGroupRows);
-    const int rt = grp * kGroupRows + rem % rows_in_grp;
-    const int ct = rem / rows_in_grp;
-    const int64_t row0 = (int64_t)rt * CT;
-    const int64_t col0 = A.col_lo + (int64_t)ct * CT;
+    int64_t row0, col0, row_hi, col_hi;
+    bool diag = false;
+    if (MODE == SYM) {
+        const int nt = (int)((g.Np - A.sym_lo + CT - 1) / CT);
+        const int total = nt * (nt + 1) / 2;
+        const int per_xcd = (total + 7) / 8;
+        const int tix = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+        if (tix >= total) return;
+        // row i of the triangle holds tiles (i, i..nt-1) and starts at i*nt - i(i-1)/2
+        const double b2 = 2.0 * nt + 1.0;
+        int i = (int)((b2 - sqrt(b2 * b2 - 8.0 * tix)) * 0.5);
+        i = max(0, min(i, nt - 1));
+        while (i > 0 && i * nt - i * (i - 1) / 2 > tix) --i;
+        while (i + 1 < nt && (i + 1) * nt - (i + 1) * i / 2 <= tix) ++i;
+        const int j = i + (tix - (i * nt - i * (i - 1) / 2));
+        row0 = A.sym_lo + (int64_t)i * CT;
+        col0 = A.sym_lo + (int64_t)j * CT;
+        row_hi = g.Np;
+        col_hi = g.Np;
+        diag = i == j;
+    } else {
+        const int nrow = (int)((A.row_hi - A.row_lo + CT - 1) / CT);
+        const int ncol = (int)((A.col_hi - A.col_lo + CT - 1) / CT);
+        const int total = nrow * ncol;
+        const int per_xcd = (total + 7) / 8;
+        const int tix = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+        if (tix >= total) return;
+        const int gsize = kGroupRows * ncol;
+        const int grp = tix / gsize, rem = tix % gsize;
+        const int rows_in_grp = min(kGroupRows, nrow - grp * kGroupRows);
+        const int rt = grp * kGroupRows + rem % rows_in_grp;
+        const int ct = rem / rows_in_grp;
+        row0 = A.row_lo + (int64_t)rt * CT;
+        col0 = A.col_lo + (int64_t)ct * CT;
+        row_hi = A.row_hi;
+        col_hi = A.col_hi;
+    }
     const uint16_t *F = (const uint16_t *)A.F;
 
-    // row thresholds in units of acc * inv|f_v|, lowered by 2^-20 relative so
-    // that the filter never drops a value the exact comparison would keep
     if (tid < CT) {
         const int64_t u = row0 + tid;
         float thr = INFINITY, iu = 0.f;
         int32_t fr = -1;
-        if (u < g.Np) {
-            const float th = A.s.theta[u];
+        if (u < row_hi) {
             iu = A.s.invn[u];
             fr = (int32_t)(u / g.P);
-            if (th == -INFINITY) {
-                thr = -INFINITY;
-            } else if (iu > 0.f) {
-                const float t = th / iu;
-                thr = t > 0.f ? t * (1.f - 0x1p-20f) : (t < 0.f ? t * (1.f + 0x1p-20f) : -1e-30f);
-            } else {
-                thr = th <= 0.f ? -INFINITY : INFINITY;
-            }
+            thr = scaled_threshold(A.s.theta[u], iu);
         }
         r_thr[tid] = thr;
         r_iu[tid] = iu;
         r_frame[tid] = fr;
         r_cnt[tid] = 0u;
+    } else if (MODE == SYM) {
+        const int t = tid - CT;
+        const int64_t v = col0 + t;
+        c_thr[t] = v < col_hi ? scaled_threshold(A.s.theta[v], A.s.invn[v]) : INFINITY;
+        c_cnt[t] = 0u;
     }
     const int32_t f_row_lo = (int32_t)(row0 / g.P);
-    const int32_t f_row_hi = (int32_t)((min<int64_t>(row0 + CT, g.Np) - 1) / g.P);
+    const int32_t f_row_hi = (int32_t)((min<int64_t>(row0 + CT, row_hi) - 1) / g.P);
     const int32_t f_col_lo = (int32_t)(col0 / g.P);
-    const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, A.col_hi) - 1) / g.P);
+    const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, col_hi) - 1) / g.P);
     const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
     u32x4 ar[4], br[4];
@@ -189,8 +230,8 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         for (int i = 0; i < 4; ++i) {
             const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
             const int64_t u = row0 + row, v = col0 + row;
-            ar[i] = u < g.Np ? *(const u32x4 *)(F + u * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
-            br[i] = v < A.col_hi ? *(const u32x4 *)(F + v * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            ar[i] = u < row_hi ? *(const u32x4 *)(F + u * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            br[i] = v < col_hi ? *(const u32x4 *)(F + v * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto store = [&](int buf) {
@@ -238,20 +279,20 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     }
 
     // ---- epilogue: lane holds column n of each block, rows per register.
+    // cosine = acc * (|f_u|^-1 |f_v|^-1), the same product in every mode.
     float iv[4];
     int32_t fv[4];
-    const int32_t vcol0 = (int32_t)(col0 + 128 * wc + n);  // column of block bj: vcol0 + 32 bj
+    const int32_t lc0 = 128 * wc + n;                   // local column of block bj: lc0 + 32 bj
+    const int32_t vcol0 = (int32_t)(col0 + lc0);
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
         const int64_t v = vcol0 + 32 * bj;
-        const bool vok = v < A.col_hi;
+        const bool vok = v < col_hi;
         iv[bj] = vok ? A.s.invn[v] : __builtin_nanf("");  // NaN never passes a comparison
         fv[bj] = vok ? (int32_t)(v / g.P) : -2;
     }
 
-    if (SEED) {
-        // every candidate of the seed frames is kept; its slot in the row's
-        // buffer is fixed: the seed columns, own frame removed
+    if (MODE == SEED) {
 #pragma unroll
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
@@ -264,7 +305,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                     const int32_t v = vcol0 + 32 * bj;
                     if (fr >= 0 && fv[bj] >= 0 && fr != fv[bj]) {
                         const int32_t slot = (fv[bj] > fr) ? v - g.P : v;
-                        const float c = acc[bi][bj][r] * iv[bj] * iu;
+                        const float c = acc[bi][bj][r] * (iu * iv[bj]);
                         A.s.cand[(row0 + lr) * A.cap + slot] = make_float2(c, __int_as_float(v));
                     }
                 }
@@ -272,39 +313,54 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         return;
     }
 
-    // filtered phase.  Fast path per 32 x 32 block: a 16-bit mask of the
-    // lane's values that pass their row's threshold.  Lanes with a hit spill
-    // their 16 scores to LDS and stage each hit in its row's LDS list; one
-    // global atomic per row then reserves the row's buffer slots.
+    // Fast path per 32 x 32 block: 16-bit masks of the lane's values that
+    // reach their row's threshold (forward) and, in SYM mode, its column's
+    // threshold (transposed).  Lanes with a hit spill their 16 accumulators to
+    // LDS and stage each hit in the receiving row's LDS list; one global atomic
+    // per row then reserves the row's buffer slots.
     __syncthreads();  // operand tiles are no longer read: reuse them
-    float2 *stage = (float2 *)smem;                                  // [CT][kRowCap]
-    float *xl = (float *)((char *)smem + sizeof(float2) * CT * kRowCap) + (wave * 64 + lane) * 16;
+    float2 *stage = (float2 *)smem;                              // [CT][kRowCap] forward
+    float2 *cstage = stage + CT * kRowCap;                       // [CT][kRowCap] transposed
+    float *xl = (float *)(cstage + (MODE == SYM ? CT * kRowCap : 0)) + (wave * 64 + lane) * 16;
+    const bool transposed = MODE == SYM && !diag;
+    auto push = [&](uint32_t *cnt_lds, float2 *lst, int li, int64_t grow, float2 e) {
+        const uint32_t slot = atomicAdd(&cnt_lds[li], 1u);
+        if (slot < (uint32_t)kRowCap) {
+            lst[li * kRowCap + slot] = e;
+        } else {  // rare: more than kRowCap hits of one row in one tile
+            const uint32_t gs = atomicAdd(&A.s.cnt[grow], 1u);
+            if (gs < (uint32_t)A.cap) A.s.cand[grow * A.cap + gs] = e;
+        }
+    };
     const float *thr_base = r_thr + 64 * wr + 4 * gq;
+    const float *iu_base = r_iu + 64 * wr + 4 * gq;
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
-            uint32_t k = 0;
+            uint32_t kf = 0, kt = 0;
+            const float cth = transposed ? c_thr[lc0 + 32 * bj] : INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                k |= (acc[bi][bj][r] * iv[bj] >= thr_base[32 * bi + 8 * (r >> 2) + (r & 3)]) ? (1u << r) : 0u;
-            if (k) {
+            for (int r = 0; r < 16; ++r) {
+                const int o = 32 * bi + 8 * (r >> 2) + (r & 3);
+                kf |= (acc[bi][bj][r] * iv[bj] >= thr_base[o]) ? (1u << r) : 0u;
+                if (transposed) kt |= (acc[bi][bj][r] * iu_base[o] >= cth) ? (1u << r) : 0u;
+            }
+            if (kf | kt) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xl[r] = acc[bi][bj][r] * iv[bj];
+                for (int r = 0; r < 16; ++r) xl[r] = acc[bi][bj][r];
+                const int lc = lc0 + 32 * bj;
                 const int32_t v = vcol0 + 32 * bj;
+                uint32_t k = kf | kt;
                 while (k) {
                     const int r = __ffs(k) - 1;
                     k &= k - 1;
                     const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
                     if (overlap && r_frame[lr] == fv[bj]) continue;  // own frame
-                    const float2 e = make_float2(xl[r] * r_iu[lr], __int_as_float(v));
-                    const uint32_t slot = atomicAdd(&r_cnt[lr], 1u);
-                    if (slot < (uint32_t)kRowCap) {
-                        stage[lr * kRowCap + slot] = e;
-                    } else {  // rare: more than kRowCap hits of one row in one tile
-                        const uint32_t gs = atomicAdd(&A.s.cnt[row0 + lr], 1u);
-                        if (gs < (uint32_t)A.cap) A.s.cand[(row0 + lr) * A.cap + gs] = e;
-                    }
+                    const float c = xl[r] * (r_iu[lr] * iv[bj]);
+                    if ((kf >> r) & 1u) push(r_cnt, stage, lr, row0 + lr, make_float2(c, __int_as_float(v)));
+                    if ((kt >> r) & 1u)
+                        push(c_cnt, cstage, lc, (int64_t)v, make_float2(c, __int_as_float((int32_t)(row0 + lr))));
                 }
             }
         }
@@ -317,6 +373,15 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             const uint32_t base = atomicAdd(&A.s.cnt[u], nloc);
             for (uint32_t i = 0; i < nloc; ++i)
                 if (base + i < (uint32_t)A.cap) A.s.cand[u * A.cap + base + i] = stage[tid * kRowCap + i];
+        }
+    } else if (transposed) {
+        const int t = tid - CT;
+        const uint32_t nloc = min(c_cnt[t], (uint32_t)kRowCap);
+        if (nloc) {
+            const int64_t v = col0 + t;
+            const uint32_t base = atomicAdd(&A.s.cnt[v], nloc);
+            for (uint32_t i = 0; i < nloc; ++i)
+                if (base + i < (uint32_t)A.cap) A.s.cand[v * A.cap + base + i] = cstage[t * kRowCap + i];
         }
     }
 }
@@ -478,6 +543,10 @@ __global__ __launch_bounds__(256) void finalize_rows(const Args A, uint32_t lo_c
     const uint32_t c = A.s.cnt[u];
     if (c <= lo_cnt || c > hi_cnt) return;
     if (A.s.over[u] || c > (uint32_t)A.cap) return;  // exact per-row engine
+    if (c > 64u * MAXE) {  // more than fits the registers: exact per-row engine
+        if (lane == 0) A.s.over[u] = 1u;
+        return;
+    }
     const int nn = (int)c;
     if (nn < A.K) {  // cannot happen without an overflow; recompute exactly
         if (lane == 0) A.s.over[u] = 1u;
@@ -545,9 +614,22 @@ template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(cons
 
 }  // namespace
 
+// Start of the symmetric square: the first doubling boundary W (2P, 4P, ...)
+// with Np - W <= 12 W, so that every row's threshold comes from at least a
+// thirteenth of the columns before the square is visited in one pass.
+int64_t corr_sym_start(const Geom &g) {
+    int64_t b = std::min<int64_t>(g.Np, 2 * (int64_t)g.P);
+    while (b < g.Np && g.Np - b > 12 * b) b *= 2;
+    return std::min<int64_t>(b, g.Np);
+}
+
 int32_t corr_capacity(const Geom &g, int32_t K) {
-    // the seed phase stores two frames' candidates; later phases add ~K-2K
+    // the seed phase stores two frames' candidates; a doubling phase adds
+    // ~K; the symmetric pass adds ~K (Np - W) / W with thresholds from W
+    const int64_t W = corr_sym_start(g);
+    const int64_t ratio = W < g.Np ? (g.Np - W + W - 1) / W : 0;
     int64_t cap = std::max<int64_t>(2 * (int64_t)g.P, 8 * (int64_t)K);
+    cap = std::max<int64_t>(cap, (int64_t)K * (2 * ratio + 1) + 256);
     cap = (cap + 63) / 64 * 64;
     return (int32_t)cap;
 }
@@ -568,11 +650,12 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.K = B.K;
     A.cap = B.cap;
     A.idx_out = B.idx_out;
-    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.cap <= 64 * 64 && B.K <= 1024;
+    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024;
     A.all_rows_fallback = gemm ? 0 : 1;
     A.s = carve(B.scratch, B.g.Np, B.cap);
     const int64_t Np = B.g.Np;
     A.seed_cols = std::min<int64_t>(Np, 2 * (int64_t)B.g.P);
+    A.sym_lo = corr_sym_start(B.g);
     const unsigned rb = (unsigned)((Np + 3) / 4);
     if (B.dino_dtype == BF16)
         hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
@@ -580,31 +663,44 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
         hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
     if (gemm) {
         const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
-        const uint32_t small = 16 * 64, big = 64 * 64;
+        const uint32_t small = 16 * 64;
         auto compact = [&]() { hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A); };
-        auto blocks_for = [&](int64_t lo, int64_t hi) {
-            const int64_t tiles = ((Np + CT - 1) / CT) * ((hi - lo + CT - 1) / CT);
-            return (unsigned)(8 * ((tiles + 7) / 8));
-        };
-        // seed phase: frames 0 and 1, every candidate kept
-        A.col_lo = 0;
-        A.col_hi = A.seed_cols;
-        hipLaunchKernelGGL(cos_phase<true>, dim3(blocks_for(0, A.seed_cols)), dim3(kCosThreads), 0, stream, A);
-        compact();
-        // doubling filtered phases
-        int64_t lo = A.seed_cols, hi = 2 * A.seed_cols;
-        while (lo < Np) {
-            hi = std::min<int64_t>(hi, Np);
-            A.col_lo = lo;
-            A.col_hi = hi;
-            hipLaunchKernelGGL(cos_phase<false>, dim3(blocks_for(lo, hi)), dim3(kCosThreads), 0, stream, A);
+        auto rect = [&](int mode, int64_t r_lo, int64_t r_hi, int64_t c_lo, int64_t c_hi) {
+            A.row_lo = r_lo;
+            A.row_hi = r_hi;
+            A.col_lo = c_lo;
+            A.col_hi = c_hi;
+            const int64_t tiles = ((r_hi - r_lo + CT - 1) / CT) * ((c_hi - c_lo + CT - 1) / CT);
+            const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
+            if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+            if (mode == SEED)
+                hipLaunchKernelGGL(cos_phase<SEED>, grid, dim3(kCosThreads), 0, stream, A);
+            else
+                hipLaunchKernelGGL(cos_phase<FILTER>, grid, dim3(kCosThreads), 0, stream, A);
+            if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
             compact();
-            lo = hi;
-            hi = 2 * hi;
+        };
+        const int64_t W = A.sym_lo;
+        // 1. seed: frames 0 and 1 for every row, every candidate kept
+        rect(SEED, 0, Np, 0, A.seed_cols);
+        // 2. doubling filtered phases for every row up to W
+        for (int64_t lo = A.seed_cols; lo < W; lo = std::min<int64_t>(2 * lo, W))
+            rect(FILTER, 0, Np, lo, std::min<int64_t>(2 * lo, W));
+        if (W < Np) {
+            // 3. rows below W keep doubling over the remaining columns
+            for (int64_t lo = W; lo < Np; lo = std::min<int64_t>(2 * lo, Np))
+                rect(FILTER, 0, W, lo, std::min<int64_t>(2 * lo, Np));
+            // 4. the square [W, Np)^2 once per unordered pair
+            const int64_t nt = (Np - W + CT - 1) / CT;
+            const int64_t tiles = nt * (nt + 1) / 2;
+            if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+            hipLaunchKernelGGL(cos_phase<SYM>, dim3((unsigned)(8 * ((tiles + 7) / 8))), dim3(kCosThreads), 0,
+                               stream, A);
+            if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+            compact();
         }
         hipLaunchKernelGGL(finalize_rows<16>, dim3(cb), dim3(256), 0, stream, A, 0u, small);
-        if ((uint32_t)A.cap > small)
-            hipLaunchKernelGGL(finalize_rows<64>, dim3(cb), dim3(256), 0, stream, A, small, big);
+        hipLaunchKernelGGL(finalize_rows<64>, dim3(cb), dim3(256), 0, stream, A, small, 0xFFFFFFFFu);
     }
     const unsigned fb = (unsigned)std::min<int64_t>(kFallbackBlocks, Np);
     if (B.dino_dtype == BF16)

@@ -98,6 +98,10 @@ struct CorrBuild {
     int32_t cap;    // candidate capacity per row
     int32_t *idx_out;   // [Np, K]
     void *scratch;      // corr_scratch_bytes()
+    // optional tracing hook: called with begin = 1 / 0 around every cosine
+    // GEMM launch (the caller records events on the stream)
+    void (*mark)(void *user, int begin, const char *name, hipStream_t stream);
+    void *mark_user;
 };
 size_t corr_scratch_bytes(const Geom &g, int32_t K, int32_t cap);
 int32_t corr_capacity(const Geom &g, int32_t K);
