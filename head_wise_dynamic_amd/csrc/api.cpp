@@ -25,6 +25,9 @@ struct saf_ctx {
     size_t corr_bytes = 0;
     void *corr_scratch = nullptr;
     size_t corr_scratch_bytes = 0;
+    // side stream for the gather path (default priority), fork/join events
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_vert = nullptr, ev_join = nullptr;
     // per-launch timing
     bool timing = false;
     struct Rec {
@@ -105,7 +108,7 @@ saf_status_t hip_fail(saf_ctx_t *c, hipError_t e, const char *what) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int QT = 128;           // query tile of the matrix-core kernel
+constexpr int QT = saf::kQueryTile;  // query tile of the matrix-core kernel
 constexpr int kSplitKeys = 8192;  // keys per split for dense special rows
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -233,6 +236,13 @@ void saf_destroy(saf_ctx_t *c) {
         (void)hipEventDestroy(r.b);
     }
     for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
+    if (c->side) {
+        (void)hipStreamSynchronize(c->side);
+        (void)hipStreamDestroy(c->side);
+    }
+    if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+    if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+    if (c->ev_vert) (void)hipEventDestroy(c->ev_vert);
     if (c->corr_idx || c->corr_scratch) {
         (void)hipDeviceSynchronize();
         if (c->corr_idx) (void)hipFree(c->corr_idx);
@@ -413,8 +423,12 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
     hipStream_t s = as_stream(stream);
     char *wp = (char *)ws;
     if (wp) wp = (char *)(((uintptr_t)wp + 255) & ~(uintptr_t)255);
-    // 1. vertical key sets
+
+    // 1. vertical key sets: given by the caller, or built here (one batch)
     std::vector<const int32_t *> vlist(g.H, nullptr);
+    std::vector<int32_t> vheads, vK;
+    std::vector<int32_t *> vout;
+    std::vector<void *> vws;
     for (int h = 0; h < g.H; ++h) {
         if (plan[h].role != SAF_VERTICAL) continue;
         if (vert_idx) {
@@ -423,20 +437,24 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         }
         int32_t *idx = (int32_t *)wp;
         wp += align256(sizeof(int32_t) * g.N);
-        void *vws = wp;
+        vws.push_back(wp);
         wp += align256(saf::vertical_ws_bytes(g.N));
-        hipError_t e;
-        {
-            Timed tm(c, s, "vertical_index");
-            e = saf::launch_vertical_index(g, q, k, lay.head_stride, lay.token_stride, h, plan[h].budget, idx,
-                                           vws, s);
-        }
-        if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
+        vheads.push_back(h);
+        vK.push_back(plan[h].budget);
+        vout.push_back(idx);
         vlist[h] = idx;
     }
+    auto build_vertical = [&](hipStream_t st) -> hipError_t {
+        if (vheads.empty()) return hipSuccess;
+        Timed tm(c, st, "vertical_index");
+        return saf::launch_vertical_batch(g, q, k, lay.head_stride, lay.token_stride, (int)vheads.size(),
+                                          vheads.data(), vK.data(), vout.data(), vws.data(), st);
+    };
 
     if (g.dtype == saf::F32) {
-        // fp32: every head on the VALU row kernel
+        // fp32: every head on the VALU row kernel, in stream order
+        hipError_t e = build_vertical(s);
+        if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
         saf::ValuLaunch L{};
         L.g = g;
         L.q = q;
@@ -461,7 +479,6 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
                 w.list_len = plan[h].role == SAF_VERTICAL ? (int32_t)std::min<int64_t>(plan[h].budget, g.N) : 0;
                 w.nsplit = 1;
             }
-            hipError_t e;
             {
                 Timed tm(c, s, "valu_attention");
                 e = saf::launch_valu_attention(L, g.N, s);
@@ -471,11 +488,84 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         return SAF_OK;
     }
 
-    // 2. bf16: shared-key heads on the matrix cores, ordered by key-set size
+    // 2. bf16.  A side stream (default priority) runs the HBM-bound work --
+    // the vertical probe + top-K, then the correspondence heads' gathered
+    // rows -- while the caller's stream runs the matrix-core kernel for the
+    // heads that do not wait for the vertical sets; the vertical heads follow
+    // once their sets exist, and the caller's stream joins the side stream at
+    // the end of the call.
+    bool forked = false;
+    if (pi.ncorr || !vheads.empty()) {
+        if (!c->side) {
+            if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+                hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&c->ev_vert, hipEventDisableTiming) != hipSuccess ||
+                hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) {
+                (void)hipGetLastError();
+                if (c->side) (void)hipStreamDestroy(c->side);
+                c->side = nullptr;
+            }
+        }
+        if (c->side && hipEventRecord(c->ev_fork, s) == hipSuccess &&
+            hipStreamWaitEvent(c->side, c->ev_fork, 0) == hipSuccess)
+            forked = true;
+    }
+    const hipStream_t ss = forked ? c->side : s;
+    // every return from here on first joins the side stream
+    struct Join {
+        saf_ctx *c;
+        hipStream_t s;
+        bool armed;
+        ~Join() {
+            if (armed) {
+                (void)hipEventRecord(c->ev_join, c->side);
+                (void)hipStreamWaitEvent(s, c->ev_join, 0);
+            }
+        }
+    } join{c, s, forked};
+
+    hipError_t e = build_vertical(ss);
+    if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
+    if (forked && !vheads.empty()) (void)hipEventRecord(c->ev_vert, ss);
+    if (pi.ncorr) {
+        saf::ValuLaunch L{};
+        L.g = g;
+        L.q = q;
+        L.k = k;
+        L.v = v;
+        L.o = o;
+        L.head_stride = lay.head_stride;
+        L.token_stride = lay.token_stride;
+        L.corr_idx = c->corr_idx;
+        L.corr_k = c->corr_k;
+        L.patch_rows_only = 1;
+        L.nwork = 0;
+        for (int h = 0; h < g.H && e == hipSuccess; ++h) {
+            if (plan[h].role != SAF_CORRESPONDENCE) continue;
+            if (L.nwork == saf::kMaxWork) {
+                Timed tm(c, ss, "gather_attention");
+                e = saf::launch_valu_attention(L, g.Np, ss);
+                L.nwork = 0;
+            }
+            saf::HeadWork &w = L.work[L.nwork++];
+            w = saf::HeadWork{};
+            w.head = h;
+            w.role = SAF_CORRESPONDENCE;
+            w.nsplit = 1;
+        }
+        if (e == hipSuccess && L.nwork) {
+            Timed tm(c, ss, "gather_attention");
+            e = saf::launch_valu_attention(L, g.Np, ss);
+        }
+        if (e != hipSuccess) return hip_fail(c, e, "gather attention kernel");
+    }
+
+    // shared-key heads on the matrix cores, longest key sets first
     struct Item {
         saf::HeadWork w;
         int64_t tiles;
         double cost;
+        bool needs_vertical;
     };
     std::vector<Item> items;
     const int64_t tpf = (g.T + QT - 1) / QT;
@@ -500,6 +590,7 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
             w.list_len = (int32_t)std::min<int64_t>(plan[h].budget, g.N);
             it.tiles = all_tiles;
             it.cost = w.list_len;
+            it.needs_vertical = !vert_idx;
             break;
         case SAF_SCANNING:
             w.rows = saf::ROWS_ALL;
@@ -532,71 +623,42 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
     M.o = o;
     M.head_stride = lay.head_stride;
     M.token_stride = lay.token_stride;
-    for (size_t i0 = 0; i0 < items.size(); i0 += saf::kMaxWork) {
-        M.nwork = 0;
-        int64_t blocks = 0;
-        for (size_t i = i0; i < std::min(items.size(), i0 + saf::kMaxWork); ++i) {
-            saf::HeadWork w = items[i].w;
-            if (w.nsplit > 1) {
-                w.part = (float *)wp;
-                wp += split_part_bytes(g, w.nsplit);
-            }
-            w.block0 = (int32_t)blocks;
-            blocks += items[i].tiles * w.nsplit;
-            M.work[M.nwork++] = w;
+    for (int pass = 0; pass < 2; ++pass) {
+        // pass 0: heads that need nothing; pass 1: vertical heads built here
+        std::vector<Item> sel;
+        for (const Item &it : items)
+            if (it.needs_vertical == (pass == 1)) sel.push_back(it);
+        if (sel.empty()) continue;
+        if (pass == 1 && forked) {
+            e = hipStreamWaitEvent(s, c->ev_vert, 0);
+            if (e != hipSuccess) return hip_fail(c, e, "hipStreamWaitEvent(vertical)");
         }
-        if (blocks >= ((int64_t)1 << 31)) return fail(c, SAF_EINVAL, "launch too large");
-        M.total_blocks = (int32_t)blocks;
-        hipError_t e;
-        {
-            Timed tm(c, s, "shared_attention");
-            e = saf::launch_mfma_attention(M, s);
-        }
-        if (e != hipSuccess) return hip_fail(c, e, "matrix-core attention kernel");
-        {
-            Timed tm(c, s, "split_combine");
-            e = saf::launch_split_combine(M, s);
-        }
-        if (e != hipSuccess) return hip_fail(c, e, "split combine kernel");
-    }
-
-    // 3. bf16: correspondence heads' patch rows on the gather path
-    if (pi.ncorr) {
-        saf::ValuLaunch L{};
-        L.g = g;
-        L.q = q;
-        L.k = k;
-        L.v = v;
-        L.o = o;
-        L.head_stride = lay.head_stride;
-        L.token_stride = lay.token_stride;
-        L.corr_idx = c->corr_idx;
-        L.corr_k = c->corr_k;
-        L.patch_rows_only = 1;
-        L.nwork = 0;
-        for (int h = 0; h < g.H; ++h) {
-            if (plan[h].role != SAF_CORRESPONDENCE) continue;
-            if (L.nwork == saf::kMaxWork) {
-                hipError_t e;
-                {
-                    Timed tm(c, s, "gather_attention");
-                    e = saf::launch_valu_attention(L, g.Np, s);
+        for (size_t i0 = 0; i0 < sel.size(); i0 += saf::kMaxWork) {
+            M.nwork = 0;
+            int64_t blocks = 0;
+            for (size_t i = i0; i < std::min(sel.size(), i0 + saf::kMaxWork); ++i) {
+                saf::HeadWork w = sel[i].w;
+                if (w.nsplit > 1) {
+                    w.part = (float *)wp;
+                    wp += split_part_bytes(g, w.nsplit);
                 }
-                if (e != hipSuccess) return hip_fail(c, e, "gather attention kernel");
-                L.nwork = 0;
+                w.block0 = (int32_t)blocks;
+                blocks += sel[i].tiles * w.nsplit;
+                M.work[M.nwork++] = w;
             }
-            saf::HeadWork &w = L.work[L.nwork++];
-            w = saf::HeadWork{};
-            w.head = h;
-            w.role = SAF_CORRESPONDENCE;
-            w.nsplit = 1;
+            if (blocks >= ((int64_t)1 << 31)) return fail(c, SAF_EINVAL, "launch too large");
+            M.total_blocks = (int32_t)blocks;
+            {
+                Timed tm(c, s, "shared_attention");
+                e = saf::launch_mfma_attention(M, s);
+            }
+            if (e != hipSuccess) return hip_fail(c, e, "matrix-core attention kernel");
+            {
+                Timed tm(c, s, "split_combine");
+                e = saf::launch_split_combine(M, s);
+            }
+            if (e != hipSuccess) return hip_fail(c, e, "split combine kernel");
         }
-        hipError_t e;
-        {
-            Timed tm(c, s, "gather_attention");
-            e = saf::launch_valu_attention(L, g.Np, s);
-        }
-        if (e != hipSuccess) return hip_fail(c, e, "gather attention kernel");
     }
     return SAF_OK;
 }

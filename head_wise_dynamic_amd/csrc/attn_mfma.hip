@@ -8,7 +8,8 @@
 // Sec. 4.1) on CDNA4 matrix cores: the selected keys are gathered by token
 // index straight into LDS tiles, so no packed copy of K/V is ever written.
 //
-// Work-group = 4 waves = 128 query rows (32 per wave); key tiles of 64.
+// Work-group = 4 waves = 256 query rows (64 per wave, as two 32-row blocks
+// that share every K and V fragment read from LDS); key tiles of 64.
 // Per wave and tile, S^T = K Q^T is formed with v_mfma_f32_32x32x16_bf16 so
 // that a lane owns one query column: the online softmax (running max m, sum l)
 // needs one cross-lane exchange (lane ^ 32) per tile.  The key rows of the
@@ -22,7 +23,7 @@
 namespace saf {
 namespace {
 
-constexpr int QT = 128;
+constexpr int QT = kQueryTile;
 constexpr int KT = 64;
 constexpr int KROW = 72;   // K tile row in LDS: 64 bf16 + 8 pad
 constexpr int VROW = 72;   // V^T tile row in LDS: 64 keys + 8 pad
@@ -67,7 +68,9 @@ __device__ __forceinline__ RowMap make_rowmap(const HeadWork &w, const Geom &g, 
     return rm;
 }
 
-__global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
+constexpr int kAttnThreads = 256;  // 4 waves x 64 query rows
+
+__global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLaunch L) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][64 * VROW];
     __shared__ float kbias[2][KT];
@@ -99,61 +102,75 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
     const int64_t kend = min<int64_t>(count, kbeg + per);
     const int64_t first_masked = key_first_masked(w, g);
 
-    // ---- this lane's query row as the B operand (4 k-steps of 16 channels)
-    const int qr = wave * 32 + n;
-    const bool qvalid = qr < rm.valid;
-    const int64_t qtok = qvalid ? tile_row(rm, g, qr) : 0;
-    bf16x8 qreg[4];
+    // ---- this wave's 64 query rows as two 32-row B operands (4 k-steps each)
+    bool qvalid[2];
+    int64_t qtok[2];
+    bf16x8 qreg[2][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qvalid) raw = *(const u32x4 *)(Q + qtok * ts + 16 * c + 8 * gq);
-        qreg[c] = __builtin_bit_cast(bf16x8, raw);
+    for (int qb = 0; qb < 2; ++qb) {
+        const int qr = wave * 64 + 32 * qb + n;
+        qvalid[qb] = qr < rm.valid;
+        qtok[qb] = qvalid[qb] ? tile_row(rm, g, qr) : 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            u32x4 raw = {0u, 0u, 0u, 0u};
+            if (qvalid[qb]) raw = *(const u32x4 *)(Q + qtok[qb] * ts + 16 * c + 8 * gq);
+            qreg[qb][c] = __builtin_bit_cast(bf16x8, raw);
+        }
     }
 
     const float sc = kLog2e * 0.125f;  // log2(e) / sqrt(64)
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 oacc[2];
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    f32x16 oacc[2][2];  // [query block][channel block]
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
 
-    // ---- tile loader: thread handles key rows 2p and 2p+1 (p = tid / 8) at
-    // channel segment seg = tid % 8, so V^T can be written two keys per
-    // 32-bit LDS store
-    u32x4 kreg[2], vreg[2];
-    bool kval[2];
-    const int lp = tid >> 3, lseg = tid & 7;
+    // ---- tile loader: unit = (key pair p, channel segment seg), one unit
+    // per thread; V^T is written two keys per 32-bit LDS store
+    constexpr int kUnits = (KT / 2) * 8 / kAttnThreads;
+    u32x4 kreg[kUnits][2], vreg[kUnits][2];
+    bool kval[kUnits][2];
     auto load_tile = [&](int64_t kt) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t m = kt + 2 * lp + i;
-            int64_t tok = -1;
-            if (m < kend) tok = key_token(w, g, m, rm.qframe);
-            kval[i] = tok >= 0;
-            if (tok >= 0) {
-                kreg[i] = *(const u32x4 *)(K + tok * ts + 8 * lseg);
-                vreg[i] = *(const u32x4 *)(V + tok * ts + 8 * lseg);
-            } else {
-                kreg[i] = u32x4{0u, 0u, 0u, 0u};
-                vreg[i] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < kUnits; ++j) {
+            const int unit = tid + kAttnThreads * j, lp = unit >> 3, lseg = unit & 7;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int64_t m = kt + 2 * lp + i;
+                int64_t tok = -1;
+                if (m < kend) tok = key_token(w, g, m, rm.qframe);
+                kval[j][i] = tok >= 0;
+                if (tok >= 0) {
+                    kreg[j][i] = *(const u32x4 *)(K + tok * ts + 8 * lseg);
+                    vreg[j][i] = *(const u32x4 *)(V + tok * ts + 8 * lseg);
+                } else {
+                    kreg[j][i] = u32x4{0u, 0u, 0u, 0u};
+                    vreg[j][i] = u32x4{0u, 0u, 0u, 0u};
+                }
             }
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * lseg]) = kreg[i];
-        uint32_t *vt = (uint32_t *)&Vt[buf][(8 * lseg) * VROW + 2 * lp];
+        for (int j = 0; j < kUnits; ++j) {
+            const int unit = tid + kAttnThreads * j, lp = unit >> 3, lseg = unit & 7;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // channels 2e and 2e+1 of the two keys
-            vt[(2 * e) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[1][e], vreg[0][e], 0x05040100u);
-            vt[(2 * e + 1) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[1][e], vreg[0][e], 0x07060302u);
-        }
-        if (lseg == 0) {
-            kbias[buf][2 * lp] = kval[0] ? 0.f : -INFINITY;
-            kbias[buf][2 * lp + 1] = kval[1] ? 0.f : -INFINITY;
+            for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * lseg]) = kreg[j][i];
+            uint32_t *vt = (uint32_t *)&Vt[buf][(8 * lseg) * VROW + 2 * lp];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // channels 2e and 2e+1 of the two keys
+                vt[(2 * e) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[j][1][e], vreg[j][0][e], 0x05040100u);
+                vt[(2 * e + 1) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[j][1][e], vreg[j][0][e], 0x07060302u);
+            }
+            if (lseg == 0) {
+                kbias[buf][2 * lp] = kval[j][0] ? 0.f : -INFINITY;
+                kbias[buf][2 * lp + 1] = kval[j][1] ? 0.f : -INFINITY;
+            }
         }
     };
 
@@ -169,17 +186,22 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
         const int64_t kt = kbeg + t * KT;
         if (t + 1 < ntiles) load_tile(kt + KT);
 
-        // S^T = K Q^T for the two 32-key blocks of this tile
-        f32x16 s[2];
+        // S^T = K Q^T: two 32-key blocks x two 32-query blocks; each K
+        // fragment feeds both query blocks
+        f32x16 s[2][2];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[bb][r] = 0.f;
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[bb][qb][r] = 0.f;
             const uint16_t *krow = &Ks[buf][(32 * bb + swap_bits23(n)) * KROW + 8 * gq];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const bf16x8 a = *(const bf16x8 *)(krow + 16 * c);
-                s[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], s[bb], 0, 0, 0);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    s[bb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][c], s[bb][qb], 0, 0, 0);
             }
         }
         // masked slots: ragged tail, or specials already on the scanning stride
@@ -187,54 +209,67 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[bb][r] += kbias[buf][32 * bb + 16 * (r >> 3) + 8 * gq + (r & 7)];
+                for (int r = 0; r < 16; ++r) {
+                    const float bias = kbias[buf][32 * bb + 16 * (r >> 3) + 8 * gq + (r & 7)];
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) s[bb][qb][r] += bias;
+                }
         }
-        // online softmax (log2 domain).  The running max is only raised when
-        // a logit exceeds it by more than 8 (weights stay <= 2^8), so the
-        // O rescale is skipped on most tiles.
-        float mx = s[0][0];
+        // online softmax per query block (log2 domain).  The running max is
+        // only raised when a logit exceeds it by more than 8 (weights stay
+        // <= 2^8), so the O rescale is skipped on most tiles.
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+        for (int qb = 0; qb < 2; ++qb) {
+            float mx = s[0][qb][0];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
-        if (__any(mx > m_run + 8.f)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-            l_run *= alpha;
+            for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][qb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+            if (__any(mx > m_run[qb] + 8.f)) {
+                const float m_new = fmaxf(m_run[qb], mx);
+                const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
+                l_run[qb] *= alpha;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float lsum = 0.f;
+                for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(s[bb][r], sc, -m_use));
-                s[bb][r] = p;
-                lsum += p;
+                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+                m_run[qb] = m_new;
             }
-        l_run += lsum;
+            const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+            float lsum = 0.f;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = fast_exp2(fmaf(s[bb][qb][r], sc, -m_use));
+                    s[bb][qb][r] = p;
+                    lsum += p;
+                }
+            l_run[qb] += lsum;
+        }
 
-        // O^T += V^T P^T, four k-steps of 16 keys
+        // O^T += V^T P^T, four k-steps of 16 keys; each V^T fragment feeds
+        // both query blocks
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int bb = e >> 1, h8 = (e & 1) * 8;
-            u32x4 pk;
-            pk[0] = pack_bf16x2(s[bb][h8 + 0], s[bb][h8 + 1]);
-            pk[1] = pack_bf16x2(s[bb][h8 + 2], s[bb][h8 + 3]);
-            pk[2] = pack_bf16x2(s[bb][h8 + 4], s[bb][h8 + 5]);
-            pk[3] = pack_bf16x2(s[bb][h8 + 6], s[bb][h8 + 7]);
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pk);
+            bf16x8 pb[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                u32x4 pk;
+                pk[0] = pack_bf16x2(s[bb][qb][h8 + 0], s[bb][qb][h8 + 1]);
+                pk[1] = pack_bf16x2(s[bb][qb][h8 + 2], s[bb][qb][h8 + 3]);
+                pk[2] = pack_bf16x2(s[bb][qb][h8 + 4], s[bb][qb][h8 + 5]);
+                pk[3] = pack_bf16x2(s[bb][qb][h8 + 6], s[bb][qb][h8 + 7]);
+                pb[qb] = __builtin_bit_cast(bf16x8, pk);
+            }
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
                 const bf16x8 a = *(const bf16x8 *)(&Vt[buf][(32 * db + n) * VROW + 16 * e + 8 * gq]);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
             }
         }
 
@@ -242,36 +277,39 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(const MfmaLaunch L) {
         __syncthreads();
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (!qvalid) return;
-
-    if (w.nsplit == 1) {
-        const float inv = 1.f / l_tot;
-        uint16_t *O = (uint16_t *)L.o + hoff + qtok * ts;
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+    for (int qb = 0; qb < 2; ++qb) {
+        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
+        if (!qvalid[qb]) continue;
+        const int qr = wave * 64 + 32 * qb + n;
+        if (w.nsplit == 1) {
+            const float inv = 1.f / l_tot;
+            uint16_t *O = (uint16_t *)L.o + hoff + qtok[qb] * ts;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d0 = 32 * db + 8 * q4 + 4 * gq;
-                u32x2 pk;
-                pk[0] = pack_bf16x2(oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv);
-                pk[1] = pack_bf16x2(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
-                *(u32x2 *)(O + d0) = pk;
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d0 = 32 * db + 8 * q4 + 4 * gq;
+                    u32x2 pk;
+                    pk[0] = pack_bf16x2(oacc[qb][db][4 * q4 + 0] * inv, oacc[qb][db][4 * q4 + 1] * inv);
+                    pk[1] = pack_bf16x2(oacc[qb][db][4 * q4 + 2] * inv, oacc[qb][db][4 * q4 + 3] * inv);
+                    *(u32x2 *)(O + d0) = pk;
+                }
+        } else {
+            float *rec = w.part + ((int64_t)(tile * QT + qr) * w.nsplit + split) * PSTRIDE;
+            if (gq == 0) {
+                rec[0] = m_run[qb];
+                rec[1] = l_tot;
             }
-    } else {
-        float *rec = w.part + ((int64_t)(tile * QT + qr) * w.nsplit + split) * PSTRIDE;
-        if (gq == 0) {
-            rec[0] = m_run;
-            rec[1] = l_tot;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int d0 = 32 * db + 8 * q4 + 4 * gq;
+                    *(f32x4 *)(rec + 2 + d0) = f32x4{oacc[qb][db][4 * q4], oacc[qb][db][4 * q4 + 1],
+                                                     oacc[qb][db][4 * q4 + 2], oacc[qb][db][4 * q4 + 3]};
+                }
         }
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int d0 = 32 * db + 8 * q4 + 4 * gq;
-                *(f32x4 *)(rec + 2 + d0) =
-                    f32x4{oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
-            }
     }
 }
 
@@ -317,7 +355,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const MfmaLaunch L) 
 
 hipError_t launch_mfma_attention(const MfmaLaunch &L, hipStream_t stream) {
     if (L.total_blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(mfma_attn_kernel, dim3(L.total_blocks), dim3(256), 0, stream, L);
+    hipLaunchKernelGGL(mfma_attn_kernel, dim3(L.total_blocks), dim3(kAttnThreads), 0, stream, L);
     return hipGetLastError();
 }
 

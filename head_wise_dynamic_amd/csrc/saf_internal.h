@@ -45,6 +45,7 @@ struct HeadWork {
 };
 
 constexpr int kMaxWork = 24;
+constexpr int kQueryTile = 256;  // query rows per work-group of the matrix-core kernel
 
 struct MfmaLaunch {
     Geom g;
@@ -86,6 +87,10 @@ size_t vertical_ws_bytes(int64_t N);
 hipError_t launch_vertical_index(const Geom &g, const void *q, const void *k, int64_t head_stride,
                                  int64_t token_stride, int32_t head, int32_t K, int32_t *idx_out,
                                  void *ws, hipStream_t stream);
+// nh heads in one set of launches (grid.y = head)
+hipError_t launch_vertical_batch(const Geom &g, const void *q, const void *k, int64_t head_stride,
+                                 int64_t token_stride, int nh, const int32_t *heads, const int32_t *Ks,
+                                 int32_t *const *idx_out, void *const *ws, hipStream_t stream);
 
 // Correspondence index build (cosine top-K over other frames).
 struct CorrBuild {

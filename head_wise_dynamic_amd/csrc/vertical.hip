@@ -13,6 +13,8 @@
 //                      lowest-index keys equal to it.
 // All passes are HBM/L2 streaming; the pages call the probe's cost
 // negligible next to attention.
+#include <algorithm>
+
 #include "device_util.h"
 #include "topk_block.h"
 
@@ -115,33 +117,43 @@ size_t vertical_ws_bytes(int64_t N) {
            align256(sizeof(float) * N) + align256(sizeof(uint32_t) * kTopkScratch);
 }
 
+hipError_t launch_vertical_batch(const Geom &g, const void *q, const void *k, int64_t head_stride,
+                                 int64_t token_stride, int nh, const int32_t *heads, const int32_t *Ks,
+                                 int32_t *const *idx_out, void *const *ws, hipStream_t stream) {
+    for (int h0 = 0; h0 < nh; h0 += kMaxVert) {
+        VertBatch B{};
+        B.g = g;
+        B.q = q;
+        B.k = k;
+        B.head_stride = head_stride;
+        B.token_stride = token_stride;
+        B.nh = std::min(kMaxVert, nh - h0);
+        for (int i = 0; i < B.nh; ++i) {
+            B.head[i] = heads[h0 + i];
+            B.K[i] = Ks[h0 + i];
+            B.idx_out[i] = idx_out[h0 + i];
+            B.ws[i] = (char *)ws[h0 + i];
+        }
+        const unsigned n = (unsigned)B.nh;
+        if (g.dtype == BF16)
+            hipLaunchKernelGGL(probe_partial<uint16_t>, dim3(kProbeBlocks, n), dim3(256), 0, stream, B);
+        else
+            hipLaunchKernelGGL(probe_partial<float>, dim3(kProbeBlocks, n), dim3(256), 0, stream, B);
+        hipLaunchKernelGGL(probe_final, dim3(1, n), dim3(64), 0, stream, B);
+        const unsigned sb = (unsigned)((g.N + 31) / 32);
+        if (g.dtype == BF16)
+            hipLaunchKernelGGL(probe_scores<uint16_t>, dim3(sb, n), dim3(256), 0, stream, B);
+        else
+            hipLaunchKernelGGL(probe_scores<float>, dim3(sb, n), dim3(256), 0, stream, B);
+        hipLaunchKernelGGL(topk_select, dim3(1, n), dim3(1024), 0, stream, B);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_vertical_index(const Geom &g, const void *q, const void *k, int64_t head_stride,
                                  int64_t token_stride, int32_t head, int32_t K, int32_t *idx_out,
                                  void *ws, hipStream_t stream) {
-    VertBatch B{};
-    B.g = g;
-    B.q = q;
-    B.k = k;
-    B.head_stride = head_stride;
-    B.token_stride = token_stride;
-    B.nh = 1;
-    B.head[0] = head;
-    B.K[0] = K;
-    B.idx_out[0] = idx_out;
-    B.ws[0] = (char *)ws;
-    const unsigned nh = 1;
-    if (g.dtype == BF16)
-        hipLaunchKernelGGL(probe_partial<uint16_t>, dim3(kProbeBlocks, nh), dim3(256), 0, stream, B);
-    else
-        hipLaunchKernelGGL(probe_partial<float>, dim3(kProbeBlocks, nh), dim3(256), 0, stream, B);
-    hipLaunchKernelGGL(probe_final, dim3(1, nh), dim3(64), 0, stream, B);
-    const unsigned sb = (unsigned)((g.N + 31) / 32);
-    if (g.dtype == BF16)
-        hipLaunchKernelGGL(probe_scores<uint16_t>, dim3(sb, nh), dim3(256), 0, stream, B);
-    else
-        hipLaunchKernelGGL(probe_scores<float>, dim3(sb, nh), dim3(256), 0, stream, B);
-    hipLaunchKernelGGL(topk_select, dim3(1, nh), dim3(1024), 0, stream, B);
-    return hipGetLastError();
+    return launch_vertical_batch(g, q, k, head_stride, token_stride, 1, &head, &K, &idx_out, &ws, stream);
 }
 
 }  // namespace saf
