@@ -276,3 +276,96 @@ def test_config2_sampled():
 
 def test_config3_sampled():
     _big_config(3, 1024, 24)
+
+
+def test_config4_stack_reuses_index_across_layers():
+    """24-layer stack workload: the correspondence index is built once from
+    the DINO features and reused by a regular layer and a correspondence-heavy
+    layer (6 correspondence heads); vertical sets are rebuilt per layer."""
+    saf = _saf()
+    layers = [make_inputs(4, layer=9), make_inputs(4, layer=10)]
+    g = layers[0].geom
+    assert np.array_equal(layers[0].dino, layers[1].dino)
+    assert len(layers[1].heads(ROLE_CORRESPONDENCE)) == 6
+    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+    say("config 4: index build (once)")
+    ctx.build_corr_index(to_dev(layers[0].dino), layers[0].corr_K)
+    gidx = ctx.get_corr_index().cpu().numpy()
+    rows = sample_rows(g, 512, seed=4)
+    t = rows % g.T
+    pr = (rows // g.T) * g.P + t - g.ns
+    patch_rows = pr[t >= g.ns]
+    oidx, _, _ = oracle.corr_index(layers[0].dino, g.S, g.ns, g.P, layers[0].corr_K, patch_rows)
+    same = {int(u): np.array_equal(gidx[u], r) for u, r in zip(patch_rows, oidx)}
+    assert np.mean(list(same.values())) > 0.8
+    ok_rows = np.array([i for i, ti, u in zip(rows, t, pr) if ti < g.ns or same[int(u)]])
+    corr = {int(u): r for u, r in zip(patch_rows, oidx)}
+    for w in layers:
+        q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
+        say(f"config 4: {w.name}")
+        o = ctx.sparse_attention(w.plan, q, k, v)
+        torch.cuda.synchronize()
+        heads = []
+        for h, (role, budget, _, _) in enumerate(w.plan):
+            if role == ROLE_VERTICAL:
+                ids, r, _, _ = oracle.vertical_index(w.q[h], w.k[h], budget)
+                gv = ctx.build_vertical_index(q, k, h, budget).cpu().numpy()
+                band_check(r, gv, budget)
+                if not np.array_equal(ids, gv):
+                    continue
+            heads.append(h)
+        outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, corr_K=w.corr_K, rows=ok_rows,
+                                  corr_rows=corr, heads=heads)
+        got = to_host_f64(o)
+        for h in heads:
+            err = np.max(np.abs(got[h][ok_rows] - outs[h]))
+            assert err <= tol(w), (w.name, h, err)
+        del q, k, v, o
+    ctx.close()
+
+
+def test_config5_long_sequence_sampled():
+    """S = 500 frames (N = 650,500): one head per role drawn, sampled rows."""
+    saf = _saf()
+    heads = [0, 4, 7, 10]  # position, vertical, correspondence, scanning
+    w = make_inputs(5, heads=heads)
+    g = w.geom
+    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+    q, k, v, dino = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.dino)
+    say("config 5: vertical index")
+    K4 = w.plan[4][1]
+    gv = ctx.build_vertical_index(q, k, 4, K4).cpu().numpy()
+    ids, r, _, _ = oracle.vertical_index(w.q[4], w.k[4], K4)
+    band_check(r, gv, K4)
+    say("config 5: index build")
+    ctx.build_corr_index(dino, w.corr_K)
+    gidx = ctx.get_corr_index().cpu().numpy()
+    crow = np.random.default_rng(5).choice(g.Np, 12, replace=False)
+    sc = oracle.corr_scores(w.dino, g.S, g.P, crow)
+    frame = np.arange(g.Np) // g.P
+    for i, u in enumerate(crow):
+        gp = (gidx[u] // g.T) * g.P + gidx[u] % g.T - g.ns
+        band_check(np.nan_to_num(sc[i], nan=-np.inf), gp, w.corr_K, valid=frame != frame[u])
+    # rows: a few special rows, frame 0 edges, random patch rows
+    rng = np.random.default_rng(55)
+    rows = np.unique(np.concatenate([[0, 4, g.T, g.N - g.T, g.N - 1], np.arange(g.ns, g.ns + 8),
+                                     rng.choice(g.N, 192, replace=False)]))
+    t = rows % g.T
+    pr = (rows // g.T) * g.P + t - g.ns
+    oidx, _, _ = oracle.corr_index(w.dino, g.S, g.ns, g.P, w.corr_K, pr[t >= g.ns])
+    full = gidx.copy()
+    full[pr[t >= g.ns]] = oidx
+    ctx.set_corr_index(torch.from_numpy(full.astype(np.int32)).cuda())
+    vt = torch.zeros((g.H, len(ids)), dtype=torch.int32)
+    vt[4] = torch.from_numpy(ids.astype(np.int32))
+    say("config 5: layer with oracle sets")
+    o = ctx.sparse_attention(w.plan, q, k, v, vert_idx=vt.cuda())
+    torch.cuda.synchronize()
+    corr = {int(u): rr for u, rr in zip(pr[t >= g.ns], oidx)}
+    outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, corr_K=w.corr_K, rows=rows,
+                              corr_rows=corr, heads=heads)
+    got = to_host_f64(o)
+    for h in heads:
+        err = np.max(np.abs(got[h][rows] - outs[h]))
+        assert err <= tol(w), (h, err)
+    ctx.close()

@@ -11,7 +11,7 @@ What is drawn (one numpy PCG64 SeedSequence per workload, spawned into seven
 sub-streams in this order: latents, frame sampling, DINO noise, per-head
 projections W_h, Q/K/V, salient keys, probe directions):
 
-* M latent scene points z ~ N(0, I_Df).
+* M latent scene points z ~ N(0, I_Df).  Normal draws are float32.
 * Frame 0's patches take P distinct latents.  In every other frame,
   round(0.7 P) randomly placed patches take latents drawn without replacement
   from frame 0's set; the remaining patches take distinct latents from the
@@ -23,6 +23,8 @@ projections W_h, Q/K/V, salient keys, probe directions):
   - vertical-line heads: a unit direction u per head; 24 patch keys drawn
     uniformly get K += 4u and every query gets Q += u.
 * bf16 workloads are rounded to bfloat16 with round-to-nearest-even.
+* Each head draws from its own sub-streams (projection, Q/K/V, salient keys,
+  direction), spawned from the four per-layer streams.
 
 Nothing here computes key sets, scores or attention: this module only draws
 and lays out numbers, so it may feed both the oracle and the GPU path.
@@ -180,8 +182,11 @@ def make_geometry_inputs(geom: Geometry, dtype: str, roles: Sequence[int],
                          budgets: Sequence[int], M: int, Df: int, seed: int,
                          qkv_seed: Optional[int] = None, corr_K: int = 0,
                          name: str = "custom", anchors: Optional[Sequence[int]] = None,
-                         dino: bool = True) -> Workload:
-    """Draw one layer's Q/K/V (+ DINO-like features) for any geometry."""
+                         dino: bool = True, heads: Optional[Sequence[int]] = None) -> Workload:
+    """Draw one layer's Q/K/V (+ DINO-like features) for any geometry.
+
+    Every head draws from its own sub-stream, so `heads` (default: all) can
+    restrict the draw to a subset; the other heads' Q/K/V are left zero."""
     if len(roles) != geom.H or len(budgets) != geom.H:
         raise ValueError("roles/budgets must have one entry per head")
     S, P, N, H, d, T, ns = geom.S, geom.P, geom.N, geom.H, geom.d, geom.T, geom.ns
@@ -192,7 +197,7 @@ def make_geometry_inputs(geom: Geometry, dtype: str, roles: Sequence[int],
     else:
         s_w, s_qkv, s_sal, s_probe = np.random.SeedSequence(qkv_seed).spawn(7)[3:]
 
-    z = np.random.default_rng(s_lat).standard_normal((M, Df))
+    z = np.random.default_rng(s_lat).standard_normal((M, Df), dtype=np.float32)
     lat = _frame_latents(np.random.default_rng(s_frames), S, P, M)
     patch_tok = geom.patch_token(np.arange(S * P))
 
@@ -202,31 +207,32 @@ def make_geometry_inputs(geom: Geometry, dtype: str, roles: Sequence[int],
         dino_arr = np.empty((S * P, Df), dtype=np.uint16 if dtype == "bf16" else np.float32)
         for f in range(S):
             sl = slice(f * P, (f + 1) * P)
-            dino_arr[sl] = _encode(z[lat[sl]] + 0.3 * rng_d.standard_normal((P, Df)), dtype)
+            dino_arr[sl] = _encode(z[lat[sl]] + np.float32(0.3) * rng_d.standard_normal((P, Df), dtype=np.float32),
+                                   dtype)
 
-    rng_w = np.random.default_rng(s_w)
-    rng_qkv = np.random.default_rng(s_qkv)
-    rng_sal = np.random.default_rng(s_sal)
-    rng_probe = np.random.default_rng(s_probe)
+    per_head = list(zip(s_w.spawn(H), s_qkv.spawn(H), s_sal.spawn(H), s_probe.spawn(H)))
     store = np.uint16 if dtype == "bf16" else np.float32
-    qo = np.empty((H, N, d), dtype=store)
-    ko = np.empty((H, N, d), dtype=store)
-    vo = np.empty((H, N, d), dtype=store)
+    qo = np.zeros((H, N, d), dtype=store)
+    ko = np.zeros((H, N, d), dtype=store)
+    vo = np.zeros((H, N, d), dtype=store)
     salient: Dict[int, np.ndarray] = {}
-    for h in range(H):
-        q = rng_qkv.standard_normal((N, d))
-        k = rng_qkv.standard_normal((N, d))
-        v = rng_qkv.standard_normal((N, d))
+    for h in (range(H) if heads is None else heads):
+        sw, sq, ss, sp = per_head[h]
+        rng_qkv = np.random.default_rng(sq)
+        q = rng_qkv.standard_normal((N, d), dtype=np.float32)
+        k = rng_qkv.standard_normal((N, d), dtype=np.float32)
+        v = rng_qkv.standard_normal((N, d), dtype=np.float32)
         if roles[h] == ROLE_CORRESPONDENCE:
-            W = rng_w.standard_normal((Df, d)) / math.sqrt(Df)
+            W = (np.random.default_rng(sw).standard_normal((Df, d)) / math.sqrt(Df)).astype(np.float32)
             zw = z @ W
-            q[patch_tok] = zw[lat] + 0.1 * q[patch_tok]
-            k[patch_tok] = zw[lat] + 0.1 * k[patch_tok]
+            q[patch_tok] = zw[lat] + np.float32(0.1) * q[patch_tok]
+            k[patch_tok] = zw[lat] + np.float32(0.1) * k[patch_tok]
         elif roles[h] == ROLE_VERTICAL:
-            u = rng_probe.standard_normal(d)
-            u /= np.linalg.norm(u)
-            sal = np.sort(patch_tok[rng_sal.choice(S * P, size=min(N_SALIENT, S * P), replace=False)])
-            k[sal] += 4.0 * u
+            u = np.random.default_rng(sp).standard_normal(d)
+            u = (u / np.linalg.norm(u)).astype(np.float32)
+            rs = np.random.default_rng(ss)
+            sal = np.sort(patch_tok[rs.choice(S * P, size=min(N_SALIENT, S * P), replace=False)])
+            k[sal] += np.float32(4.0) * u
             q += u
             salient[h] = sal
         qo[h] = _encode(q, dtype)
@@ -239,7 +245,8 @@ def make_geometry_inputs(geom: Geometry, dtype: str, roles: Sequence[int],
                     dino=dino_arr, Df=Df, corr_K=corr_K, lat=lat, salient=salient, seed=seed)
 
 
-def make_layer(cid: int, layer: int = 0, dino: bool = True) -> Workload:
+def make_layer(cid: int, layer: int = 0, dino: bool = True,
+               heads: Optional[Sequence[int]] = None) -> Workload:
     """Inputs of one measured configuration (one layer of config 4's stack)."""
     c = CONFIGS[cid]
     geom = Geometry(S=c["S"], ns=c["ns"], P=c["P"])
@@ -254,11 +261,12 @@ def make_layer(cid: int, layer: int = 0, dino: bool = True) -> Workload:
         name = f"{name}_L{layer}"
     budgets = [_budget(r, c["vert_K"], c["corr_K"], c["scan_s"]) for r in roles]
     return make_geometry_inputs(geom, c["dtype"], roles, budgets, c["M"], c["Df"], seed=cid,
-                                qkv_seed=qkv_seed, corr_K=c["corr_K"], name=name, dino=dino)
+                                qkv_seed=qkv_seed, corr_K=c["corr_K"], name=name, dino=dino, heads=heads)
 
 
-def make_inputs(cid: int, layer: int = 0, dino: bool = True) -> Workload:
-    return make_layer(cid, layer, dino)
+def make_inputs(cid: int, layer: int = 0, dino: bool = True,
+                heads: Optional[Sequence[int]] = None) -> Workload:
+    return make_layer(cid, layer, dino, heads)
 
 
 def sample_rows(geom: Geometry, n_target: int, seed: int = 12345) -> np.ndarray:
