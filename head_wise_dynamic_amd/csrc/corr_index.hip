@@ -480,9 +480,10 @@ template <int MAXE> struct RowSel {
 // a longer row is then filtered by streaming over all its entries.
 template <int MAXE>
 __global__ __launch_bounds__(256) void compact_rows(const Args A) {
-    const int64_t u = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    // only rows [row_lo, row_hi) received candidates in the last phase
+    const int64_t u = A.row_lo + (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (u >= A.g.Np) return;
+    if (u >= A.row_hi) return;
     const uint32_t c = A.s.cnt[u];
     const uint32_t nn = min(c, (uint32_t)A.cap);
     if (c > (uint32_t)A.cap && lane == 0) A.s.over[u] = 1u;
@@ -664,7 +665,10 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     if (gemm) {
         const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
         const uint32_t small = 16 * 64;
-        auto compact = [&]() { hipLaunchKernelGGL(compact_rows<16>, dim3(cb), dim3(256), 0, stream, A); };
+        auto compact = [&]() {
+            const unsigned nb = (unsigned)((A.row_hi - A.row_lo + kRowWaves - 1) / kRowWaves);
+            hipLaunchKernelGGL(compact_rows<16>, dim3(nb), dim3(256), 0, stream, A);
+        };
         auto rect = [&](int mode, int64_t r_lo, int64_t r_hi, int64_t c_lo, int64_t c_hi) {
             A.row_lo = r_lo;
             A.row_hi = r_hi;
@@ -693,6 +697,8 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             // 4. the square [W, Np)^2 once per unordered pair
             const int64_t nt = (Np - W + CT - 1) / CT;
             const int64_t tiles = nt * (nt + 1) / 2;
+            A.row_lo = W;
+            A.row_hi = Np;
             if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
             hipLaunchKernelGGL(cos_phase<SYM>, dim3((unsigned)(8 * ((tiles + 7) / 8))), dim3(kCosThreads), 0,
                                stream, A);
