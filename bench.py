@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=10, help="reps of each breakdown measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--per-frame-k", type=int, default=4,
+                    help="also time the per-frame index build with this K per frame (0: skip)")
     ap.add_argument("--cpu-row-stride", type=int, default=37)
     ap.add_argument("--cpu-corr-rows", type=int, default=64)
     return ap.parse_args()
@@ -182,6 +184,26 @@ def main():
         dense_ms = statistics.median(dn)
         del od
 
+    # per-frame index (K best of every other frame), built in a context of its
+    # own so the step's cached index is untouched; not part of the step
+    per_frame = None
+    if args.per_frame_k > 0:
+        pctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+        pctx.build_corr_index(dino, args.per_frame_k, mode=saf.SAF_CORR_PER_FRAME)
+        torch.cuda.synchronize()
+        pf = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pctx.build_corr_index(dino, args.per_frame_k, mode=saf.SAF_CORR_PER_FRAME)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pf.append(e0.elapsed_time(e1))
+        pf_ms = statistics.median(pf)
+        per_frame = {"K_per_frame": args.per_frame_k, "row_length": pctx.corr_k(), "build_ms": round(pf_ms, 3),
+                     "tflops": round(2.0 * g.Np * g.Np * w.Df / (pf_ms * 1e-3) / 1e12, 2)}
+        pctx.close()
+
     # ---- roofline of the dominant kernel (largest single-kernel share)
     pairs = key_counts(w)
     shared_pairs = sum(p for kind, p in pairs if kind == "shared")
@@ -250,6 +272,7 @@ def main():
         "dense_tflops": round(4.0 * d * g.H * g.N * g.N / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "speedup_attn_vs_dense": round(dense_ms / attn_ms, 2) if dense_ms else None,
         "speedup_step_vs_dense": round(dense_ms / ms_per_step, 2) if dense_ms else None,
+        "per_frame_index": per_frame,
         "sparsity": round(1.0 - (shared_pairs + gather_pairs) / (g.H * g.N * g.N), 4),
         "roofline": roofline,
         "roofline_other": others,

@@ -22,6 +22,7 @@ struct saf_ctx {
     std::string err;
     int32_t *corr_idx = nullptr;  // [Np, corr_k]
     int32_t corr_k = 0;
+    int32_t corr_build_k = 0;  // K the index was built with (per frame in per-frame mode)
     size_t corr_bytes = 0;
     void *corr_scratch = nullptr;
     size_t corr_scratch_bytes = 0;
@@ -295,20 +296,31 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     if (K < 1) return fail(c, SAF_EINVAL, "K %d < 1", K);
     if (Df < 1) return fail(c, SAF_EINVAL, "Df %d < 1", Df);
     if (row_stride < Df) return fail(c, SAF_EINVAL, "dino row stride %lld < Df", (long long)row_stride);
-    if (mode == SAF_CORR_PER_FRAME) return fail(c, SAF_EUNSUPPORTED, "per-frame mode is not implemented");
-    if (mode != SAF_CORR_TOTAL) return fail(c, SAF_EINVAL, "bad mode %d", mode);
+    if (mode != SAF_CORR_TOTAL && mode != SAF_CORR_PER_FRAME) return fail(c, SAF_EINVAL, "bad mode %d", mode);
+    const bool per_frame = mode == SAF_CORR_PER_FRAME;
     if (Df > 4096) return fail(c, SAF_EUNSUPPORTED, "Df %d > 4096", Df);
     const int64_t q = dino_dtype == SAF_BF16 ? 8 : 4;
     if (row_stride % q || !aligned16(dino))
         return fail(c, SAF_EINVAL, "dino rows must be 16-byte aligned");
-    const int64_t ncand = (int64_t)(g.S - 1) * g.P;
-    const int32_t Kc = (int32_t)std::min<int64_t>(K, ncand);
-    if (Kc > 1024) return fail(c, SAF_EUNSUPPORTED, "K %d > 1024", Kc);
+    // K kept per row (total) or per other frame (per-frame); Kc = index row length
+    int32_t Kk, Kc;
+    if (per_frame) {
+        if (g.P > saf::kFrameMaxP) return fail(c, SAF_EUNSUPPORTED, "per-frame mode: P %d > %d", g.P, saf::kFrameMaxP);
+        Kk = std::min(K, g.P);
+        const int64_t row = (int64_t)(g.S - 1) * Kk;
+        if (row > INT32_MAX / 2) return fail(c, SAF_EUNSUPPORTED, "index row of %lld entries", (long long)row);
+        Kc = (int32_t)row;
+    } else {
+        const int64_t ncand = (int64_t)(g.S - 1) * g.P;
+        Kk = Kc = (int32_t)std::min<int64_t>(K, ncand);
+        if (Kc > 1024) return fail(c, SAF_EUNSUPPORTED, "K %d > 1024", Kc);
+    }
 
     saf_status_t st = ensure_corr_storage(c, Kc);
     if (st != SAF_OK) return st;
-    const int32_t cap = saf::corr_capacity(g, Kc);
-    const size_t sb = saf::corr_scratch_bytes(g, Kc, cap);
+    const int32_t cap = per_frame ? 0 : saf::corr_capacity(g, Kc);
+    const int32_t chunk_rows = per_frame ? saf::corr_frame_chunk_rows(g) : 0;
+    const size_t sb = per_frame ? saf::corr_frame_scratch_bytes(g, chunk_rows) : saf::corr_scratch_bytes(g, Kc, cap);
     if (c->corr_scratch_bytes < sb) {
         if (c->corr_scratch) {
             hipError_t e = hipFree(c->corr_scratch);
@@ -330,8 +342,10 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     B.dino_dtype = dino_dtype;
     B.Df = Df;
     B.row_stride = row_stride;
-    B.K = Kc;
+    B.K = Kk;
     B.cap = cap;
+    B.per_frame = per_frame ? 1 : 0;
+    B.chunk_rows = chunk_rows;
     B.idx_out = c->corr_idx;
     B.scratch = c->corr_scratch;
     B.mark = mark_launch;
@@ -343,6 +357,7 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     }
     if (e != hipSuccess) return hip_fail(c, e, "correspondence index kernels");
     c->corr_k = Kc;
+    c->corr_build_k = Kk;
     return SAF_OK;
 }
 
@@ -357,6 +372,7 @@ saf_status_t saf_set_corr_index(saf_ctx_t *c, const int32_t *dev_idx, int32_t Kc
     hipError_t e = hipMemcpyAsync(c->corr_idx, dev_idx, c->corr_bytes, hipMemcpyDeviceToDevice, as_stream(stream));
     if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync(index)");
     c->corr_k = Kc;
+    c->corr_build_k = Kc;
     return SAF_OK;
 }
 
@@ -410,9 +426,10 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
     if (pi.ncorr) {
         if (!c->corr_idx) return fail(c, SAF_ESTATE, "a correspondence head needs a built index");
         for (int h = 0; h < g.H; ++h)
-            if (plan[h].role == SAF_CORRESPONDENCE && plan[h].budget != 0 && plan[h].budget != c->corr_k)
-                return fail(c, SAF_ESTATE, "head %d budget %d differs from the index's K %d", h,
-                            plan[h].budget, c->corr_k);
+            if (plan[h].role == SAF_CORRESPONDENCE && plan[h].budget != 0 && plan[h].budget != c->corr_k &&
+                plan[h].budget != c->corr_build_k)
+                return fail(c, SAF_ESTATE, "head %d budget %d differs from the index's K %d (row length %d)", h,
+                            plan[h].budget, c->corr_build_k, c->corr_k);
     }
     size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws);
     if (need > 0) need += 256;  // room to align the start to 256 bytes

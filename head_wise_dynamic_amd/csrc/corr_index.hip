@@ -72,6 +72,7 @@ struct Args {
     int64_t row_lo, row_hi;  // current phase: rows
     int64_t seed_cols;       // columns of the seed phase (whole frames)
     int64_t sym_lo;          // start of the symmetric square [sym_lo, Np)^2
+    float *chunk;            // STORE mode: cosines of rows [row_lo, row_hi) x all columns
 };
 
 template <typename T> __device__ inline float ldf(const T *p, int64_t i);
@@ -120,7 +121,9 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
 //          it reaches the row's threshold;
 //   SYM    the upper triangle of tiles of [sym_lo,Np) x [sym_lo,Np): cosine is
 //          symmetric, so each off-diagonal tile feeds its rows (forward) and,
-//          transposed, its columns' rows.
+//          transposed, its columns' rows;
+//   STORE  rows [row_lo,row_hi) x every column: the cosines are written to a
+//          row-chunk buffer (per-frame selection reads them back).
 constexpr int CT = 256;
 constexpr int CK = 64;
 constexpr int CROW = CK + 8;   // padded LDS row: 144 B, conflict-free 16-byte reads
@@ -128,7 +131,7 @@ constexpr int kGroupRows = 4;  // row tiles per group in the tile order
 
 constexpr int kTileElems = CT * CROW;     // one operand tile in LDS (bf16)
 constexpr int kCosThreads = 512;           // 8 waves: 4 (rows) x 2 (columns) of 64 x 128
-enum CosMode { SEED = 0, FILTER = 1, SYM = 2 };
+enum CosMode { SEED = 0, FILTER = 1, SYM = 2, STORE = 3 };
 
 // threshold of a row in units of acc * (inverse norm of the other side),
 // lowered by 2^-20 relative so that the filter never drops a value the exact
@@ -290,6 +293,22 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         const bool vok = v < col_hi;
         iv[bj] = vok ? A.s.invn[v] : __builtin_nanf("");  // NaN never passes a comparison
         fv[bj] = vok ? (int32_t)(v / g.P) : -2;
+    }
+
+    if (MODE == STORE) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+                if (r_frame[lr] < 0) continue;
+                const float iu = r_iu[lr];
+                float *crow = A.chunk + (row0 + lr - A.row_lo) * g.Np;
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj)
+                    if (fv[bj] >= 0) crow[vcol0 + 32 * bj] = acc[bi][bj][r] * (iu * iv[bj]);
+            }
+        return;
     }
 
     if (MODE == SEED) {
@@ -583,6 +602,114 @@ __global__ __launch_bounds__(256) void finalize_rows(const Args A, uint32_t lo_c
     }
 }
 
+// ---- per-frame mode: cosines of a row chunk on the VALU (fp32 features, or
+// a channel count the matrix-core tiles do not cover)
+template <typename T> __global__ __launch_bounds__(256) void cos_store_valu(const Args A) {
+    const Geom &g = A.g;
+    const int64_t rows = A.row_hi - A.row_lo;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * g.Np) return;
+    const int64_t u = A.row_lo + idx / g.Np, v = idx % g.Np;
+    const T *F = (const T *)A.F;
+    float acc = 0.f;
+    for (int c = 0; c < A.Df; ++c) acc = fmaf(ldf<T>(F, u * A.stride + c), ldf<T>(F, v * A.stride + c), acc);
+    A.chunk[idx] = acc * (A.s.invn[u] * A.s.invn[v]);
+}
+
+// ---- per-frame mode: one wave per (row, other frame) selects the frame's K
+// best patches by (cosine desc, index asc) and writes their tokens ascending.
+// Patch i of the frame sits in register slot i / 64 of lane i % 64, so an
+// ordered ballot compaction over (slot, lane) emits the kept set in index
+// order.  Small K: K rounds of a wave-wide argmax; otherwise a bitwise search
+// for the K-th key and the index cut among its ties.
+constexpr int kFrameRoundsMaxK = 8;
+
+template <int MAXE>
+__global__ __launch_bounds__(256) void frame_topk(const Args A) {
+    const Geom &g = A.g;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    const int64_t rows = A.row_hi - A.row_lo;
+    if (item >= rows * g.S) return;
+    const int64_t u = A.row_lo + item / g.S;
+    const int32_t gf = (int32_t)(item % g.S), fu = (int32_t)(u / g.P);
+    if (gf == fu) return;
+    const float *src = A.chunk + (u - A.row_lo) * g.Np + (int64_t)gf * g.P;
+    const int ne = (g.P + 63) / 64;
+    uint32_t key[MAXE];  // order_key of the cosine; 0 marks an empty slot
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        const int i = e * 64 + lane;
+        key[e] = (e < ne && i < g.P) ? max(order_key(src[i]), 1u) : 0u;
+    }
+    const uint32_t K = (uint32_t)A.K;
+    uint64_t keep = 0;  // bit e: slot e is selected
+    if (K <= kFrameRoundsMaxK) {
+        for (uint32_t k = 0; k < K; ++k) {
+            // best of this lane among unselected slots: largest key, then lowest slot
+            uint32_t bk = 0;
+            int be = -1;
+#pragma unroll
+            for (int e = 0; e < MAXE; ++e)
+                if (e < ne && !((keep >> e) & 1ull) && key[e] > bk) {
+                    bk = key[e];
+                    be = e;
+                }
+            // wave argmax of (key desc, patch index asc)
+            uint64_t w = ((uint64_t)bk << 32) | (uint32_t)(0x7FFFFFFF - (be < 0 ? 0x7FFFFFFF : be * 64 + lane));
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint64_t x = __shfl_xor(w, o);
+                w = x > w ? x : w;
+            }
+            const uint32_t wi = 0x7FFFFFFFu - (uint32_t)(w & 0xFFFFFFFFu);
+            if ((w >> 32) != 0 && (int)(wi & 63) == lane) keep |= 1ull << (wi >> 6);
+        }
+    } else {
+        auto count = [&](auto pred) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < MAXE; ++e)
+                if (e < ne) c += (uint32_t)__popcll(__ballot(key[e] != 0u && pred(e)));
+            return c;
+        };
+        uint32_t thr = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            if (count([&](int e) { return key[e] >= cand; }) >= K) thr = cand;
+        }
+        const uint32_t need = K - count([&](int e) { return key[e] > thr; });
+        int32_t ithr = INT32_MAX;
+        if (count([&](int e) { return key[e] == thr; }) != need) {
+            uint32_t lo = 0;  // largest index cut with fewer than need tied entries below it
+            for (int bit = 30; bit >= 0; --bit) {
+                const uint32_t cand = lo | (1u << bit);
+                if (count([&](int e) { return key[e] == thr && (uint32_t)(e * 64 + lane) < cand; }) < need)
+                    lo = cand;
+            }
+            ithr = (int32_t)lo;
+        }
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e)
+            if (e < ne && key[e] != 0u && (key[e] > thr || (key[e] == thr && e * 64 + lane <= ithr)))
+                keep |= 1ull << e;
+    }
+    const int32_t slot = gf - (gf > fu ? 1 : 0);
+    int32_t *out = A.idx_out + u * ((int64_t)(g.S - 1) * A.K) + (int64_t)slot * A.K;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int32_t tok0 = gf * g.T + g.ns;
+    uint32_t pos = 0;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        if (e < ne) {
+            const bool kp = (keep >> e) & 1ull;
+            const uint64_t m = __ballot(kp);
+            if (kp) out[pos + (uint32_t)__popcll(m & below)] = tok0 + e * 64 + lane;
+            pos += (uint32_t)__popcll(m);
+        }
+    }
+}
+
 // ---- exact per-row engine: one 1024-thread block per flagged row
 template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(const Args A) {
     __shared__ float fu[4096];
@@ -642,6 +769,53 @@ size_t corr_scratch_bytes(const Geom &g, int32_t K, int32_t cap) {
            align256(sizeof(float2) * (size_t)Np * cap) + align256(sizeof(float) * (size_t)kFallbackBlocks * Np);
 }
 
+// rows per chunk of the per-frame mode: a multiple of the tile height whose
+// fp32 cosine block stays near kFrameChunkBytes
+constexpr size_t kFrameChunkBytes = (size_t)512 << 20;
+int32_t corr_frame_chunk_rows(const Geom &g) {
+    const int64_t want = (int64_t)(kFrameChunkBytes / (sizeof(float) * (size_t)g.Np)) / CT * CT;
+    const int64_t all = (g.Np + CT - 1) / CT * CT;
+    return (int32_t)std::max<int64_t>(CT, std::min<int64_t>(want, all));
+}
+
+size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows) {
+    return align256(sizeof(float) * g.Np) * 2 + align256(sizeof(uint32_t) * g.Np) * 2 +
+           align256(sizeof(float) * (size_t)chunk_rows * g.Np);
+}
+
+static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, hipStream_t stream) {
+    const Geom &g = B.g;
+    const int64_t Np = g.Np;
+    A.chunk = A.s.rowbuf;  // cand is empty (cap 0): the chunk follows the per-row arrays
+    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0;
+    for (int64_t r0 = 0; r0 < Np; r0 += B.chunk_rows) {
+        A.row_lo = r0;
+        A.row_hi = std::min<int64_t>(Np, r0 + B.chunk_rows);
+        A.col_lo = 0;
+        A.col_hi = Np;
+        const int64_t rows = A.row_hi - A.row_lo;
+        if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+        if (gemm) {
+            const int64_t tiles = ((rows + CT - 1) / CT) * ((Np + CT - 1) / CT);
+            hipLaunchKernelGGL(cos_phase<STORE>, dim3((unsigned)(8 * ((tiles + 7) / 8))), dim3(kCosThreads), 0,
+                               stream, A);
+        } else {
+            const unsigned nb = (unsigned)((rows * Np + 255) / 256);
+            if (B.dino_dtype == BF16)
+                hipLaunchKernelGGL(cos_store_valu<uint16_t>, dim3(nb), dim3(256), 0, stream, A);
+            else
+                hipLaunchKernelGGL(cos_store_valu<float>, dim3(nb), dim3(256), 0, stream, A);
+        }
+        if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+        const unsigned fb = (unsigned)((rows * g.S + kRowWaves - 1) / kRowWaves);
+        if (g.P <= 24 * 64)
+            hipLaunchKernelGGL(frame_topk<24>, dim3(fb), dim3(256), 0, stream, A);
+        else
+            hipLaunchKernelGGL(frame_topk<64>, dim3(fb), dim3(256), 0, stream, A);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     Args A{};
     A.g = B.g;
@@ -653,8 +827,18 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.idx_out = B.idx_out;
     const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024;
     A.all_rows_fallback = gemm ? 0 : 1;
-    A.s = carve(B.scratch, B.g.Np, B.cap);
+    A.s = carve(B.scratch, B.g.Np, B.per_frame ? 0 : B.cap);
     const int64_t Np = B.g.Np;
+    if (B.per_frame) {
+        if (B.g.P > kFrameMaxP) return hipErrorInvalidValue;
+        A.all_rows_fallback = 1;  // init_rows: norms only
+        const unsigned rb = (unsigned)((Np + 3) / 4);
+        if (B.dino_dtype == BF16)
+            hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
+        else
+            hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
+        return launch_corr_frames(A, B, stream);
+    }
     A.seed_cols = std::min<int64_t>(Np, 2 * (int64_t)B.g.P);
     A.sym_lo = corr_sym_start(B.g);
     const unsigned rb = (unsigned)((Np + 3) / 4);

@@ -99,10 +99,12 @@ struct CorrBuild {
     int32_t dino_dtype;
     int32_t Df;
     int64_t row_stride;
-    int32_t K;      // kept per row (already clamped)
-    int32_t cap;    // candidate capacity per row
-    int32_t *idx_out;   // [Np, K]
-    void *scratch;      // corr_scratch_bytes()
+    int32_t K;      // kept per row (total mode) or per other frame (per-frame mode), clamped
+    int32_t cap;    // candidate capacity per row (total mode)
+    int32_t per_frame;  // 1: the K best of every other frame, [Np, (S-1) K]
+    int32_t chunk_rows; // per-frame mode: rows whose cosines are materialised at once
+    int32_t *idx_out;   // [Np, K] or [Np, (S-1) K]
+    void *scratch;      // corr_scratch_bytes() / corr_frame_scratch_bytes()
     // optional tracing hook: called with begin = 1 / 0 around every cosine
     // GEMM launch (the caller records events on the stream)
     void (*mark)(void *user, int begin, const char *name, hipStream_t stream);
@@ -110,6 +112,9 @@ struct CorrBuild {
 };
 size_t corr_scratch_bytes(const Geom &g, int32_t K, int32_t cap);
 int32_t corr_capacity(const Geom &g, int32_t K);
+constexpr int32_t kFrameMaxP = 4096;  // per-frame mode: patches per frame the selection holds
+int32_t corr_frame_chunk_rows(const Geom &g);
+size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows);
 hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream);
 
 }  // namespace saf

@@ -100,7 +100,8 @@ typedef struct {
 typedef struct {
     int32_t role;          /* saf_role_t */
     int32_t budget;        /* VERTICAL: K >= 1 (clamped to N); SCANNING: stride >= 1;
-                              CORRESPONDENCE: 0 or the cached index's K; others: 0 */
+                              CORRESPONDENCE: 0, the cached index's row length Kc
+                              or the K it was built with; others: 0 */
     int32_t anchor_frame;  /* POSITION: anchor frame in [0, S); others ignored */
     int32_t flags;         /* must be 0 */
 } saf_head_plan_t;
@@ -126,14 +127,21 @@ saf_status_t saf_workspace_size(const saf_ctx_t *ctx, const saf_head_plan_t *pla
 
 /* Build the correspondence index (Sec. 4.3, "DINO Top-K Kernel") from DINO
  * features of the S*P patches (row u = patch number u, Df channels contiguous,
- * rows dino_row_stride elements apart, dtype dino_dtype).  For every patch u:
- * cosine c_uv = f_u.f_v / (|f_u||f_v|) (0 when a norm is 0) against the
- * patches v of the other frames; the first K by (c desc, token asc) (TOTAL;
- * clamped to (S-1)P) are stored as global token indices, ascending.  The
- * index is kept in the context and reused by every later
- * saf_sparse_attention call (the cache of Sec. 4.3) until rebuilt.
- * Errors: SAF_EINVAL (S < 2, K < 1, Df < 1, bad stride/pointer),
- * SAF_EUNSUPPORTED (PER_FRAME mode, Df not a multiple of 32), SAF_ENOMEM. */
+ * rows dino_row_stride elements apart, dtype dino_dtype, 16-byte aligned rows).
+ * For every patch u: cosine c_uv = f_u.f_v / (|f_u||f_v|) (0 when a norm is 0)
+ * against the patches v of the other frames, ranked by (c desc, token asc).
+ *   SAF_CORR_TOTAL:     the first min(K, (S-1)P) over all other frames;
+ *                       Kc = that count (at most 1024).
+ *   SAF_CORR_PER_FRAME: the first min(K, P) of every other frame (P <= 4096);
+ *                       Kc = (S-1) min(K, P).
+ * Each row of Kc global token indices is stored ascending.  The index is kept
+ * in the context and reused by every later saf_sparse_attention call (the
+ * cache of Sec. 4.3) until rebuilt.  The device scratch the build needs is
+ * owned by the context (allocated on first use, grown when a larger build
+ * needs more).
+ * Errors: SAF_EINVAL (S < 2, K < 1, Df < 1, bad mode/stride/pointer),
+ * SAF_EUNSUPPORTED (Df > 4096, TOTAL with Kc > 1024, PER_FRAME with
+ * P > 4096), SAF_ENOMEM. */
 saf_status_t saf_build_corr_index(saf_ctx_t *ctx, const void *dino, int32_t dino_dtype,
                                   int32_t Df, int64_t dino_row_stride, int32_t K,
                                   int32_t mode, void *stream);

@@ -122,13 +122,18 @@ def test_build_corr_index_validation():
         assert b(c, FAKE, 1, 0, 64, 8, 0, None) == saf.SAF_EINVAL        # Df < 1
         assert b(c, FAKE, 1, 64, 32, 8, 0, None) == saf.SAF_EINVAL       # stride < Df
         assert b(c, FAKE, 5, 64, 64, 8, 0, None) == saf.SAF_EINVAL       # dtype
-        assert b(c, FAKE, 1, 64, 64, 8, 1, None) == saf.SAF_EUNSUPPORTED  # per-frame mode
         assert b(c, FAKE, 1, 64, 64, 8, 7, None) == saf.SAF_EINVAL
         assert b(c, FAKE, 1, 64, 68, 8, 0, None) == saf.SAF_EINVAL       # rows not 16-byte aligned
         kc = C.c_int32()
         assert saf.saf_get_corr_index(c, None, kc, None) == saf.SAF_ESTATE
         assert saf.saf_set_corr_index(c, FAKE, 0, None) == saf.SAF_EINVAL
         assert saf.saf_set_corr_index(c, FAKE, 3 * 256 + 1, None) == saf.SAF_EINVAL
+    finally:
+        saf.saf_destroy(c)
+    c = _ctx(S=2, P=4097)
+    try:   # the per-frame selection holds at most 4096 patches per frame
+        assert saf.saf_build_corr_index(c, FAKE, 1, 64, 64, 8, 1, None) == saf.SAF_EUNSUPPORTED
+        assert saf.saf_build_corr_index(c, FAKE, 1, 64, 64, 2000, 0, None) == saf.SAF_EUNSUPPORTED
     finally:
         saf.saf_destroy(c)
 
