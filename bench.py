@@ -31,6 +31,36 @@ METRIC = "ms per 16-head sparse global-attn layer at S=100 frames; HBM GB/s & MF
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
+# HBM counters of the cosine GEMM launches of one step (rocprofv3 --pmc
+# FETCH_SIZE, then WRITE_SIZE, in separate runs; KiB per dispatch averaged per
+# kernel and summed over the step's 1 seed + 6 filtered + 1 symmetric launches).
+# Each counter is scaled by what it reads for a plain 1 GiB device copy in the
+# same run (FETCH_SIZE 524308.6 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
+# for the kernel source with this digest only; after any change the traffic is
+# reported as null until the counters are taken again.
+COSINE_GEMM_COUNTERS = {
+    "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
+    "sha256": "8b6beb5ea6d6f5ae5219fde4b87ed6e978efcdaaf278f412170e2169c0ab49c8",
+    "fetch_kib_per_step": 790074.68 + 6 * 680916.76 + 32145306.03,
+    "write_kib_per_step": 2901359.58 + 6 * 119775.85 + 3954062.88,
+    "fetch_scale": 1048576.0 / 524308.6,
+    "write_scale": 1048576.0 / 1048576.0,
+}
+
+
+def counters_traffic_gb(rec):
+    """HBM bytes (GB) per step from the recorded counters, or None when the
+    kernel source no longer matches the one they were taken on."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+                return None
+    except OSError:
+        return None
+    kib = rec["fetch_kib_per_step"] * rec["fetch_scale"] + rec["write_kib_per_step"] * rec["write_scale"]
+    return kib * 1024 / 1e9
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -41,6 +71,8 @@ def parse():
     ap.add_argument("--reps", type=int, default=10, help="reps of each breakdown measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy 1 GiB device to device twice (a known-size kernel for HBM counters)")
     ap.add_argument("--per-frame-k", type=int, default=4,
                     help="also time the per-frame index build with this K per frame (0: skip)")
     ap.add_argument("--cpu-row-stride", type=int, default=37)
@@ -99,6 +131,14 @@ def main():
     o = torch.empty_like(q)
     ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
     stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         ctx.build_corr_index(dino, w.corr_K)
@@ -231,8 +271,11 @@ def main():
                                    launches=launch_counts.get("cosine_gemm", 0))
     dom = max(cand, key=lambda n: cand[n]["ms"])
     r = cand[dom]
+    traffic = counters_traffic_gb(COSINE_GEMM_COUNTERS) if dom == "cosine_gemm" else None
     roofline = {"kernel": dom, "bound": r["bound"], "achieved": round(r["achieved"], 2), "peak": r["peak"],
-                "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4), "traffic": None,
+                "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4),
+                "traffic": round(traffic, 2) if traffic is not None else None,
+                "traffic_unit": "GB of HBM traffic per step (all launches of the kernel)",
                 "kernel_ms_per_step": round(r["ms"], 4), "launches_per_step": r.get("launches", 1)}
     others = {n: {"achieved": round(c["achieved"], 2), "unit": c["unit"], "peak": c["peak"],
                   "frac": round(c["achieved"] / c["peak"], 4), "kernel_ms": round(c["ms"], 4)}
