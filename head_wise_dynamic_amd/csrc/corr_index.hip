@@ -3,26 +3,31 @@
 // c_uv = f_u . f_v / (|f_u| |f_v|), ties to the lower token, stored as global
 // token indices in ascending order.  Built once per sequence and cached.
 //
-// bf16 features (the fast engine):
-//   * inverse norms 1/|f_u| in fp32;
-//   * the cosine matrix is never stored.  Columns are visited in doubling
-//     phases of patches [0,P), [P,2P), [2P,4P), ...; each phase is one MFMA
-//     GEMM (128 x 128 tiles, v_mfma_f32_32x32x16_bf16, fp32 accumulate,
-//     normalised after the dot) whose epilogue keeps only c >= theta_u, the
-//     row's current lower bound of its K-th best score, appending survivors
-//     to a per-row candidate buffer (wave ballot + one atomic per half-wave);
-//   * after each phase a compaction wave per row keeps the exact top-K of its
-//     buffer and raises theta_u to the K-th score.  Because theta_u is the
-//     K-th best of actual candidates it never exceeds the true K-th score, so
-//     no member of the final top-K is ever filtered out;
-//   * a final wave per row selects the top-K, sorts it by token and writes it.
-//   Expected survivors per phase are ~K (the K-th best of X candidates
-//   admits ~K of the next X), so buffers of max(P + 2K, 8K) entries suffice;
-//   a row whose buffer overflows anyway is flagged and recomputed exactly by
-//   the per-row engine below.
+// Total mode, bf16 features (the fast engine).  The cosine matrix is never
+// stored: each phase is one MFMA GEMM over a block of the pair space (256 x
+// 256 tiles, v_mfma_f32_32x32x16_bf16, fp32 accumulate, normalised after the
+// dot by fp32 inverse norms) whose epilogue keeps only c >= theta_u, the
+// row's current lower bound of its K-th best score, and appends survivors
+// to a per-row candidate buffer (staged in LDS, one global atomic per row
+// per tile).  After each phase a compaction wave per row raises theta_u to a
+// lower bound of the K-th best of its buffer and drops what lies below.
+//   1. seed: columns of frames 0 and 1, every candidate kept;
+//   2. doubling phases [2P, 4P), [4P, 8P), ... up to W, for every row;
+//   3. rows below W continue doubling over [W, Np);
+//   4. the square [W, Np)^2 once per unordered pair (cosine is symmetric: a
+//      tile feeds its rows and, transposed, its columns).  Its filter is a
+//      guess theta_g_u of the K-th best overall (a rank of the columns seen in
+//      [0, W) scaled by their share of the candidates); at the end a row's
+//      exact K-th best must reach theta_g_u, else the row is recomputed;
+//   5. a final wave per row selects the exact top-K, sorts it by token and
+//      writes it.
+//   A row whose buffer overflows is flagged and recomputed exactly by the
+//   per-row engine at the end.
 // fp32 features (and flagged rows): one 1024-thread block per row computes
 //   every cosine with VALU FMAs into a scratch row and runs an exact block
 //   top-K (radix select + ordered compaction).
+// Per-frame mode (K best of every other frame): the GEMM writes fp32 row
+//   chunks of the cosine matrix, then one wave per (row, frame) selects.
 #include "device_util.h"
 #include "topk_block.h"
 
@@ -37,6 +42,7 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 struct Scratch {
     float *invn;      // [Np]
     float *theta;     // [Np]
+    float *theta_g;   // [Np] filter threshold of the symmetric pass (a guess, checked at the end)
     uint32_t *cnt;    // [Np]
     uint32_t *over;   // [Np] row needs the exact per-row engine
     float2 *cand;     // [Np * cap] (score, patch index as float bits)
@@ -49,6 +55,8 @@ __host__ __device__ inline Scratch carve(void *base, int64_t Np, int32_t cap) {
     s.invn = (float *)p;
     p += align256(sizeof(float) * Np);
     s.theta = (float *)p;
+    p += align256(sizeof(float) * Np);
+    s.theta_g = (float *)p;
     p += align256(sizeof(float) * Np);
     s.cnt = (uint32_t *)p;
     p += align256(sizeof(uint32_t) * Np);
@@ -73,6 +81,7 @@ struct Args {
     int64_t seed_cols;       // columns of the seed phase (whole frames)
     int64_t sym_lo;          // start of the symmetric square [sym_lo, Np)^2
     float *chunk;            // STORE mode: cosines of rows [row_lo, row_hi) x all columns
+    int32_t guess_k;         // compaction: also set theta_g from the guess_k-th best (0: no)
 };
 
 template <typename T> __device__ inline float ldf(const T *p, int64_t i);
@@ -97,6 +106,7 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
     if (lane == 0) {
         A.s.invn[u] = acc > 0.f ? 1.f / sqrtf(acc) : 0.f;
         A.s.theta[u] = -INFINITY;
+        A.s.theta_g[u] = -INFINITY;
         // the seed phase fills slots [0, seed_cols minus the own frame)
         const int64_t fr = u / A.g.P;
         A.s.cnt[u] = A.all_rows_fallback ? 0u
@@ -209,7 +219,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         if (u < row_hi) {
             iu = A.s.invn[u];
             fr = (int32_t)(u / g.P);
-            thr = scaled_threshold(A.s.theta[u], iu);
+            thr = scaled_threshold(MODE == SYM ? A.s.theta_g[u] : A.s.theta[u], iu);
         }
         r_thr[tid] = thr;
         r_iu[tid] = iu;
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     } else if (MODE == SYM) {
         const int t = tid - CT;
         const int64_t v = col0 + t;
-        c_thr[t] = v < col_hi ? scaled_threshold(A.s.theta[v], A.s.invn[v]) : INFINITY;
+        c_thr[t] = v < col_hi ? scaled_threshold(A.s.theta_g[v], A.s.invn[v]) : INFINITY;
         c_cnt[t] = 0u;
     }
     const int32_t f_row_lo = (int32_t)(row0 / g.P);
@@ -506,15 +516,19 @@ __global__ __launch_bounds__(256) void compact_rows(const Args A) {
     const uint32_t c = A.s.cnt[u];
     const uint32_t nn = min(c, (uint32_t)A.cap);
     if (c > (uint32_t)A.cap && lane == 0) A.s.over[u] = 1u;
-    if ((int)nn <= A.K) return;
+    if ((int)nn <= A.K) {
+        if (A.guess_k && lane == 0) A.s.theta_g[u] = A.s.theta[u];
+        return;
+    }
     float2 *buf = A.s.cand + u * A.cap;
-    uint32_t total = nn, thr = 0;
+    uint32_t total = nn, thr = 0, gkey = 0;
     for (int pass = 0; pass < 4 && (int)total > A.K; ++pass) {
         const int nreg = (int)min<uint32_t>(total, 64u * MAXE);
         RowSel<MAXE> R;
         R.load(buf, nreg, lane);
         R.select_bound(A.K, lane);
         thr = R.thr;
+        if (A.guess_k) gkey = R.prefix_search(A.guess_k, lane, 16);
         if ((int)total == nreg) {
             uint32_t mine = 0;
 #pragma unroll
@@ -550,6 +564,7 @@ __global__ __launch_bounds__(256) void compact_rows(const Args A) {
     if (lane == 0) {
         A.s.cnt[u] = total;
         A.s.theta[u] = order_key_to_float(thr);
+        if (A.guess_k) A.s.theta_g[u] = order_key_to_float(max(gkey, thr));
     }
 }
 
@@ -576,6 +591,12 @@ __global__ __launch_bounds__(256) void finalize_rows(const Args A, uint32_t lo_c
     RowSel<MAXE> R;
     R.load(buf, nn, lane);
     R.select_exact(A.K, lane);
+    // A row of the symmetric pass kept only columns >= theta_g there; its
+    // K-th best is exact when it reaches theta_g, else recompute the row.
+    if (u >= A.sym_lo && R.thr < order_key(A.s.theta_g[u])) {
+        if (lane == 0) A.s.over[u] = 1u;
+        return;
+    }
     uint32_t mine = 0;
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) mine += R.kept(e, lane) ? 1u : 0u;
@@ -762,11 +783,24 @@ int32_t corr_capacity(const Geom &g, int32_t K) {
     return (int32_t)cap;
 }
 
+// bytes carve() lays out before rowbuf
+static size_t carve_head_bytes(int64_t Np, int32_t cap) {
+    return align256(sizeof(float) * Np) * 3 + align256(sizeof(uint32_t) * Np) * 2 +
+           align256(sizeof(float2) * (size_t)Np * cap);
+}
+
 size_t corr_scratch_bytes(const Geom &g, int32_t K, int32_t cap) {
     (void)K;
-    const int64_t Np = g.Np;
-    return align256(sizeof(float) * Np) * 2 + align256(sizeof(uint32_t) * Np) * 2 +
-           align256(sizeof(float2) * (size_t)Np * cap) + align256(sizeof(float) * (size_t)kFallbackBlocks * Np);
+    return carve_head_bytes(g.Np, cap) + align256(sizeof(float) * (size_t)kFallbackBlocks * g.Np);
+}
+
+// Rank whose value guesses the K-th best over all candidates from the W seen
+// columns: with the seen columns a fraction f of the candidates, the K-th best
+// overall sits near rank K f among them; 2.5x that rank keeps the chance that
+// fewer than K candidates reach the guess small (such rows are recomputed).
+static int32_t corr_guess_rank(const Geom &g, int32_t K, int64_t W) {
+    const double f = (double)W / ((double)(g.S - 1) * g.P);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(K, (int64_t)std::ceil(2.5 * K * f)));
 }
 
 // rows per chunk of the per-frame mode: a multiple of the tile height whose
@@ -779,8 +813,7 @@ int32_t corr_frame_chunk_rows(const Geom &g) {
 }
 
 size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows) {
-    return align256(sizeof(float) * g.Np) * 2 + align256(sizeof(uint32_t) * g.Np) * 2 +
-           align256(sizeof(float) * (size_t)chunk_rows * g.Np);
+    return carve_head_bytes(g.Np, 0) + align256(sizeof(float) * (size_t)chunk_rows * g.Np);
 }
 
 static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, hipStream_t stream) {
@@ -853,6 +886,8 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             const unsigned nb = (unsigned)((A.row_hi - A.row_lo + kRowWaves - 1) / kRowWaves);
             hipLaunchKernelGGL(compact_rows<16>, dim3(nb), dim3(256), 0, stream, A);
         };
+        const int64_t W = A.sym_lo;
+        const int32_t guess = corr_guess_rank(B.g, B.K, W);
         auto rect = [&](int mode, int64_t r_lo, int64_t r_hi, int64_t c_lo, int64_t c_hi) {
             A.row_lo = r_lo;
             A.row_hi = r_hi;
@@ -866,9 +901,12 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             else
                 hipLaunchKernelGGL(cos_phase<FILTER>, grid, dim3(kCosThreads), 0, stream, A);
             if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+            // the compaction after every row has seen [0, W) sets the
+            // symmetric pass's thresholds
+            A.guess_k = (W < Np && r_lo == 0 && r_hi == Np && c_hi == W) ? guess : 0;
             compact();
+            A.guess_k = 0;
         };
-        const int64_t W = A.sym_lo;
         // 1. seed: frames 0 and 1 for every row, every candidate kept
         rect(SEED, 0, Np, 0, A.seed_cols);
         // 2. doubling filtered phases for every row up to W

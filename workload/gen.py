@@ -288,3 +288,22 @@ def sample_rows(geom: Geometry, n_target: int, seed: int = 12345) -> np.ndarray:
         pick = rng.choice(N, size=min(extra, N), replace=False)
         base = np.unique(np.concatenate([base, pick.astype(np.int64)]))
     return base
+
+
+def make_front_loaded_dino(S: int, P: int, Df: int, first_frames: int, n_rows: int, copies: int,
+                           seed: int) -> Tuple[np.ndarray, np.ndarray]:
+    """bf16 features [S*P, Df] of i.i.d. N(0, 1) draws, except that n_rows
+    patches of frames >= first_frames each get `copies` near-copies (the
+    patch plus N(0, 0.05^2) noise) among the patches of frames
+    [0, first_frames).  Returns (features as bf16 bits, the n_rows patches).
+    Such rows have their best matches concentrated in the first frames."""
+    rng = np.random.default_rng(seed)
+    F = rng.standard_normal((S * P, Df), dtype=np.float32)
+    front = first_frames * P
+    if n_rows * copies > front:
+        raise ValueError("not enough patches in the first frames for the copies")
+    rows = np.sort(rng.choice(np.arange(front, S * P), n_rows, replace=False))
+    slots = rng.permutation(front)[:n_rows * copies].reshape(n_rows, copies)
+    for r, sl in zip(rows, slots):
+        F[sl] = F[r] + np.float32(0.05) * rng.standard_normal((copies, Df), dtype=np.float32)
+    return bf16_round(F), rows
