@@ -228,6 +228,67 @@ def attention(q, k, v, rows, keys) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # One layer: every head by its role, on a subset of query rows.
+def block_scores(F: np.ndarray, S: int, P: int, b: int, qblocks: Sequence[int]) -> np.ndarray:
+    """Block-wise DINO similarity (Sec. 4.3, block-wise implementation).
+
+    Blocks are b consecutive patches of one frame (b divides P); block B =
+    patches B*b .. B*b+b-1.  The similarity of two blocks is the token-level
+    cosine averaged over their b x b patch pairs, computed here literally
+    from the cosine rows.  Returns [len(qblocks), S*P/b]; NaN for the blocks
+    of the query block's own frame."""
+    if P % b:
+        raise ValueError("block size must divide P")
+    nb = S * (P // b)
+    qblocks = _i64(qblocks)
+    out = np.empty((qblocks.size, nb), dtype=np.float64)
+    for i, A in enumerate(qblocks):
+        c = corr_scores(F, S, P, np.arange(A * b, (A + 1) * b))   # [b, S*P]
+        out[i] = c.reshape(b, nb, b).mean(axis=(0, 2))
+    return out
+
+
+def block_corr_index(F: np.ndarray, S: int, ns: int, P: int, b: int, K: int, rows: Sequence[int],
+                     mode: int = MODE_TOTAL):
+    """Correspondence key rows under block-wise similarity.
+
+    Every patch of query block A gets the patches of A's selected blocks: the
+    first min(K, (S-1)P/b) blocks of other frames by (similarity desc, block
+    asc) (total mode), or the first min(K, P/b) of every other frame
+    (per-frame mode).  Returns (idx [nrows, kb*b] global tokens ascending,
+    {query block: (selected blocks, kth score, best dropped score)})."""
+    if P % b:
+        raise ValueError("block size must divide P")
+    T, per = ns + P, P // b
+    rows = _i64(rows)
+    qb = np.unique(rows // b)
+    sc = block_scores(F, S, P, b, qb)
+    blk = np.arange(S * per)
+    sel = {}
+    for i, A in enumerate(qb):
+        fa = A // per
+        if mode == MODE_TOTAL:
+            ok = blk // per != fa
+            ids, kth, nxt = topk(sc[i][ok], K, blk[ok])
+        else:
+            parts, kth, nxt = [], [], []
+            for f in range(S):
+                if f == fa:
+                    continue
+                g = blk[f * per:(f + 1) * per]
+                ids_f, k_f, n_f = topk(sc[i][g], K, g)
+                parts.append(ids_f)
+                kth.append(k_f)
+                nxt.append(n_f)
+            ids = np.concatenate(parts)
+        sel[int(A)] = (ids, kth, nxt)
+    kb = len(next(iter(sel.values()))[0]) if sel else 0
+    out = np.empty((rows.size, kb * b), dtype=np.int64)
+    for r, u in enumerate(rows):
+        patches = (sel[int(u // b)][0][:, None] * b + np.arange(b)[None, :]).reshape(-1)
+        out[r] = (patches // P) * T + ns + patches % P
+    return out, sel
+
+
 # ---------------------------------------------------------------------------
 def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int = MODE_TOTAL,
                rows: Optional[np.ndarray] = None, corr_rows: Optional[Dict[int, np.ndarray]] = None):

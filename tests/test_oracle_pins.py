@@ -327,3 +327,72 @@ def test_layer_corr_heads_specials_attend_everything():
             mask[i, want_idx[u]] = True
     want = _masked_dense(w.q[0], w.k[0], w.v[0], mask)
     np.testing.assert_allclose(outs[0], want, rtol=0, atol=1e-12)
+
+
+# ---- block-wise DINO similarity (Sec. 4.3 "block-wise implementation")
+@pytest.mark.parametrize("mode", [oracle.MODE_TOTAL, oracle.MODE_PER_FRAME])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_index_with_one_patch_blocks_is_the_token_index(mode, dtype):
+    geom = Geometry(S=4, ns=5, P=30)
+    w = make_geometry_inputs(geom, dtype, [ROLE_CORRESPONDENCE] * 16, [8] * 16, M=80, Df=48, seed=5)
+    rows = np.arange(geom.Np)
+    want, _, _ = oracle.corr_index(w.dino, geom.S, geom.ns, geom.P, 8, rows, mode)
+    got, _ = oracle.block_corr_index(w.dino, geom.S, geom.ns, geom.P, 1, 8, rows, mode)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_block_scores_equal_dot_of_mean_unit_vectors():
+    # mean over a x b pairs of u.v/(|u||v|) = (mean of unit u) . (mean of unit v)
+    S, P, b, Df = 3, 12, 4, 20
+    F = _rand((S * P, Df), 23)
+    F[5] = 0.0                        # a zero feature contributes cosine 0
+    F64 = F.astype(np.float64)
+    n = np.linalg.norm(F64, axis=1)
+    U = np.divide(F64, n[:, None], out=np.zeros_like(F64), where=n[:, None] > 0)
+    M = U.reshape(S * P // b, b, Df).mean(axis=1)
+    sc = oracle.block_scores(F, S, P, b, np.arange(S * P // b))
+    want = M @ M.T
+    per = P // b
+    own = (np.arange(S * per)[:, None] // per) == (np.arange(S * per)[None, :] // per)
+    assert np.all(np.isnan(sc[own]))
+    np.testing.assert_allclose(sc[~own], want[~own], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [oracle.MODE_TOTAL, oracle.MODE_PER_FRAME])
+def test_block_index_recovers_planted_block_matches(mode):
+    # one-hot features: block j of frame 0 is e_j in all its patches; block k
+    # of frame 1 is e_perm[k].  The only block of frame 1 with similarity 1 to
+    # frame-0 block j is perm^-1(j); everything else scores 0 against it.
+    S, ns, P, b = 2, 3, 24, 6
+    per = P // b
+    perm = np.array([2, 0, 3, 1])
+    F = np.zeros((S * P, 8), dtype=np.float32)
+    for j in range(per):
+        F[j * b:(j + 1) * b, j] = 1.0
+        F[P + j * b:P + (j + 1) * b, perm[j]] = 1.0
+    rows = np.arange(S * P)
+    got, sel = oracle.block_corr_index(F, S, ns, P, b, 1, rows, mode)
+    T = ns + P
+    for j in range(per):
+        k = int(np.where(perm == j)[0][0])            # frame-1 block holding e_j
+        assert sel[j][0].tolist() == [per + k]
+        assert sel[per + k][0].tolist() == [j]
+        want = [T + ns + k * b + i for i in range(b)]
+        for u in range(j * b, (j + 1) * b):
+            assert got[u].tolist() == want
+
+
+def test_block_index_shares_sets_within_a_block_and_clamps():
+    geom = Geometry(S=5, ns=2, P=16)
+    w = make_geometry_inputs(geom, "f32", [ROLE_CORRESPONDENCE] * 16, [8] * 16, M=40, Df=24, seed=8)
+    rows = np.arange(geom.Np)
+    got, _ = oracle.block_corr_index(w.dino, 5, 2, 16, 4, 3, rows)
+    assert got.shape == (geom.Np, 12)
+    for u in rows:
+        np.testing.assert_array_equal(got[u], got[(u // 4) * 4])
+        assert np.all(np.diff(got[u]) > 0)
+        assert np.all(got[u] // geom.T != u // 16)            # other frames only
+    pf, _ = oracle.block_corr_index(w.dino, 5, 2, 16, 4, 100, rows, oracle.MODE_PER_FRAME)
+    assert pf.shape == (geom.Np, 4 * 16)                       # clamps to every other patch
+    with pytest.raises(ValueError):
+        oracle.block_corr_index(w.dino, 5, 2, 16, 3, 3, rows)
