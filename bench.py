@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--reps", type=int, default=10, help="reps of each breakdown measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--block", type=int, default=37,
+                    help="also time the block-wise index with blocks of this many patches (0: skip)")
+    ap.add_argument("--block-k", type=int, default=7, help="blocks kept per query block for --block")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device to device twice (a known-size kernel for HBM counters)")
     ap.add_argument("--per-frame-k", type=int, default=4,
@@ -244,6 +247,31 @@ def main():
                      "tflops": round(2.0 * g.Np * g.Np * w.Df / (pf_ms * 1e-3) / 1e12, 2)}
         pctx.close()
 
+    # block-wise index (blocks of --block patches, --block-k blocks per query
+    # block) and the layer on it, in a context of its own; not part of the step
+    block = None
+    if args.block > 0 and g.P % args.block == 0:
+        bctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+        bplan = [(r, 0 if r == 2 else b, a, f) for (r, b, a, f) in w.plan]
+        bctx.build_corr_index_blocks(dino, args.block, args.block_k)
+        bctx.sparse_attention(bplan, q, k, v, o=o)
+        torch.cuda.synchronize()
+        bt, ba = [], []
+        for _ in range(3):
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(stream)
+            bctx.build_corr_index_blocks(dino, args.block, args.block_k)
+            e1.record(stream)
+            bctx.sparse_attention(bplan, q, k, v, o=o)
+            e2.record(stream)
+            torch.cuda.synchronize()
+            bt.append(e0.elapsed_time(e1))
+            ba.append(e1.elapsed_time(e2))
+        block = {"block": args.block, "K_blocks": args.block_k, "row_length": bctx.corr_k(),
+                 "build_ms": round(statistics.median(bt), 3), "attn_only_ms": round(statistics.median(ba), 4),
+                 "step_ms": round(statistics.median(bt) + statistics.median(ba), 3)}
+        bctx.close()
+
     # ---- roofline of the dominant kernel (largest single-kernel share)
     pairs = key_counts(w)
     shared_pairs = sum(p for kind, p in pairs if kind == "shared")
@@ -316,6 +344,7 @@ def main():
         "speedup_attn_vs_dense": round(dense_ms / attn_ms, 2) if dense_ms else None,
         "speedup_step_vs_dense": round(dense_ms / ms_per_step, 2) if dense_ms else None,
         "per_frame_index": per_frame,
+        "block_index": block,
         "sparsity": round(1.0 - (shared_pairs + gather_pairs) / (g.H * g.N * g.N), 4),
         "roofline": roofline,
         "roofline_other": others,

@@ -60,6 +60,7 @@ _PROTOS = {
     "saf_last_error": (C.c_char_p, [_VP]),
     "saf_workspace_size": (C.c_int, [_VP, _VP, C.POINTER(_SZ)]),
     "saf_build_corr_index": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _VP]),
+    "saf_build_corr_index_blocks": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _I32, _VP]),
     "saf_set_corr_index": (C.c_int, [_VP, _VP, _I32, _VP]),
     "saf_get_corr_index": (C.c_int, [_VP, _VP, C.POINTER(_I32), _VP]),
     "saf_build_vertical_index": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _VP, _VP, _SZ, _VP]),
@@ -110,6 +111,10 @@ def saf_workspace_size(ctx, plan, nbytes: C.c_size_t) -> int:
 
 def saf_build_corr_index(ctx, dino, dino_dtype, Df, row_stride, K, mode, stream) -> int:
     return lib().saf_build_corr_index(ctx, dino, dino_dtype, Df, row_stride, K, mode, stream)
+
+
+def saf_build_corr_index_blocks(ctx, dino, dino_dtype, Df, row_stride, block, K, mode, stream) -> int:
+    return lib().saf_build_corr_index_blocks(ctx, dino, dino_dtype, Df, row_stride, block, K, mode, stream)
 
 
 def saf_set_corr_index(ctx, dev_idx, Kc, stream) -> int:
@@ -215,6 +220,13 @@ class Context:
             raise ValueError("dino must be [S*P, Df] with contiguous channels")
         self._check(saf_build_corr_index(self._ctx, C.c_void_p(dino.data_ptr()), _DT.get(dino.dtype, 99),
                                          dino.shape[1], dino.stride(0), K, mode, _stream(stream)))
+
+    def build_corr_index_blocks(self, dino: torch.Tensor, block: int, K: int, mode: int = SAF_CORR_TOTAL,
+                                stream=None):
+        if dino.dim() != 2 or dino.stride(1) != 1:
+            raise ValueError("dino must be [S*P, Df] with contiguous channels")
+        self._check(saf_build_corr_index_blocks(self._ctx, C.c_void_p(dino.data_ptr()), _DT.get(dino.dtype, 99),
+                                                dino.shape[1], dino.stride(0), block, K, mode, _stream(stream)))
 
     def set_corr_index(self, idx: torch.Tensor, stream=None):
         if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():

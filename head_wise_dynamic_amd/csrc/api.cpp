@@ -286,6 +286,25 @@ static saf_status_t ensure_corr_storage(saf_ctx_t *c, int32_t K) {
     return SAF_OK;
 }
 
+// grow the context-owned build scratch to at least sb bytes
+static saf_status_t ensure_corr_scratch(saf_ctx_t *c, size_t sb) {
+    if (c->corr_scratch_bytes >= sb) return SAF_OK;
+    if (c->corr_scratch) {
+        hipError_t e = hipFree(c->corr_scratch);
+        c->corr_scratch = nullptr;
+        c->corr_scratch_bytes = 0;
+        if (e != hipSuccess) return hip_fail(c, e, "hipFree(corr scratch)");
+    }
+    hipError_t e = hipMalloc(&c->corr_scratch, sb);
+    if (e != hipSuccess) {
+        c->corr_scratch = nullptr;
+        (void)hipGetLastError();
+        return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for index scratch failed", sb);
+    }
+    c->corr_scratch_bytes = sb;
+    return SAF_OK;
+}
+
 saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_dtype, int32_t Df,
                                   int64_t row_stride, int32_t K, int32_t mode, void *stream) {
     if (!c) return SAF_EINVAL;
@@ -321,21 +340,8 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     const int32_t cap = per_frame ? 0 : saf::corr_capacity(g, Kc);
     const int32_t chunk_rows = per_frame ? saf::corr_frame_chunk_rows(g) : 0;
     const size_t sb = per_frame ? saf::corr_frame_scratch_bytes(g, chunk_rows) : saf::corr_scratch_bytes(g, Kc, cap);
-    if (c->corr_scratch_bytes < sb) {
-        if (c->corr_scratch) {
-            hipError_t e = hipFree(c->corr_scratch);
-            c->corr_scratch = nullptr;
-            c->corr_scratch_bytes = 0;
-            if (e != hipSuccess) return hip_fail(c, e, "hipFree(corr scratch)");
-        }
-        hipError_t e = hipMalloc(&c->corr_scratch, sb);
-        if (e != hipSuccess) {
-            c->corr_scratch = nullptr;
-            (void)hipGetLastError();
-            return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for index scratch failed", sb);
-        }
-        c->corr_scratch_bytes = sb;
-    }
+    st = ensure_corr_scratch(c, sb);
+    if (st != SAF_OK) return st;
     saf::CorrBuild B{};
     B.g = g;
     B.dino = dino;
@@ -358,6 +364,57 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     if (e != hipSuccess) return hip_fail(c, e, "correspondence index kernels");
     c->corr_k = Kc;
     c->corr_build_k = Kk;
+    return SAF_OK;
+}
+
+saf_status_t saf_build_corr_index_blocks(saf_ctx_t *c, const void *dino, int32_t dino_dtype, int32_t Df,
+                                         int64_t row_stride, int32_t block, int32_t K, int32_t mode,
+                                         void *stream) {
+    if (!c) return SAF_EINVAL;
+    const saf::Geom &g = c->g;
+    if (!dino) return fail(c, SAF_EINVAL, "null dino pointer");
+    if (dino_dtype != SAF_F32 && dino_dtype != SAF_BF16) return fail(c, SAF_EINVAL, "bad dino dtype");
+    if (g.S < 2) return fail(c, SAF_EINVAL, "correspondence index needs S >= 2");
+    if (K < 1) return fail(c, SAF_EINVAL, "K %d < 1", K);
+    if (Df < 1) return fail(c, SAF_EINVAL, "Df %d < 1", Df);
+    if (row_stride < Df) return fail(c, SAF_EINVAL, "dino row stride %lld < Df", (long long)row_stride);
+    if (block < 1 || g.P % block) return fail(c, SAF_EINVAL, "block %d does not divide P = %d", block, g.P);
+    if (mode != SAF_CORR_TOTAL && mode != SAF_CORR_PER_FRAME) return fail(c, SAF_EINVAL, "bad mode %d", mode);
+    if (Df > 4096) return fail(c, SAF_EUNSUPPORTED, "Df %d > 4096", Df);
+    const bool per_frame = mode == SAF_CORR_PER_FRAME;
+    const int32_t per = g.P / block;
+    if (per_frame && per > saf::kFrameMaxP)
+        return fail(c, SAF_EUNSUPPORTED, "per-frame mode: %d blocks per frame > %d", per, saf::kFrameMaxP);
+    const int32_t rb = saf::corr_block_row_blocks(g, block, K, per_frame ? 1 : 0);
+    if (!per_frame && rb > 1024) return fail(c, SAF_EUNSUPPORTED, "%d blocks per row > 1024", rb);
+    const int64_t kc64 = (int64_t)rb * block;
+    if (kc64 > INT32_MAX / 2) return fail(c, SAF_EUNSUPPORTED, "index row of %lld entries", (long long)kc64);
+    const int32_t Kc = (int32_t)kc64;
+    saf_status_t st = ensure_corr_storage(c, Kc);
+    if (st != SAF_OK) return st;
+    st = ensure_corr_scratch(c, saf::corr_block_scratch_bytes(g, block, Df, K, per_frame ? 1 : 0));
+    if (st != SAF_OK) return st;
+    saf::CorrBlockBuild B{};
+    B.g = g;
+    B.dino = dino;
+    B.dino_dtype = dino_dtype;
+    B.Df = Df;
+    B.row_stride = row_stride;
+    B.block = block;
+    B.K = per_frame ? std::min(K, per) : rb;
+    B.per_frame = per_frame ? 1 : 0;
+    B.idx_out = c->corr_idx;
+    B.scratch = c->corr_scratch;
+    B.mark = mark_launch;
+    B.mark_user = c;
+    hipError_t e;
+    {
+        Timed tm(c, as_stream(stream), "corr_index_blocks");
+        e = saf::launch_corr_blocks(B, as_stream(stream));
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "block correspondence index kernels");
+    c->corr_k = Kc;
+    c->corr_build_k = B.K;
     return SAF_OK;
 }
 

@@ -82,6 +82,7 @@ struct Args {
     int64_t sym_lo;          // start of the symmetric square [sym_lo, Np)^2
     float *chunk;            // STORE mode: cosines of rows [row_lo, row_hi) x all columns
     int32_t guess_k;         // compaction: also set theta_g from the guess_k-th best (0: no)
+    int32_t raw_dot;         // scores are plain dot products (unit "norms")
 };
 
 template <typename T> __device__ inline float ldf(const T *p, int64_t i);
@@ -104,7 +105,7 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
     if (lane == 0) {
-        A.s.invn[u] = acc > 0.f ? 1.f / sqrtf(acc) : 0.f;
+        A.s.invn[u] = A.raw_dot ? 1.f : (acc > 0.f ? 1.f / sqrtf(acc) : 0.f);
         A.s.theta[u] = -INFINITY;
         A.s.theta_g[u] = -INFINITY;
         // the seed phase fills slots [0, seed_cols minus the own frame)
@@ -623,18 +624,57 @@ __global__ __launch_bounds__(256) void finalize_rows(const Args A, uint32_t lo_c
     }
 }
 
-// ---- per-frame mode: cosines of a row chunk on the VALU (fp32 features, or
-// a channel count the matrix-core tiles do not cover)
-template <typename T> __global__ __launch_bounds__(256) void cos_store_valu(const Args A) {
+// ---- cosines of a row chunk on the VALU (fp32 features, or a channel count
+// the matrix-core tiles do not cover): 64 x 64 output tiles per work-group,
+// 16-channel slices of both operands staged in LDS, 4 x 4 outputs per thread.
+constexpr int kStoreTile = 64, kStoreK = 16;
+template <typename T> __global__ __launch_bounds__(256) void cos_store_tiled(const Args A) {
+    __shared__ float As[kStoreK][kStoreTile + 4], Bs[kStoreK][kStoreTile + 4];
     const Geom &g = A.g;
-    const int64_t rows = A.row_hi - A.row_lo;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= rows * g.Np) return;
-    const int64_t u = A.row_lo + idx / g.Np, v = idx % g.Np;
     const T *F = (const T *)A.F;
-    float acc = 0.f;
-    for (int c = 0; c < A.Df; ++c) acc = fmaf(ldf<T>(F, u * A.stride + c), ldf<T>(F, v * A.stride + c), acc);
-    A.chunk[idx] = acc * (A.s.invn[u] * A.s.invn[v]);
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int64_t r0 = A.row_lo + (int64_t)blockIdx.y * kStoreTile, c0 = (int64_t)blockIdx.x * kStoreTile;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int k0 = 0; k0 < A.Df; k0 += kStoreK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + 256 * i, r = e / kStoreK, k = e % kStoreK;
+            const int64_t u = r0 + r, v = c0 + r;
+            const bool kin = k0 + k < A.Df;
+            As[k][r] = (u < A.row_hi && kin) ? ldf<T>(F, u * A.stride + k0 + k) : 0.f;
+            Bs[k][r] = (v < g.Np && kin) ? ldf<T>(F, v * A.stride + k0 + k) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kStoreK; ++k) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = As[k][ty + 16 * i];
+                b[i] = Bs[k][tx + 16 * i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t u = r0 + ty + 16 * i;
+        if (u >= A.row_hi) continue;
+        const float iu = A.s.invn[u];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t v = c0 + tx + 16 * j;
+            if (v < g.Np) A.chunk[(u - A.row_lo) * g.Np + v] = acc[i][j] * (iu * A.s.invn[v]);
+        }
+    }
 }
 
 // ---- per-frame mode: one wave per (row, other frame) selects the frame's K
@@ -645,7 +685,7 @@ template <typename T> __global__ __launch_bounds__(256) void cos_store_valu(cons
 // for the K-th key and the index cut among its ties.
 constexpr int kFrameRoundsMaxK = 8;
 
-template <int MAXE>
+template <int MAXE, bool CAND>
 __global__ __launch_bounds__(256) void frame_topk(const Args A) {
     const Geom &g = A.g;
     const int lane = threadIdx.x & 63;
@@ -716,6 +756,28 @@ __global__ __launch_bounds__(256) void frame_topk(const Args A) {
                 keep |= 1ull << e;
     }
     const int32_t slot = gf - (gf > fu ? 1 : 0);
+    if (CAND) {
+        // candidates (score, patch) for an exact selection over all frames
+        float2 *cand = A.s.cand + u * A.cap + (int64_t)slot * A.K;
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        uint32_t pos = 0;
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) {
+            if (e < ne) {
+                const bool kp = (keep >> e) & 1ull;
+                const uint64_t m = __ballot(kp);
+                if (kp)
+                    cand[pos + (uint32_t)__popcll(m & below)] =
+                        make_float2(order_key_to_float(key[e]), __int_as_float(gf * g.P + e * 64 + lane));
+                pos += (uint32_t)__popcll(m);
+            }
+        }
+        if (slot == 0 && lane == 0) {
+            A.s.cnt[u] = (uint32_t)((g.S - 1) * A.K);
+            A.s.over[u] = 0u;
+        }
+        return;
+    }
     int32_t *out = A.idx_out + u * ((int64_t)(g.S - 1) * A.K) + (int64_t)slot * A.K;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int32_t tok0 = gf * g.T + g.ns;
@@ -816,10 +878,20 @@ size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows) {
     return carve_head_bytes(g.Np, 0) + align256(sizeof(float) * (size_t)chunk_rows * g.Np);
 }
 
-static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, hipStream_t stream) {
+size_t corr_raw_total_scratch_bytes(const Geom &g, int32_t K) {
+    const int32_t cap = (g.S - 1) * std::min<int32_t>(K, g.P);
+    const int64_t rows = std::max<int64_t>(corr_frame_chunk_rows(g), kFallbackBlocks);
+    return carve_head_bytes(g.Np, cap) + align256(sizeof(float) * (size_t)rows * g.Np);
+}
+
+// cand = false: per-frame index into A.idx_out.  cand = true: every row's
+// per-frame top-A.K as (score, patch) candidates in A.s.cand (A.cap =
+// (S-1) A.K per row), for an exact selection over all frames afterwards.
+static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, bool cand, hipStream_t stream) {
     const Geom &g = B.g;
     const int64_t Np = g.Np;
-    A.chunk = A.s.rowbuf;  // cand is empty (cap 0): the chunk follows the per-row arrays
+    if (B.chunk_rows < 1) return hipErrorInvalidValue;
+    A.chunk = A.s.rowbuf;  // the chunk follows the per-row arrays and candidates
     const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0;
     for (int64_t r0 = 0; r0 < Np; r0 += B.chunk_rows) {
         A.row_lo = r0;
@@ -833,18 +905,26 @@ static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, hipStream_t st
             hipLaunchKernelGGL(cos_phase<STORE>, dim3((unsigned)(8 * ((tiles + 7) / 8))), dim3(kCosThreads), 0,
                                stream, A);
         } else {
-            const unsigned nb = (unsigned)((rows * Np + 255) / 256);
+            const dim3 grid((unsigned)((Np + kStoreTile - 1) / kStoreTile),
+                            (unsigned)((rows + kStoreTile - 1) / kStoreTile));
             if (B.dino_dtype == BF16)
-                hipLaunchKernelGGL(cos_store_valu<uint16_t>, dim3(nb), dim3(256), 0, stream, A);
+                hipLaunchKernelGGL(cos_store_tiled<uint16_t>, grid, dim3(256), 0, stream, A);
             else
-                hipLaunchKernelGGL(cos_store_valu<float>, dim3(nb), dim3(256), 0, stream, A);
+                hipLaunchKernelGGL(cos_store_tiled<float>, grid, dim3(256), 0, stream, A);
         }
         if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
         const unsigned fb = (unsigned)((rows * g.S + kRowWaves - 1) / kRowWaves);
-        if (g.P <= 24 * 64)
-            hipLaunchKernelGGL(frame_topk<24>, dim3(fb), dim3(256), 0, stream, A);
-        else
-            hipLaunchKernelGGL(frame_topk<64>, dim3(fb), dim3(256), 0, stream, A);
+        if (cand) {
+            if (g.P <= 24 * 64)
+                hipLaunchKernelGGL((frame_topk<24, true>), dim3(fb), dim3(256), 0, stream, A);
+            else
+                hipLaunchKernelGGL((frame_topk<64, true>), dim3(fb), dim3(256), 0, stream, A);
+        } else {
+            if (g.P <= 24 * 64)
+                hipLaunchKernelGGL((frame_topk<24, false>), dim3(fb), dim3(256), 0, stream, A);
+            else
+                hipLaunchKernelGGL((frame_topk<64, false>), dim3(fb), dim3(256), 0, stream, A);
+        }
     }
     return hipGetLastError();
 }
@@ -858,6 +938,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.K = B.K;
     A.cap = B.cap;
     A.idx_out = B.idx_out;
+    A.raw_dot = B.raw_dot;
     const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024;
     A.all_rows_fallback = gemm ? 0 : 1;
     A.s = carve(B.scratch, B.g.Np, B.per_frame ? 0 : B.cap);
@@ -870,7 +951,37 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
         else
             hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
-        return launch_corr_frames(A, B, stream);
+        return launch_corr_frames(A, B, false, stream);
+    }
+    if (B.raw_dot) {
+        // Total mode by way of frames: the K best overall lie among the
+        // min(K, P) best of each frame, so every row's per-frame top lists
+        // become its candidates and finalize selects exactly among them.
+        if (B.g.P > kFrameMaxP) return hipErrorInvalidValue;
+        const int32_t kf = std::min<int32_t>(B.K, B.g.P);
+        A.cap = (B.g.S - 1) * kf;
+        A.s = carve(B.scratch, Np, A.cap);
+        A.seed_cols = 0;
+        A.sym_lo = Np;
+        A.all_rows_fallback = 0;
+        const unsigned rb = (unsigned)((Np + 3) / 4);
+        if (B.dino_dtype == BF16)
+            hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
+        else
+            hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
+        Args F = A;
+        F.K = kf;
+        hipError_t e = launch_corr_frames(F, B, true, stream);
+        if (e != hipSuccess) return e;
+        const unsigned cb = (unsigned)((Np + kRowWaves - 1) / kRowWaves);
+        hipLaunchKernelGGL(finalize_rows<16>, dim3(cb), dim3(256), 0, stream, A, 0u, 16u * 64u);
+        hipLaunchKernelGGL(finalize_rows<64>, dim3(cb), dim3(256), 0, stream, A, 16u * 64u, 0xFFFFFFFFu);
+        const unsigned fb = (unsigned)std::min<int64_t>(kFallbackBlocks, Np);
+        if (B.dino_dtype == BF16)
+            hipLaunchKernelGGL(fallback_rows<uint16_t>, dim3(fb), dim3(1024), 0, stream, A);
+        else
+            hipLaunchKernelGGL(fallback_rows<float>, dim3(fb), dim3(1024), 0, stream, A);
+        return hipGetLastError();
     }
     A.seed_cols = std::min<int64_t>(Np, 2 * (int64_t)B.g.P);
     A.sym_lo = corr_sym_start(B.g);

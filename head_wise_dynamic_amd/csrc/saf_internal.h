@@ -103,6 +103,7 @@ struct CorrBuild {
     int32_t cap;    // candidate capacity per row (total mode)
     int32_t per_frame;  // 1: the K best of every other frame, [Np, (S-1) K]
     int32_t chunk_rows; // per-frame mode: rows whose cosines are materialised at once
+    int32_t raw_dot;    // 1: rank by the plain dot product f_u . f_v (no normalisation)
     int32_t *idx_out;   // [Np, K] or [Np, (S-1) K]
     void *scratch;      // corr_scratch_bytes() / corr_frame_scratch_bytes()
     // optional tracing hook: called with begin = 1 / 0 around every cosine
@@ -115,6 +116,30 @@ int32_t corr_capacity(const Geom &g, int32_t K);
 constexpr int32_t kFrameMaxP = 4096;  // per-frame mode: patches per frame the selection holds
 int32_t corr_frame_chunk_rows(const Geom &g);
 size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows);
+// raw_dot total mode (per-frame candidates, then an exact selection)
+size_t corr_raw_total_scratch_bytes(const Geom &g, int32_t K);
 hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream);
+
+// Block-wise index: blocks of `block` consecutive patches of a frame; block
+// similarity = dot of the blocks' mean unit features (the token cosine
+// averaged over the block pairs); each patch gets the patches of its block's
+// selected blocks.
+struct CorrBlockBuild {
+    Geom g;                 // token geometry (P % block == 0)
+    const void *dino;
+    int32_t dino_dtype, Df;
+    int64_t row_stride;
+    int32_t block;          // patches per block
+    int32_t K;              // blocks kept per query block (total) or per other frame (clamped)
+    int32_t per_frame;
+    int32_t *idx_out;       // [Np, Kc] tokens, Kc = kept blocks * block
+    void *scratch;          // corr_block_scratch_bytes()
+    void (*mark)(void *user, int begin, const char *name, hipStream_t stream);
+    void *mark_user;
+};
+Geom corr_block_geom(const Geom &g, int32_t block);
+int32_t corr_block_row_blocks(const Geom &g, int32_t block, int32_t K, int per_frame);
+size_t corr_block_scratch_bytes(const Geom &g, int32_t block, int32_t Df, int32_t K, int per_frame);
+hipError_t launch_corr_blocks(const CorrBlockBuild &B, hipStream_t stream);
 
 }  // namespace saf

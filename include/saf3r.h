@@ -146,6 +146,27 @@ saf_status_t saf_build_corr_index(saf_ctx_t *ctx, const void *dino, int32_t dino
                                   int32_t Df, int64_t dino_row_stride, int32_t K,
                                   int32_t mode, void *stream);
 
+/* Block-wise variant of the correspondence index (Sec. 4.3: block-level
+ * similarities averaged over tokens, a cheaper build).  A block is `block`
+ * consecutive patches of one frame (block must divide P; block = the patch
+ * grid width makes it one row of patches).  The similarity of blocks A and B
+ * is the token cosine averaged over their block x block patch pairs, i.e. the
+ * dot product of the blocks' mean unit features (fp32; zero features count
+ * as 0).  For every query block the blocks of other frames are ranked by
+ * (similarity desc, block asc):
+ *   SAF_CORR_TOTAL:     the first min(K, (S-1)P/block) blocks (at most 1024);
+ *   SAF_CORR_PER_FRAME: the first min(K, P/block) of every other frame.
+ * Every patch of the query block gets the patches of those blocks, so
+ * Kc = kept blocks * block global token indices per row, ascending.  The
+ * result replaces the cached index exactly like saf_build_corr_index, and a
+ * correspondence head's budget may name Kc or the K kept here.
+ * Errors: SAF_EINVAL (S < 2, K < 1, Df < 1, block not dividing P, bad
+ * mode/stride/pointer), SAF_EUNSUPPORTED (Df > 4096, too many blocks),
+ * SAF_ENOMEM. */
+saf_status_t saf_build_corr_index_blocks(saf_ctx_t *ctx, const void *dino, int32_t dino_dtype,
+                                         int32_t Df, int64_t dino_row_stride, int32_t block,
+                                         int32_t K, int32_t mode, void *stream);
+
 /* Replace the cached index with caller data: dev_idx holds S*P rows of Kc
  * global token indices (int32, device memory), each row a set of distinct
  * patch tokens of other frames.  The data is copied (stream-ordered).

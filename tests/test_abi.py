@@ -138,6 +138,26 @@ def test_build_corr_index_validation():
         saf.saf_destroy(c)
 
 
+def test_build_corr_index_blocks_validation():
+    c = _ctx()
+    try:
+        b = saf.saf_build_corr_index_blocks
+        assert b(c, None, 1, 64, 64, 4, 8, 0, None) == saf.SAF_EINVAL
+        assert b(c, FAKE, 1, 64, 64, 0, 8, 0, None) == saf.SAF_EINVAL       # block < 1
+        assert b(c, FAKE, 1, 64, 64, 3, 8, 0, None) == saf.SAF_EINVAL       # 3 does not divide P = 256
+        assert b(c, FAKE, 1, 64, 64, 4, 0, 0, None) == saf.SAF_EINVAL       # K < 1
+        assert b(c, FAKE, 1, 64, 64, 4, 8, 2, None) == saf.SAF_EINVAL       # mode
+        assert b(c, FAKE, 1, 64, 32, 4, 8, 0, None) == saf.SAF_EINVAL       # stride < Df
+        assert b(c, FAKE, 1, 8192, 8192, 4, 8, 0, None) == saf.SAF_EUNSUPPORTED  # Df
+    finally:
+        saf.saf_destroy(c)
+    c = _ctx(S=9)
+    try:   # 2000 of the 8 x 256 one-patch blocks in one row
+        assert saf.saf_build_corr_index_blocks(c, FAKE, 1, 64, 64, 1, 2000, 0, None) == saf.SAF_EUNSUPPORTED
+    finally:
+        saf.saf_destroy(c)
+
+
 def test_vertical_index_validation():
     c = _ctx()
     try:
