@@ -227,7 +227,7 @@ def attention(q, k, v, rows, keys) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# One layer: every head by its role, on a subset of query rows.
+# Block-wise correspondence (Sec. 4.3)
 def block_scores(F: np.ndarray, S: int, P: int, b: int, qblocks: Sequence[int]) -> np.ndarray:
     """Block-wise DINO similarity (Sec. 4.3, block-wise implementation).
 
@@ -290,6 +290,7 @@ def block_corr_index(F: np.ndarray, S: int, ns: int, P: int, b: int, K: int, row
 
 
 # ---------------------------------------------------------------------------
+# One layer: every head by its role, on a subset of query rows.
 def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int = MODE_TOTAL,
                rows: Optional[np.ndarray] = None, corr_rows: Optional[Dict[int, np.ndarray]] = None):
     """Key sets per head for the given query rows, from the oracle's own selection.
