@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--block", type=int, default=37,
                     help="also time the block-wise index with blocks of this many patches (0: skip)")
     ap.add_argument("--block-k", type=int, default=7, help="blocks kept per query block for --block")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="skip timing one offline-profiling pass (Sec. 4.2) over this sequence")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device to device twice (a known-size kernel for HBM counters)")
     ap.add_argument("--per-frame-k", type=int, default=4,
@@ -272,6 +274,37 @@ def main():
                  "step_ms": round(statistics.median(bt) + statistics.median(ba), 3)}
         bctx.close()
 
+    # one offline-profiling pass (Sec. 4.2) with this sequence as the single
+    # calibration sample: dense reference, baseline at sigma = 0.85 and seven
+    # candidates, per-head errors and the selection; not part of the step
+    prof = None
+    if not args.no_profile:
+        from head_wise_dynamic_amd import profiling
+        pctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+        cands = [(1, 1024, 0), (1, 2048, 0), (1, 4096, 0), (2, 128, 0), (2, 256, 0), (0, 0, 0), (3, 16, 0)]
+        smp = dict(q=q, k=k, v=v, dino=dino)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = profiling.profile_heads(pctx, [smp], cands, sigma=0.85)
+        torch.cuda.synchronize()
+        t_prof = time.perf_counter() - t0
+        full = pctx.dense_attention(q, k, v)
+        sums = pctx.head_nmse(full, o)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pctx.head_nmse(full, o, out=sums)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        nmse_ms = e0.elapsed_time(e1)
+        names = {0: "position", 1: "vertical", 2: "correspondence", 3: "scanning", 4: "dense"}
+        prof = {"sigma": 0.85, "configs": [f"{names[r]}:{b}" for r, b, _ in res["configs"]],
+                "choice_per_head": [int(c) for c in res["choice"]], "wall_ms": round(t_prof * 1e3, 1),
+                "error_kernel_ms": round(nmse_ms, 4),
+                "error_kernel_gbs": round(2 * g.H * g.N * g.d * 2 / (nmse_ms * 1e-3) / 1e9, 1)}
+        del full
+        pctx.close()
+
     # ---- roofline of the dominant kernel (largest single-kernel share)
     pairs = key_counts(w)
     shared_pairs = sum(p for kind, p in pairs if kind == "shared")
@@ -345,6 +378,7 @@ def main():
         "speedup_step_vs_dense": round(dense_ms / ms_per_step, 2) if dense_ms else None,
         "per_frame_index": per_frame,
         "block_index": block,
+        "offline_profiling": prof,
         "sparsity": round(1.0 - (shared_pairs + gather_pairs) / (g.H * g.N * g.N), 4),
         "roofline": roofline,
         "roofline_other": others,

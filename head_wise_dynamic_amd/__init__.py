@@ -61,6 +61,10 @@ _PROTOS = {
     "saf_workspace_size": (C.c_int, [_VP, _VP, C.POINTER(_SZ)]),
     "saf_build_corr_index": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _VP]),
     "saf_build_corr_index_blocks": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _I32, _VP]),
+    "saf_head_nmse": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _VP, _VP]),
+    "saf_head_pairs": (C.c_int, [_VP, C.POINTER(saf_head_plan_t), _I32, C.POINTER(C.c_int64)]),
+    "saf_profile_select": (C.c_int32, [C.POINTER(C.c_double), C.POINTER(C.c_double), _I32]),
+    "saf_baseline_stride": (C.c_int32, [C.c_double]),
     "saf_set_corr_index": (C.c_int, [_VP, _VP, _I32, _VP]),
     "saf_get_corr_index": (C.c_int, [_VP, _VP, C.POINTER(_I32), _VP]),
     "saf_build_vertical_index": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _VP, _VP, _SZ, _VP]),
@@ -115,6 +119,22 @@ def saf_build_corr_index(ctx, dino, dino_dtype, Df, row_stride, K, mode, stream)
 
 def saf_build_corr_index_blocks(ctx, dino, dino_dtype, Df, row_stride, block, K, mode, stream) -> int:
     return lib().saf_build_corr_index_blocks(ctx, dino, dino_dtype, Df, row_stride, block, K, mode, stream)
+
+
+def saf_head_nmse(ctx, o_full, o_sparse, layout, dev_out, stream) -> int:
+    return lib().saf_head_nmse(ctx, o_full, o_sparse, layout, dev_out, stream)
+
+
+def saf_head_pairs(ctx, head, corr_kc, pairs) -> int:
+    return lib().saf_head_pairs(ctx, head, corr_kc, pairs)
+
+
+def saf_profile_select(errors, costs, n) -> int:
+    return lib().saf_profile_select(errors, costs, n)
+
+
+def saf_baseline_stride(sigma) -> int:
+    return lib().saf_baseline_stride(sigma)
 
 
 def saf_set_corr_index(ctx, dev_idx, Kc, stream) -> int:
@@ -283,6 +303,23 @@ class Context:
         cnt = C.c_int32()
         self._check(saf_read_kernel_timing(self._ctx, max_entries, names, ms, cnt))
         return [(names[i].decode(), float(ms[i])) for i in range(min(cnt.value, max_entries))]
+
+    def head_nmse(self, o_full: torch.Tensor, o_sparse: torch.Tensor, out: torch.Tensor = None, stream=None):
+        """[H, 2] float64 (device): per head sum (o_full - o_sparse)^2 and sum o_full^2."""
+        lay, l2 = self.layout_of(o_full), self.layout_of(o_sparse)
+        if (lay.head_stride, lay.token_stride) != (l2.head_stride, l2.token_stride) or o_full.dtype != o_sparse.dtype:
+            raise ValueError("outputs must share a layout and dtype")
+        if out is None:
+            out = torch.empty((self.H, 2), dtype=torch.float64, device=o_full.device)
+        self._check(saf_head_nmse(self._ctx, C.c_void_p(o_full.data_ptr()), C.c_void_p(o_sparse.data_ptr()), lay,
+                                  C.c_void_p(out.data_ptr()), _stream(stream)))
+        return out
+
+    def head_pairs(self, role: int, budget: int = 0, anchor: int = 0, corr_kc: int = 0) -> int:
+        n = C.c_int64()
+        h = saf_head_plan_t(role, budget, anchor, 0)
+        self._check(saf_head_pairs(self._ctx, C.byref(h), corr_kc, C.byref(n)))
+        return n.value
 
     def dense_attention(self, q, k, v, o=None, stream=None) -> torch.Tensor:
         lay = self.layout_of(q)

@@ -26,6 +26,7 @@ struct saf_ctx {
     size_t corr_bytes = 0;
     void *corr_scratch = nullptr;
     size_t corr_scratch_bytes = 0;
+    double *nmse_part = nullptr;  // [H][kNmseBlocks][2] partial sums of the error kernel
     // side stream for the gather path (default priority), fork/join events
     hipStream_t side = nullptr;
     hipEvent_t ev_fork = nullptr, ev_vert = nullptr, ev_join = nullptr;
@@ -244,10 +245,11 @@ void saf_destroy(saf_ctx_t *c) {
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
     if (c->ev_join) (void)hipEventDestroy(c->ev_join);
     if (c->ev_vert) (void)hipEventDestroy(c->ev_vert);
-    if (c->corr_idx || c->corr_scratch) {
+    if (c->corr_idx || c->corr_scratch || c->nmse_part) {
         (void)hipDeviceSynchronize();
         if (c->corr_idx) (void)hipFree(c->corr_idx);
         if (c->corr_scratch) (void)hipFree(c->corr_scratch);
+        if (c->nmse_part) (void)hipFree(c->nmse_part);
     }
     delete c;
 }
@@ -836,3 +838,87 @@ saf_status_t saf_read_kernel_timing(saf_ctx_t *c, int32_t max, const char **name
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ offline profiling
+saf_status_t saf_head_nmse(saf_ctx_t *c, const void *o_full, const void *o_sparse, saf_layout_t lay,
+                           double *dev_out, void *stream) {
+    if (!c) return SAF_EINVAL;
+    if (!o_full || !o_sparse || !dev_out) return fail(c, SAF_EINVAL, "null pointer");
+    saf_status_t st = check_layout(c, lay);
+    if (st != SAF_OK) return st;
+    if (!aligned16(o_full) || !aligned16(o_sparse)) return fail(c, SAF_EINVAL, "outputs must be 16-byte aligned");
+    if (!c->nmse_part) {
+        const size_t bytes = sizeof(double) * 2 * (size_t)c->g.H * saf::kNmseBlocks;
+        hipError_t e = hipMalloc((void **)&c->nmse_part, bytes);
+        if (e != hipSuccess) {
+            c->nmse_part = nullptr;
+            (void)hipGetLastError();
+            return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for error partials failed", bytes);
+        }
+    }
+    hipError_t e;
+    {
+        Timed tm(c, as_stream(stream), "head_nmse");
+        e = saf::launch_head_nmse(c->g, o_full, o_sparse, lay.head_stride, lay.token_stride, c->nmse_part,
+                                  dev_out, as_stream(stream));
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "error kernels");
+    return SAF_OK;
+}
+
+saf_status_t saf_head_pairs(const saf_ctx_t *cc, const saf_head_plan_t *head, int32_t corr_kc, int64_t *pairs) {
+    saf_ctx_t *c = const_cast<saf_ctx_t *>(cc);
+    if (!c) return SAF_EINVAL;
+    if (!head || !pairs) return fail(c, SAF_EINVAL, "null pointer");
+    const saf::Geom &g = c->g;
+    const int64_t N = g.N, S = g.S, ns = g.ns, P = g.P, T = g.T;
+    switch (head->role) {
+    case SAF_DENSE:
+        *pairs = N * N;
+        return SAF_OK;
+    case SAF_POSITION: {
+        if (head->anchor_frame < 0 || head->anchor_frame >= g.S)
+            return fail(c, SAF_EINVAL, "anchor frame %d outside [0, S)", head->anchor_frame);
+        // the anchor frame's rows see specials + their own frame; the others also the anchor
+        *pairs = T * (ns * S + P) + (S - 1) * T * (ns * S + 2 * P);
+        return SAF_OK;
+    }
+    case SAF_SCANNING: {
+        const int64_t s = head->budget;
+        if (s < 1) return fail(c, SAF_EINVAL, "stride %lld < 1", (long long)s);
+        int64_t keys = (N + s - 1) / s;
+        for (int64_t f = 0; f < S; ++f)
+            for (int64_t t = 0; t < ns; ++t) keys += ((f * T + t) % s) ? 1 : 0;
+        *pairs = N * keys;
+        return SAF_OK;
+    }
+    case SAF_VERTICAL:
+        if (head->budget < 1) return fail(c, SAF_EINVAL, "K %d < 1", head->budget);
+        *pairs = N * std::min<int64_t>(head->budget, N);
+        return SAF_OK;
+    case SAF_CORRESPONDENCE: {
+        const int64_t kc = corr_kc > 0 ? corr_kc : c->corr_k;
+        if (kc < 1) return fail(c, SAF_ESTATE, "no index row length given and no cached index");
+        // patch rows gather kc keys; special rows attend to every key
+        *pairs = S * P * std::min<int64_t>(kc, (S - 1) * P) + ns * S * N;
+        return SAF_OK;
+    }
+    default:
+        return fail(c, SAF_EINVAL, "bad role %d", head->role);
+    }
+}
+
+int32_t saf_profile_select(const double *errors, const double *costs, int32_t n) {
+    if (!errors || !costs || n < 1) return -1;
+    int32_t best = 0;
+    for (int32_t i = 1; i < n; ++i)
+        if (costs[i] <= costs[0] && errors[i] < errors[best]) best = i;
+    return best;
+}
+
+int32_t saf_baseline_stride(double sigma) {
+    if (!(sigma >= 0.0 && sigma < 1.0)) return -1;
+    int32_t s = 1;
+    while ((1.0 / s) > (1.0 - sigma) + 1e-12) ++s;  // smallest stride keeping <= 1 - sigma of the keys
+    return s;
+}

@@ -142,4 +142,11 @@ int32_t corr_block_row_blocks(const Geom &g, int32_t block, int32_t K, int per_f
 size_t corr_block_scratch_bytes(const Geom &g, int32_t block, int32_t Df, int32_t K, int per_frame);
 hipError_t launch_corr_blocks(const CorrBlockBuild &B, hipStream_t stream);
 
+// Per-head error sums of Eq. 1 (fp64): out[2h] = sum (ref - test)^2,
+// out[2h + 1] = sum ref^2.  part: 2 * H * kNmseBlocks doubles.  d = 64,
+// rows 16-byte aligned.
+constexpr int kNmseBlocks = 256;
+hipError_t launch_head_nmse(const Geom &g, const void *ref, const void *test, int64_t head_stride,
+                            int64_t token_stride, double *part, double *out, hipStream_t stream);
+
 }  // namespace saf

@@ -221,6 +221,36 @@ saf_status_t saf_set_kernel_timing(saf_ctx_t *ctx, int32_t enable);
 saf_status_t saf_read_kernel_timing(saf_ctx_t *ctx, int32_t max, const char **names, float *ms,
                                     int32_t *count);
 
+/* ---- Offline head profiling (Sec. 4.2) ---------------------------------- */
+
+/* Error sums of Eq. 1 for every head: dev_out[2h] = sum over the head's N x d
+ * outputs of (o_full - o_sparse)^2 and dev_out[2h + 1] = sum of o_full^2,
+ * accumulated in fp64 in a fixed order (dev_out: 2H doubles, device memory).
+ * Both outputs have the context's dtype and the given layout.  The context
+ * keeps a small partial-sum buffer (allocated on first use).
+ * Errors: SAF_EINVAL (null pointer, bad layout), SAF_ENOMEM, SAF_EHIP. */
+saf_status_t saf_head_nmse(saf_ctx_t *ctx, const void *o_full, const void *o_sparse, saf_layout_t layout,
+                           double *dev_out, void *stream);
+
+/* Query-key pairs one head computes under *head at this geometry (its
+ * floating-point work, the cost of Eq. 2, is 4 head_dim per pair).  For a
+ * correspondence head corr_kc is the index row length (<= 0: the cached
+ * index's).  Host only.  Errors: SAF_EINVAL (bad role/budget/anchor),
+ * SAF_ESTATE (correspondence with no row length). */
+saf_status_t saf_head_pairs(const saf_ctx_t *ctx, const saf_head_plan_t *head, int32_t corr_kc,
+                            int64_t *pairs);
+
+/* Eq. 2 by progressive substitution: entry 0 is the baseline; walking
+ * entries 1 .. n-1 in order, an entry replaces the current choice when its
+ * error is strictly lower and its cost does not exceed the baseline's.
+ * Returns the chosen index, or -1 for n < 1 or null arrays.  Host only. */
+int32_t saf_profile_select(const double *errors, const double *costs, int32_t n);
+
+/* Stride of the uniform-sampling baseline with sparsity ratio sigma in
+ * [0, 1): the smallest stride keeping at most a fraction 1 - sigma of the
+ * keys.  Returns -1 for sigma outside [0, 1).  Host only. */
+int32_t saf_baseline_stride(double sigma);
+
 #ifdef __cplusplus
 }
 #endif

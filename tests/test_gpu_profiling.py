@@ -1,0 +1,116 @@
+"""Offline head profiling on the GPU (SAF3R Sec. 4.2) vs the CPU oracle.
+
+* the per-head error sums of Eq. 1 from the library's reduction kernel equal
+  the oracle's NMSE of the same outputs (relative 1e-9);
+* the whole search (baseline + candidates, errors averaged over samples,
+  Eq. 2 selection) on fp32 workloads: every error within 1e-4 relative (or
+  1e-7 absolute) of the oracle's, computed from the oracle's own outputs,
+  and the same chosen configuration for every head whose best two feasible
+  errors are not within that tolerance of each other.
+"""
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import profiling as oprof
+from workload import Geometry, make_geometry_inputs, ROLE_CORRESPONDENCE, ROLE_POSITION, ROLE_SCANNING, \
+    ROLE_VERTICAL
+
+from helpers import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _saf():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import head_wise_dynamic_amd as saf
+    saf.lib()
+    return saf
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("nhd", [False, True])
+def test_head_error_sums_match_oracle(dtype, nhd):
+    saf = _saf()
+    S, ns, P, H, d = 3, 5, 200, 16, 64
+    N = S * (ns + P)
+    ctx = saf.Context(S, ns, P, H, d, dtype)
+    g = torch.Generator().manual_seed(3)
+    a = torch.randn(H, N, d, generator=g)
+    b = a + 0.05 * torch.randn(H, N, d, generator=g)
+    b[3] = 0.0                                    # error = 1 for this head
+    b[5] = a[5]                                   # error = 0
+    ad, bd = a.to(dtype), b.to(dtype)
+    if nhd:
+        ad, bd = ad.transpose(0, 1).contiguous(), bd.transpose(0, 1).contiguous()
+    say(f"head error sums {dtype} nhd={nhd}")
+    sums = ctx.head_nmse(ad.cuda(), bd.cuda()).cpu().numpy()
+    a64 = ad.float().double().numpy()
+    b64 = bd.float().double().numpy()
+    if nhd:
+        a64, b64 = a64.transpose(1, 0, 2), b64.transpose(1, 0, 2)
+    for h in range(H):
+        want = oprof.nmse(a64[h], b64[h])
+        got = sums[h, 0] / sums[h, 1]
+        assert got == pytest.approx(want, rel=1e-9, abs=1e-15), h
+    assert sums[5, 0] == 0.0
+    assert sums[3, 0] / sums[3, 1] == pytest.approx(1.0, rel=1e-12)
+    ctx.close()
+
+
+def _planted():
+    from test_oracle_profiling import _planted_sample
+    return _planted_sample()
+
+
+def _compare(res_gpu, res_orc, H):
+    assert res_gpu["configs"] == [tuple(c) for c in res_orc["configs"]]
+    np.testing.assert_array_equal(res_gpu["costs"], res_orc["costs"])
+    eg, eo = res_gpu["errors"], res_orc["errors"]
+    tol = np.maximum(1e-4 * np.abs(eo), 1e-7)
+    assert np.all(np.abs(eg - eo) <= tol), np.max(np.abs(eg - eo) / np.maximum(np.abs(eo), 1e-12))
+    feas = res_orc["costs"] <= res_orc["costs"][0]
+    for h in range(H):
+        e = np.sort(eo[h][feas])
+        if e.size > 1 and e[1] - e[0] <= 2 * max(1e-4 * e[0], 1e-7):
+            continue            # near-tie between the two best: either choice is right
+        assert res_gpu["choice"][h] == res_orc["choice"][h], (h, eo[h])
+
+
+def test_profile_planted_heads_matches_oracle():
+    saf = _saf()
+    from head_wise_dynamic_amd import profiling
+    w = _planted()
+    g = w.geom
+    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.float32)
+    cands = [(ROLE_VERTICAL, 3, 0), (ROLE_CORRESPONDENCE, 1, 0), (ROLE_POSITION, 0, 0), (ROLE_SCANNING, 4, 0)]
+    say("profile planted heads")
+    smp = dict(q=to_dev(w.q), k=to_dev(w.k), v=to_dev(w.v), dino=to_dev(w.dino))
+    res = profiling.profile_heads(ctx, [smp], cands, sigma=0.5)
+    orc = oprof.profile([w], cands, sigma=0.5)
+    _compare(res, orc, g.H)
+    assert res["configs"][res["choice"][0]] == (ROLE_VERTICAL, 3, 0)
+    assert res["configs"][res["choice"][1]] == (ROLE_CORRESPONDENCE, 1, 0)
+    ctx.close()
+
+
+def test_profile_generated_workload_matches_oracle():
+    saf = _saf()
+    from head_wise_dynamic_amd import profiling
+    geom = Geometry(S=3, ns=5, P=40)
+    roles = [ROLE_POSITION] * 4 + [ROLE_VERTICAL] * 4 + [ROLE_CORRESPONDENCE] * 4 + [ROLE_SCANNING] * 4
+    ws = [make_geometry_inputs(geom, "f32", roles, [0, 0, 0, 0, 24, 24, 24, 24, 8, 8, 8, 8, 4, 4, 4, 4],
+                               M=120, Df=32, seed=s) for s in (11, 12)]
+    cands = [(ROLE_VERTICAL, 24, 0), (ROLE_VERTICAL, 48, 0), (ROLE_CORRESPONDENCE, 8, 0),
+             (ROLE_CORRESPONDENCE, 16, 0), (ROLE_POSITION, 0, 0), (ROLE_SCANNING, 8, 0)]
+    ctx = saf.Context(geom.S, geom.ns, geom.P, geom.H, geom.d, torch.float32)
+    say("profile generated workload, 2 samples")
+    smps = [dict(q=to_dev(w.q), k=to_dev(w.k), v=to_dev(w.v), dino=to_dev(w.dino)) for w in ws]
+    res = profiling.profile_heads(ctx, smps, cands, sigma=0.75)
+    orc = oprof.profile(ws, cands, sigma=0.75)
+    _compare(res, orc, geom.H)
+    ctx.close()
