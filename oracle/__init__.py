@@ -17,7 +17,10 @@ assembles per-head key sets the way the pages describe them:
   no DINO feature, attend to every key;
 * scanning heads  -- fixed stride of the token index plus all special tokens
   (Sec. 4.1 "Uniform Sampling Kernel");
-* dense           -- every key (full global attention).
+* dense           -- every key (full global attention);
+* corr + stride   -- a patch query's correspondence keys united with the
+  scanning set of a given stride (the combination the paper proposes for
+  scenes where DINO features miss regions); special queries attend to all.
 
 Parity pins: see tests/test_oracle_pins.py.  Every function has at least one
 pin independent of its own code (brute force, closed form, printed values).
@@ -36,6 +39,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 ROLE_POSITION, ROLE_VERTICAL, ROLE_CORRESPONDENCE, ROLE_SCANNING, ROLE_DENSE = 0, 1, 2, 3, 4
+# correspondence top-K united with the uniform stride set (Sec. 5, the second
+# direction named for the DINO Top-K kernel): budget = the stride
+ROLE_CORR_STRIDE = 5
 MODE_TOTAL, MODE_PER_FRAME = 0, 1
 
 
@@ -303,7 +309,7 @@ def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int =
     out = {}
     vert = {}
     corr = dict(corr_rows or {})
-    if any(p[0] == ROLE_CORRESPONDENCE for p in plan):
+    if any(p[0] in (ROLE_CORRESPONDENCE, ROLE_CORR_STRIDE) for p in plan):
         need = [int((i // T) * P + (i % T) - ns) for i in rows[~is_special]]
         missing = sorted(set(need) - set(corr))
         if missing:
@@ -323,6 +329,15 @@ def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int =
             vert[h] = dict(ids=ids, scores=r, kth=kth, next=nxt)
             sets = [ids]
             row_set = np.zeros(rows.size, dtype=np.int64)
+        elif role == ROLE_CORR_STRIDE:
+            scan = scan_set(S, ns, P, budget)
+            sets = [np.arange(N, dtype=np.int64)]
+            row_set = np.zeros(rows.size, dtype=np.int64)
+            for r_i, i in enumerate(rows):
+                if not is_special[r_i]:
+                    u = int((i // T) * P + (i % T) - ns)
+                    row_set[r_i] = len(sets)
+                    sets.append(np.union1d(scan, corr[u]))
         elif role == ROLE_CORRESPONDENCE:
             sets = [np.arange(N, dtype=np.int64)]
             row_set = np.zeros(rows.size, dtype=np.int64)

@@ -396,3 +396,35 @@ def test_block_index_shares_sets_within_a_block_and_clamps():
     assert pf.shape == (geom.Np, 4 * 16)                       # clamps to every other patch
     with pytest.raises(ValueError):
         oracle.block_corr_index(w.dino, 5, 2, 16, 3, 3, rows)
+
+
+# ---- correspondence top-K united with the stride set
+def test_corr_stride_sets_are_the_union():
+    geom = Geometry(S=3, ns=2, P=20)
+    w = make_geometry_inputs(geom, "f32", [ROLE_CORRESPONDENCE] * 16, [6] * 16, M=50, Df=16, seed=12)
+    idx, _, _ = oracle.corr_index(w.dino, 3, 2, 20, 6, np.arange(geom.Np))
+    for s in (1, 4, 7, 10 ** 6):
+        plan = [(oracle.ROLE_CORR_STRIDE, s, 0, 0)] * 16
+        sets, _, _ = oracle.layer_sets(geom, plan, w.q, w.k, w.v, w.dino, corr_K=6)
+        row_set, ss = sets[0]
+        scan = {j for j in range(geom.N) if j % s == 0} | {f * geom.T + t for f in range(3) for t in range(2)}
+        for i in range(geom.N):
+            got = ss[row_set[i]]
+            if i % geom.T < 2:
+                assert len(got) == geom.N                      # special queries: every key
+                continue
+            u = (i // geom.T) * 20 + i % geom.T - 2
+            want = sorted(scan | set(idx[u].tolist()))
+            assert got.tolist() == want
+            assert len(got) == len(scan) + len(set(idx[u].tolist()) - scan)
+
+
+def test_corr_stride_with_stride_one_is_dense():
+    geom = Geometry(S=2, ns=1, P=12)
+    w = make_geometry_inputs(geom, "f32", [ROLE_CORRESPONDENCE] * 16, [4] * 16, M=30, Df=16, seed=13)
+    u_plan = [(oracle.ROLE_CORR_STRIDE, 1, 0, 0)] * 16
+    d_plan = [(oracle.ROLE_DENSE, 0, 0, 0)] * 16
+    a, _, _ = oracle.layer(geom, u_plan, w.q, w.k, w.v, w.dino, corr_K=4)
+    b, _, _ = oracle.layer(geom, d_plan, w.q, w.k, w.v)
+    for h in range(16):
+        np.testing.assert_allclose(a[h], b[h], rtol=0, atol=1e-14)
