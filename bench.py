@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--block", type=int, default=37,
                     help="also time the block-wise index with blocks of this many patches (0: skip)")
     ap.add_argument("--block-k", type=int, default=7, help="blocks kept per query block for --block")
+    ap.add_argument("--corr-stride", type=int, default=64,
+                    help="also time the layer with its correspondence heads united with this stride (0: skip)")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip timing one offline-profiling pass (Sec. 4.2) over this sequence")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -249,6 +251,23 @@ def main():
                      "tflops": round(2.0 * g.Np * g.Np * w.Df / (pf_ms * 1e-3) / 1e12, 2)}
         pctx.close()
 
+    # the layer with its correspondence heads as correspondence top-K united
+    # with a stride (cached total index); not part of the step
+    corr_stride = None
+    if args.corr_stride > 0:
+        csplan = [(5, args.corr_stride, a, f) if r == 2 else (r, b, a, f) for (r, b, a, f) in w.plan]
+        ctx.sparse_attention(csplan, q, k, v, o=o)
+        torch.cuda.synchronize()
+        ct = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ctx.sparse_attention(csplan, q, k, v, o=o)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ct.append(e0.elapsed_time(e1))
+        corr_stride = {"stride": args.corr_stride, "attn_only_ms": round(statistics.median(ct), 4)}
+
     # block-wise index (blocks of --block patches, --block-k blocks per query
     # block) and the layer on it, in a context of its own; not part of the step
     block = None
@@ -378,6 +397,7 @@ def main():
         "speedup_step_vs_dense": round(dense_ms / ms_per_step, 2) if dense_ms else None,
         "per_frame_index": per_frame,
         "block_index": block,
+        "corr_stride_layer": corr_stride,
         "offline_profiling": prof,
         "sparsity": round(1.0 - (shared_pairs + gather_pairs) / (g.H * g.N * g.N), 4),
         "roofline": roofline,

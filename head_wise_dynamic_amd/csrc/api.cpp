@@ -139,15 +139,25 @@ saf_status_t check_tensors(saf_ctx_t *c, const void *q, const void *k, const voi
 }
 
 struct PlanInfo {
-    int nvert = 0, ncorr = 0;
+    int nvert = 0, ncorr = 0, nunion = 0;
     int64_t vert_ws = 0;      // bytes for in-call vertical index builds
     int64_t split_ws = 0;     // bytes for dense-row split partials
+    int64_t union_ws = 0;     // bytes for the records of correspondence + stride heads
     int corr_splits = 1;
 };
 
 int corr_special_splits(const saf::Geom &g) {
     const int64_t s = (g.N + kSplitKeys - 1) / kSplitKeys;
     return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
+}
+
+// records of one correspondence + stride head: the stride set's (one per
+// token row of the matrix-core tiles) and the gathered keys' (one per patch)
+int64_t union_tok_rec_bytes(const saf::Geom &g) {
+    return (int64_t)align256(sizeof(float) * saf::kRecStride * (size_t)((g.N + QT - 1) / QT * QT));
+}
+int64_t union_rec_bytes(const saf::Geom &g) {
+    return union_tok_rec_bytes(g) + (int64_t)align256(sizeof(float) * saf::kRecStride * (size_t)g.Np);
 }
 
 int64_t split_part_bytes(const saf::Geom &g, int nsplit) {
@@ -176,6 +186,12 @@ saf_status_t check_plan(saf_ctx_t *c, const saf_head_plan_t *plan, PlanInfo *pi)
             if (p.budget < 0) return fail(c, SAF_EINVAL, "head %d: negative budget", h);
             ++pi->ncorr;
             break;
+        case SAF_CORR_STRIDE:
+            if (g.S < 2) return fail(c, SAF_EINVAL, "head %d: correspondence needs S >= 2", h);
+            if (p.budget < 1) return fail(c, SAF_EINVAL, "head %d: stride %d < 1", h, p.budget);
+            ++pi->ncorr;
+            ++pi->nunion;
+            break;
         case SAF_SCANNING:
             if (p.budget < 1) return fail(c, SAF_EINVAL, "head %d: scanning stride %d < 1", h, p.budget);
             if (g.ns == 0 && p.budget > g.N) {
@@ -193,6 +209,7 @@ saf_status_t check_plan(saf_ctx_t *c, const saf_head_plan_t *plan, PlanInfo *pi)
     if (pi->ncorr && g.dtype == saf::BF16) {
         pi->corr_splits = corr_special_splits(g);
         if (pi->corr_splits > 1) pi->split_ws = (int64_t)pi->ncorr * split_part_bytes(g, pi->corr_splits);
+        pi->union_ws = (int64_t)pi->nunion * union_rec_bytes(g);
     }
     return SAF_OK;
 }
@@ -265,7 +282,7 @@ saf_status_t saf_workspace_size(const saf_ctx_t *cc, const saf_head_plan_t *plan
     PlanInfo pi;
     const saf_status_t st = check_plan(c, plan, &pi);
     if (st != SAF_OK) return st;
-    *bytes = (size_t)(pi.vert_ws + pi.split_ws) + 256;
+    *bytes = (size_t)(pi.vert_ws + pi.split_ws + pi.union_ws) + 256;
     return SAF_OK;
 }
 
@@ -490,7 +507,7 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
                 return fail(c, SAF_ESTATE, "head %d budget %d differs from the index's K %d (row length %d)", h,
                             plan[h].budget, c->corr_build_k, c->corr_k);
     }
-    size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws);
+    size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws);
     if (need > 0) need += 256;  // room to align the start to 256 bytes
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(c, SAF_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -564,6 +581,16 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         return SAF_OK;
     }
 
+    // records of the correspondence + stride heads (bf16): the stride set's
+    // from the matrix-core kernel, the gathered keys' from the row kernel
+    std::vector<float *> union_tok(g.H, nullptr), union_patch(g.H, nullptr);
+    for (int h = 0; h < g.H; ++h)
+        if (plan[h].role == SAF_CORR_STRIDE) {
+            union_tok[h] = (float *)wp;
+            union_patch[h] = (float *)(wp + union_tok_rec_bytes(g));
+            wp += union_rec_bytes(g);
+        }
+
     // 2. bf16.  A side stream (default priority) runs the HBM-bound work --
     // the vertical probe + top-K, then the correspondence heads' gathered
     // rows -- while the caller's stream runs the matrix-core kernel for the
@@ -617,7 +644,7 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         L.patch_rows_only = 1;
         L.nwork = 0;
         for (int h = 0; h < g.H && e == hipSuccess; ++h) {
-            if (plan[h].role != SAF_CORRESPONDENCE) continue;
+            if (plan[h].role != SAF_CORRESPONDENCE && plan[h].role != SAF_CORR_STRIDE) continue;
             if (L.nwork == saf::kMaxWork) {
                 Timed tm(c, ss, "gather_attention");
                 e = saf::launch_valu_attention(L, g.Np, ss);
@@ -626,8 +653,13 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
             saf::HeadWork &w = L.work[L.nwork++];
             w = saf::HeadWork{};
             w.head = h;
-            w.role = SAF_CORRESPONDENCE;
+            w.role = plan[h].role;
             w.nsplit = 1;
+            if (plan[h].role == SAF_CORR_STRIDE) {
+                w.budget = plan[h].budget;
+                w.rec_out = 1;
+                w.part = union_patch[h];
+            }
         }
         if (e == hipSuccess && L.nwork) {
             Timed tm(c, ss, "gather_attention");
@@ -654,6 +686,19 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         w.anchor = plan[h].anchor_frame;
         w.nsplit = 1;
         Item it{};
+        if (plan[h].role == SAF_CORR_STRIDE) {
+            // the stride set for every row, as records merged with the gathered keys'
+            saf::HeadWork sw = w;
+            sw.role = saf::SCANNING;
+            sw.rows = saf::ROWS_ALL;
+            sw.rec_out = 1;
+            sw.part = union_tok[h];
+            Item si{};
+            si.w = sw;
+            si.tiles = all_tiles;
+            si.cost = (double)((g.N + sw.budget - 1) / sw.budget) + (double)g.ns * g.S;
+            items.push_back(si);
+        }
         switch (plan[h].role) {
         case SAF_POSITION:
             w.rows = saf::ROWS_FRAME;
@@ -679,6 +724,7 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
             it.cost = (double)g.N;
             break;
         case SAF_CORRESPONDENCE:
+        case SAF_CORR_STRIDE:
             if (g.ns == 0) continue;
             w.role = saf::DENSE;  // special-token rows attend to every key
             w.rows = saf::ROWS_SPECIALS;
@@ -734,6 +780,36 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
                 e = saf::launch_split_combine(M, s);
             }
             if (e != hipSuccess) return hip_fail(c, e, "split combine kernel");
+        }
+    }
+    if (pi.nunion) {
+        // both records exist once the side stream's gather is done
+        if (forked) {
+            e = hipEventRecord(c->ev_join, ss);
+            if (e == hipSuccess) e = hipStreamWaitEvent(s, c->ev_join, 0);
+            if (e != hipSuccess) return hip_fail(c, e, "joining the gather stream");
+        }
+        saf::UnionMerge U{};
+        U.g = g;
+        U.o = o;
+        U.head_stride = lay.head_stride;
+        U.token_stride = lay.token_stride;
+        for (int h = 0; h < g.H; ++h) {
+            if (plan[h].role != SAF_CORR_STRIDE) continue;
+            U.head[U.nhead] = h;
+            U.rec_tok[U.nhead] = union_tok[h];
+            U.rec_patch[U.nhead] = union_patch[h];
+            if (++U.nhead == saf::kMaxWork || h == g.H - 1) {
+                Timed tm(c, s, "union_merge");
+                e = saf::launch_union_merge(U, s);
+                if (e != hipSuccess) return hip_fail(c, e, "union merge kernel");
+                U.nhead = 0;
+            }
+        }
+        if (U.nhead) {
+            Timed tm(c, s, "union_merge");
+            e = saf::launch_union_merge(U, s);
+            if (e != hipSuccess) return hip_fail(c, e, "union merge kernel");
         }
     }
     return SAF_OK;

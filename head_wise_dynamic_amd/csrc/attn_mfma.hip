@@ -27,7 +27,7 @@ constexpr int QT = kQueryTile;
 constexpr int KT = 64;
 constexpr int KROW = 72;   // K tile row in LDS: 64 bf16 + 8 pad
 constexpr int VROW = 72;   // V^T tile row in LDS: 64 keys + 8 pad
-constexpr int PSTRIDE = 66;  // split partial record: m, l, o[64]
+constexpr int PSTRIDE = kRecStride;  // split partial record: m, l, o[64]
 
 __device__ __forceinline__ int swap_bits23(int m) {
     return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
         if (!qvalid[qb]) continue;
         const int qr = wave * 64 + 32 * qb + n;
-        if (w.nsplit == 1) {
+        if (w.nsplit == 1 && !w.rec_out) {
             const float inv = 1.f / l_tot;
             uint16_t *O = (uint16_t *)L.o + hoff + qtok[qb] * ts;
 #pragma unroll

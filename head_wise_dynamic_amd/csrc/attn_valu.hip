@@ -48,25 +48,39 @@ template <> struct Lanes<float> {
 
 constexpr int NP = 8;  // row loads per chunk and lane
 
+// Running softmax state of one query row: m is wave-uniform; l and o are
+// per lane group (each group of LPR lanes takes different keys) until finish.
+template <typename T> struct RowAcc {
+    float qv[Lanes<T>::EPL];
+    float m, l, o[Lanes<T>::EPL];
+};
+
 template <typename T>
-__device__ void attend_row(const ValuLaunch &L, const HeadWork &w, int64_t qtok, int32_t qframe,
-                           const int32_t *idx_row, int64_t count, int lane) {
+__device__ void row_init(const ValuLaunch &L, const HeadWork &w, int64_t qtok, int lane, RowAcc<T> &a) {
+    using E = Lanes<T>;
+    const int sub = lane % E::LPR;
+    const T *Q = (const T *)L.q + (int64_t)w.head * L.head_stride;
+    E::load(Q + qtok * L.token_stride + sub * E::EPL, a.qv);
+    a.m = -INFINITY;
+    a.l = 0.f;
+#pragma unroll
+    for (int e = 0; e < E::EPL; ++e) a.o[e] = 0.f;
+}
+
+// Continue the row's online softmax over `count` keys: idx_row[m] when given,
+// else the m-th key of w's key set.  skip > 0 drops listed keys on that
+// stride (they are counted by another key list of the same row).
+template <typename T>
+__device__ void row_accumulate(const ValuLaunch &L, const HeadWork &w, int32_t qframe, const int32_t *idx_row,
+                               int64_t count, int64_t skip, int lane, RowAcc<T> &a) {
     using E = Lanes<T>;
     constexpr int EPL = E::EPL, LPR = E::LPR, RPP = E::RPP, CH = NP * RPP;
     const Geom &g = L.g;
     const int sub = lane % LPR, grp = lane / LPR;
     const int64_t hoff = (int64_t)w.head * L.head_stride, ts = L.token_stride;
-    const T *Q = (const T *)L.q + hoff;
     const T *K = (const T *)L.k + hoff;
     const T *V = (const T *)L.v + hoff;
-
-    float qv[EPL];
-    E::load(Q + qtok * ts + sub * EPL, qv);
     const float sc = kLog2e * 0.125f;
-
-    float m_run = -INFINITY, l_run = 0.f, o[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
     for (int64_t c0 = 0; c0 < count; c0 += CH) {
         int64_t tok[NP];
@@ -76,6 +90,7 @@ __device__ void attend_row(const ValuLaunch &L, const HeadWork &w, int64_t qtok,
             const int64_t m = c0 + p * RPP + grp;
             tok[p] = -1;
             if (m < count) tok[p] = idx_row ? (int64_t)idx_row[m] : key_token(w, g, m, qframe);
+            if (skip > 0 && tok[p] >= 0 && tok[p] % skip == 0) tok[p] = -1;
         }
         float kx[NP][EPL];
 #pragma unroll
@@ -92,7 +107,7 @@ __device__ void attend_row(const ValuLaunch &L, const HeadWork &w, int64_t qtok,
         for (int p = 0; p < NP; ++p) {
             float dot = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) dot = fmaf(qv[e], kx[p][e], dot);
+            for (int e = 0; e < EPL; ++e) dot = fmaf(a.qv[e], kx[p][e], dot);
 #pragma unroll
             for (int x = 1; x < LPR; x <<= 1) dot += __shfl_xor(dot, x);
             s[p] = tok[p] >= 0 ? dot * sc : -INFINITY;
@@ -101,39 +116,63 @@ __device__ void attend_row(const ValuLaunch &L, const HeadWork &w, int64_t qtok,
 #pragma unroll
         for (int x = LPR; x < 64; x <<= 1) cm = fmaxf(cm, __shfl_xor(cm, x));
         if (cm == -INFINITY) continue;  // wave-uniform: every slot masked
-        const float m_new = fmaxf(m_run, cm);
-        const float alpha = fast_exp2(m_run - m_new);
+        const float m_new = fmaxf(a.m, cm);
+        const float alpha = fast_exp2(a.m - m_new);
         float lsum = 0.f;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             s[p] = fast_exp2(s[p] - m_new);
             lsum += s[p];
         }
-        l_run = l_run * alpha + lsum;
-        m_run = m_new;
+        a.l = a.l * alpha + lsum;
+        a.m = m_new;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+        for (int e = 0; e < EPL; ++e) a.o[e] *= alpha;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             if (tok[p] >= 0) {
                 float vx[EPL];
                 E::load(V + tok[p] * ts + sub * EPL, vx);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) o[e] = fmaf(s[p], vx[e], o[e]);
+                for (int e = 0; e < EPL; ++e) a.o[e] = fmaf(s[p], vx[e], a.o[e]);
             }
         }
     }
+}
+
+template <typename T> __device__ void row_reduce(int lane, RowAcc<T> &a) {
 #pragma unroll
-    for (int x = LPR; x < 64; x <<= 1) {
-        l_run += __shfl_xor(l_run, x);
+    for (int x = Lanes<T>::LPR; x < 64; x <<= 1) {
+        a.l += __shfl_xor(a.l, x);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], x);
+        for (int e = 0; e < Lanes<T>::EPL; ++e) a.o[e] += __shfl_xor(a.o[e], x);
     }
-    if (grp == 0) {
-        const float inv = 1.f / l_run;
+}
+
+template <typename T>
+__device__ void row_store(const ValuLaunch &L, const HeadWork &w, int64_t qtok, int lane, RowAcc<T> &a) {
+    using E = Lanes<T>;
+    row_reduce<T>(lane, a);
+    if (lane / E::LPR == 0) {
+        const float inv = 1.f / a.l;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] *= inv;
-        E::store((T *)L.o + hoff + qtok * ts + sub * EPL, o);
+        for (int e = 0; e < E::EPL; ++e) a.o[e] *= inv;
+        E::store((T *)L.o + (int64_t)w.head * L.head_stride + qtok * L.token_stride + (lane % E::LPR) * E::EPL,
+                 a.o);
+    }
+}
+
+// unnormalised record (m, l, o[64]) for a later merge
+template <typename T> __device__ void row_record(float *rec, int lane, RowAcc<T> &a) {
+    using E = Lanes<T>;
+    row_reduce<T>(lane, a);
+    if (lane / E::LPR == 0) {
+#pragma unroll
+        for (int e = 0; e < E::EPL; ++e) rec[2 + (lane % E::LPR) * E::EPL + e] = a.o[e];
+        if (lane == 0) {
+            rec[0] = a.m;
+            rec[1] = a.l;
+        }
     }
 }
 
@@ -155,23 +194,70 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(const ValuLaunch L, int6
     const int32_t qframe = (int32_t)(tok / g.T);
     for (int i = 0; i < L.nwork; ++i) {
         const HeadWork w = L.work[i];
-        const int32_t *idx_row = nullptr;
-        int64_t count;
-        if (w.role == CORRESPONDENCE) {
-            if (u >= 0) {
+        RowAcc<T> acc;
+        row_init<T>(L, w, tok, lane, acc);
+        // up to two key lists continue one online softmax (a single call
+        // site keeps the register budget of the plain roles)
+        HeadWork kw = w;
+        const int32_t *idx_row = nullptr, *second = nullptr;
+        int64_t count = 0, skip = 0;
+        bool record = false;
+        if (w.role == CORRESPONDENCE || w.role == CORR_STRIDE) {
+            if (u < 0) {  // special-token query: every key
+                kw.role = DENSE;
+                count = g.N;
+            } else if (w.role == CORRESPONDENCE) {
                 idx_row = L.corr_idx + u * L.corr_k;
                 count = L.corr_k;
-            } else {
-                HeadWork d = w;
-                d.role = DENSE;
-                attend_row<T>(L, d, tok, qframe, nullptr, g.N, lane);
-                continue;
+            } else if (w.rec_out) {
+                // gathered keys off the stride; the stride set comes from the matrix cores
+                idx_row = L.corr_idx + u * L.corr_k;
+                count = L.corr_k;
+                skip = w.budget;
+                record = true;
+            } else {  // stride set, then the gathered keys off the stride
+                kw.role = SCANNING;
+                count = key_count(kw, g, qframe);
+                second = L.corr_idx + u * L.corr_k;
             }
         } else {
             count = key_count(w, g, qframe);
         }
-        attend_row<T>(L, w, tok, qframe, idx_row, count, lane);
+        for (int ph = 0; ph < 2; ++ph) {
+            row_accumulate<T>(L, kw, qframe, idx_row, count, skip, lane, acc);
+            if (!second) break;
+            kw = w;
+            idx_row = second;
+            count = L.corr_k;
+            skip = w.budget;
+            second = nullptr;
+        }
+        if (record)
+            row_record<T>(w.part + u * kRecStride, lane, acc);
+        else
+            row_store<T>(L, w, tok, lane, acc);
     }
+}
+
+// one wave per (patch row, head), lane = channel
+__global__ __launch_bounds__(256) void union_merge_kernel(const UnionMerge U) {
+    const Geom &g = U.g;
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw >= g.Np * U.nhead) return;
+    const int hi = (int)(gw / g.Np);
+    const int64_t u = gw % g.Np;
+    const int64_t tok = (u / g.P) * g.T + g.ns + (u % g.P);
+    const float *ra = U.rec_tok[hi] + tok * kRecStride;
+    const float *rb = U.rec_patch[hi] + u * kRecStride;
+    const float ma = ra[0], mb = rb[0];
+    const float M = fmaxf(ma, mb);
+    const float fa = ma == -INFINITY ? 0.f : fast_exp2(ma - M);
+    const float fb = mb == -INFINITY ? 0.f : fast_exp2(mb - M);
+    const float l = ra[1] * fa + rb[1] * fb;
+    const float o = ra[2 + lane] * fa + rb[2 + lane] * fb;
+    uint16_t *O = (uint16_t *)U.o + (int64_t)U.head[hi] * U.head_stride + tok * U.token_stride;
+    O[lane] = (uint16_t)f32_to_bf16_bits(o / l);
 }
 
 }  // namespace
@@ -183,6 +269,13 @@ hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t
         hipLaunchKernelGGL(valu_attn_kernel<uint16_t>, grid, dim3(256), 0, stream, L, nrows);
     else
         hipLaunchKernelGGL(valu_attn_kernel<float>, grid, dim3(256), 0, stream, L, nrows);
+    return hipGetLastError();
+}
+
+hipError_t launch_union_merge(const UnionMerge &U, hipStream_t stream) {
+    if (U.nhead <= 0) return hipSuccess;
+    const int64_t waves = U.g.Np * U.nhead;
+    hipLaunchKernelGGL(union_merge_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, U);
     return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 
 namespace saf {
 
-enum Role : int32_t { POSITION = 0, VERTICAL = 1, CORRESPONDENCE = 2, SCANNING = 3, DENSE = 4 };
+enum Role : int32_t { POSITION = 0, VERTICAL = 1, CORRESPONDENCE = 2, SCANNING = 3, DENSE = 4, CORR_STRIDE = 5 };
 enum Dtype : int32_t { F32 = 0, BF16 = 1 };
 
 // Geometry with derived sizes.  Token j = f * T + t; special iff t < ns.
@@ -41,8 +41,13 @@ struct HeadWork {
     int32_t nsplit;     // key splits per query tile (1 = no split)
     int32_t block0;     // first work-group of this head in the launch
     const int32_t *list;// VERTICAL key list (device, ascending)
-    float *part;        // split partials (nsplit > 1): [tiles*QT rows][nsplit] x (m, l, o[64])
+    float *part;        // split partials (nsplit > 1 or rec_out): [tiles*QT rows][nsplit] x (m, l, o[64])
+    int32_t rec_out;    // write the (m, l, o) record even with nsplit == 1 (merged later)
 };
+
+// Softmax partial record of one query row: running max m (log2 units of the
+// scaled logit), l = sum 2^(s - m), o[64] = sum 2^(s - m) v.
+constexpr int kRecStride = 66;
 
 constexpr int kMaxWork = 24;
 constexpr int kQueryTile = 256;  // query rows per work-group of the matrix-core kernel
@@ -77,6 +82,19 @@ struct ValuLaunch {
 hipError_t launch_mfma_attention(const MfmaLaunch &L, hipStream_t stream);
 hipError_t launch_split_combine(const MfmaLaunch &L, hipStream_t stream);
 hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t stream);
+// CORR_STRIDE heads (bf16): merge, for every patch row, the stride set's
+// record from the matrix-core kernel (rows = tokens) with the gathered
+// keys' record (rows = patches) and write O.
+struct UnionMerge {
+    Geom g;
+    void *o;
+    int64_t head_stride, token_stride;
+    int32_t nhead;
+    int32_t head[kMaxWork];
+    const float *rec_tok[kMaxWork];    // [N rows (tiles*QT)] x kRecStride
+    const float *rec_patch[kMaxWork];  // [Np] x kRecStride
+};
+hipError_t launch_union_merge(const UnionMerge &U, hipStream_t stream);
 
 // Vertical probe: qbar (fp32) of one head, probe scores, exact top-K.
 //   ws layout per head: partial sums [kProbeBlocks][64] f32, qbar [64] f32,

@@ -26,6 +26,11 @@
  *                      index (phase 0) plus every special token (Sec. 4.1
  *                      "Uniform Sampling Kernel").
  *   SAF_DENSE          every key (full global attention).
+ *   SAF_CORR_STRIDE    a patch query's cached correspondence keys united with
+ *                      the SAF_SCANNING set of stride `budget` (the union the
+ *                      paper names, in its analysis of the DINO Top-K kernel,
+ *                      to cover regions DINO features miss); special queries
+ *                      attend to every key.
  *
  * Token layout: frame f holds T = ns + P tokens, the ns special tokens
  * (camera, registers) first, then P patch tokens; token j = f * T + t.  Patch
@@ -76,7 +81,8 @@ typedef enum {
     SAF_VERTICAL = 1,
     SAF_CORRESPONDENCE = 2,
     SAF_SCANNING = 3,
-    SAF_DENSE = 4
+    SAF_DENSE = 4,
+    SAF_CORR_STRIDE = 5
 } saf_role_t;
 
 /* Correspondence top-K per query: over all other frames together, or K per
@@ -101,7 +107,8 @@ typedef struct {
     int32_t role;          /* saf_role_t */
     int32_t budget;        /* VERTICAL: K >= 1 (clamped to N); SCANNING: stride >= 1;
                               CORRESPONDENCE: 0, the cached index's row length Kc
-                              or the K it was built with; others: 0 */
+                              or the K it was built with; CORR_STRIDE: stride >= 1;
+                              others: 0 */
     int32_t anchor_frame;  /* POSITION: anchor frame in [0, S); others ignored */
     int32_t flags;         /* must be 0 */
 } saf_head_plan_t;
