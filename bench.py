@@ -82,8 +82,10 @@ def parse():
                     help="first copy 1 GiB device to device twice (a known-size kernel for HBM counters)")
     ap.add_argument("--per-frame-k", type=int, default=4,
                     help="also time the per-frame index build with this K per frame (0: skip)")
-    ap.add_argument("--cpu-row-stride", type=int, default=37)
-    ap.add_argument("--cpu-corr-rows", type=int, default=64)
+    ap.add_argument("--cpu-row-stride", type=int, default=5,
+                    help="CPU baseline: attention on every n-th query row of every head")
+    ap.add_argument("--cpu-corr-rows", type=int, default=512,
+                    help="CPU baseline: correspondence index rows timed")
     return ap.parse_args()
 
 
@@ -181,11 +183,14 @@ def main():
             per["launches:" + name] = per.get("launches:" + name, 0) + 1
         for name, ms in per.items():
             groups.setdefault(name, []).append(ms)
-    launches = {}
+    launches = {}   # per layer: summed time of each launch group
     for _ in range(args.reps):
         ctx.sparse_attention(w.plan, q, k, v, o=o)
         torch.cuda.synchronize()
+        per = {}
         for name, ms in ctx.read_kernel_timing():
+            per[name] = per.get(name, 0.0) + ms
+        for name, ms in per.items():
             launches.setdefault(name, []).append(ms)
     ctx.set_kernel_timing(False)
     launch_counts = {n.split(":", 1)[1]: int(v[0]) for n, v in groups.items() if n.startswith("launches:")}
