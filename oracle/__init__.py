@@ -232,6 +232,50 @@ def attention(q, k, v, rows, keys) -> np.ndarray:
     return attention_sets(q, k, v, rows, np.zeros(rows.size, dtype=np.int64), [keys])
 
 
+def _as_f64(a: np.ndarray) -> np.ndarray:
+    """float32 values, or bfloat16 bits (uint16) decoded exactly, as float64."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    raise TypeError("oracle inputs are float32 or bfloat16 bits (uint16)")
+
+
+def qk_index(q: np.ndarray, k: np.ndarray, S: int, ns: int, P: int, K: int, rows: Sequence[int],
+             mode: int = MODE_TOTAL):
+    """Correspondence key rows taken from one head's own attention logits
+    instead of DINO features (SAF3R Sec. 5, first direction named for the
+    DINO Top-K kernel): for patch u (token i) the patch tokens j of other
+    frames ranked by (q_i . k_j desc, token asc) -- the 1/sqrt(d) scale
+    does not change the order -- first min(K, (S-1)P) of them (total) or
+    min(K, P) of every other frame (per frame).  q, k: one head's [N, d].
+    Returns (idx [nrows, kc] ascending, kth score per row)."""
+    T = ns + P
+    Q, Kf = _as_f64(q), _as_f64(k)
+    patch_tok = np.array([(v // P) * T + ns + v % P for v in range(S * P)], dtype=np.int64)
+    rows = _i64(rows)
+    out, kth = [], []
+    for u in rows:
+        fu = u // P
+        s = Kf[patch_tok] @ Q[patch_tok[u]]
+        if mode == MODE_TOTAL:
+            ok = np.arange(S * P) // P != fu
+            ids, kv, _ = topk(s[ok], K, patch_tok[ok])
+        else:
+            parts, kv = [], []
+            for f in range(S):
+                if f == fu:
+                    continue
+                ids_f, k_f, _ = topk(s[f * P:(f + 1) * P], K, patch_tok[f * P:(f + 1) * P])
+                parts.append(ids_f)
+                kv.append(k_f)
+            ids = np.concatenate(parts)
+        out.append(ids)
+        kth.append(kv)
+    return np.array(out, dtype=np.int64), kth
+
+
 # ---------------------------------------------------------------------------
 # Block-wise correspondence (Sec. 4.3)
 def block_scores(F: np.ndarray, S: int, P: int, b: int, qblocks: Sequence[int]) -> np.ndarray:

@@ -428,3 +428,54 @@ def test_corr_stride_with_stride_one_is_dense():
     b, _, _ = oracle.layer(geom, d_plan, w.q, w.k, w.v)
     for h in range(16):
         np.testing.assert_allclose(a[h], b[h], rtol=0, atol=1e-14)
+
+
+# ---- correspondence index from one head's logits
+@pytest.mark.parametrize("mode", [oracle.MODE_TOTAL, oracle.MODE_PER_FRAME])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_qk_index_matches_brute_force(mode, dtype):
+    S, ns, P, d, K = 3, 2, 14, 16, 5
+    T, N = ns + P, S * (ns + P)
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((N, d)).astype(np.float32)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    k[[T + ns + 3, 2 * T + ns + 3]] = k[ns + 3]              # exact ties between frames
+    if dtype == "bf16":
+        q, k = bf16_round(q), bf16_round(k)
+        qf, kf = bf16_to_f32(q).astype(np.float64), bf16_to_f32(k).astype(np.float64)
+    else:
+        qf, kf = q.astype(np.float64), k.astype(np.float64)
+    got, _ = oracle.qk_index(q, k, S, ns, P, K, np.arange(S * P), mode)
+    tok = np.array([(v // P) * T + ns + v % P for v in range(S * P)])
+    for u in range(S * P):
+        fu = u // P
+        s = kf[tok] @ qf[tok[u]]
+        if mode == oracle.MODE_TOTAL:
+            cand = [v for v in range(S * P) if v // P != fu]
+            order = sorted(cand, key=lambda v: (-s[v], tok[v]))[:K]
+        else:
+            order = []
+            for f in range(S):
+                if f != fu:
+                    order += sorted(range(f * P, (f + 1) * P), key=lambda v: (-s[v], tok[v]))[:K]
+        np.testing.assert_array_equal(got[u], np.sort(tok[order]))
+
+
+def test_qk_index_on_unit_features_is_the_cosine_index():
+    # with Q = K = the unit-normalised features, q.k is the cosine; one-hot
+    # features with distinct magnitudes keep every ranking free of near-ties
+    S, ns, P = 3, 1, 8
+    T, N = ns + P, S * (ns + P)
+    F = np.zeros((S * P, 8), dtype=np.float32)
+    for v in range(S * P):
+        F[v, v % 8] = 1.0 + 0.1 * (v // 8)
+        F[v, (v + 3) % 8] = 0.5
+    rng = np.random.default_rng(3)
+    F += 0.01 * rng.standard_normal(F.shape).astype(np.float32)
+    U = (F / np.linalg.norm(F, axis=1, keepdims=True)).astype(np.float32)
+    q = np.zeros((N, 8), dtype=np.float32)
+    tok = np.array([(v // P) * T + ns + v % P for v in range(S * P)])
+    q[tok] = U
+    want, _, _ = oracle.corr_index(F, S, ns, P, 4, np.arange(S * P))
+    got, _ = oracle.qk_index(q, q, S, ns, P, 4, np.arange(S * P))
+    np.testing.assert_array_equal(got, want)
