@@ -76,6 +76,8 @@ def parse():
     ap.add_argument("--block-k", type=int, default=7, help="blocks kept per query block for --block")
     ap.add_argument("--corr-stride", type=int, default=64,
                     help="also time the layer with its correspondence heads united with this stride (0: skip)")
+    ap.add_argument("--no-qk-index", action="store_true",
+                    help="skip timing the index built from the first correspondence head's logits")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip timing one offline-profiling pass (Sec. 4.2) over this sequence")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -256,6 +258,26 @@ def main():
                      "tflops": round(2.0 * g.Np * g.Np * w.Df / (pf_ms * 1e-3) / 1e12, 2)}
         pctx.close()
 
+    # the index taken from the first correspondence head's logits (K as the
+    # DINO index), in a context of its own; not part of the step
+    qk = None
+    if not args.no_qk_index:
+        h0 = [h for h, p in enumerate(w.plan) if p[0] == 2][0]
+        qctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+        qctx.build_corr_index_qk(q, k, h0, w.corr_K)
+        torch.cuda.synchronize()
+        qt = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            qctx.build_corr_index_qk(q, k, h0, w.corr_K)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            qt.append(e0.elapsed_time(e1))
+        qk = {"head": h0, "K": w.corr_K, "build_ms": round(statistics.median(qt), 3),
+              "tflops": round(2.0 * g.Np * g.Np * g.d / (statistics.median(qt) * 1e-3) / 1e12, 2)}
+        qctx.close()
+
     # the layer with its correspondence heads as correspondence top-K united
     # with a stride (cached total index); not part of the step
     corr_stride = None
@@ -403,6 +425,7 @@ def main():
         "per_frame_index": per_frame,
         "block_index": block,
         "corr_stride_layer": corr_stride,
+        "qk_index": qk,
         "offline_profiling": prof,
         "sparsity": round(1.0 - (shared_pairs + gather_pairs) / (g.H * g.N * g.N), 4),
         "roofline": roofline,

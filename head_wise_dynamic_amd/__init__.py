@@ -62,6 +62,7 @@ _PROTOS = {
     "saf_workspace_size": (C.c_int, [_VP, _VP, C.POINTER(_SZ)]),
     "saf_build_corr_index": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _VP]),
     "saf_build_corr_index_blocks": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _I32, _VP]),
+    "saf_build_corr_index_qk": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _I32, _VP]),
     "saf_head_nmse": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _VP, _VP]),
     "saf_head_pairs": (C.c_int, [_VP, C.POINTER(saf_head_plan_t), _I32, C.POINTER(C.c_int64)]),
     "saf_profile_select": (C.c_int32, [C.POINTER(C.c_double), C.POINTER(C.c_double), _I32]),
@@ -120,6 +121,10 @@ def saf_build_corr_index(ctx, dino, dino_dtype, Df, row_stride, K, mode, stream)
 
 def saf_build_corr_index_blocks(ctx, dino, dino_dtype, Df, row_stride, block, K, mode, stream) -> int:
     return lib().saf_build_corr_index_blocks(ctx, dino, dino_dtype, Df, row_stride, block, K, mode, stream)
+
+
+def saf_build_corr_index_qk(ctx, q, k, layout, head, K, mode, stream) -> int:
+    return lib().saf_build_corr_index_qk(ctx, q, k, layout, head, K, mode, stream)
 
 
 def saf_head_nmse(ctx, o_full, o_sparse, layout, dev_out, stream) -> int:
@@ -248,6 +253,12 @@ class Context:
             raise ValueError("dino must be [S*P, Df] with contiguous channels")
         self._check(saf_build_corr_index_blocks(self._ctx, C.c_void_p(dino.data_ptr()), _DT.get(dino.dtype, 99),
                                                 dino.shape[1], dino.stride(0), block, K, mode, _stream(stream)))
+
+    def build_corr_index_qk(self, q: torch.Tensor, k: torch.Tensor, head: int, K: int, mode: int = SAF_CORR_TOTAL,
+                            stream=None):
+        lay = self.layout_of(q)
+        self._check(saf_build_corr_index_qk(self._ctx, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()), lay, head,
+                                            K, mode, _stream(stream)))
 
     def set_corr_index(self, idx: torch.Tensor, stream=None):
         if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():

@@ -386,6 +386,64 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     return SAF_OK;
 }
 
+saf_status_t saf_build_corr_index_qk(saf_ctx_t *c, const void *q, const void *k, saf_layout_t lay, int32_t head,
+                                     int32_t K, int32_t mode, void *stream) {
+    if (!c) return SAF_EINVAL;
+    const saf::Geom &g = c->g;
+    if (!q || !k) return fail(c, SAF_EINVAL, "null q/k pointer");
+    if (g.S < 2) return fail(c, SAF_EINVAL, "correspondence index needs S >= 2");
+    if (head < 0 || head >= g.H) return fail(c, SAF_EINVAL, "head %d outside [0, %d)", head, g.H);
+    if (K < 1) return fail(c, SAF_EINVAL, "K %d < 1", K);
+    if (mode != SAF_CORR_TOTAL && mode != SAF_CORR_PER_FRAME) return fail(c, SAF_EINVAL, "bad mode %d", mode);
+    saf_status_t st = check_layout(c, lay);
+    if (st != SAF_OK) return st;
+    if (!aligned16(q) || !aligned16(k)) return fail(c, SAF_EINVAL, "q/k must be 16-byte aligned");
+    const bool per_frame = mode == SAF_CORR_PER_FRAME;
+    int32_t Kk, Kc;
+    if (per_frame) {
+        if (g.P > saf::kFrameMaxP) return fail(c, SAF_EUNSUPPORTED, "per-frame mode: P %d > %d", g.P, saf::kFrameMaxP);
+        Kk = std::min(K, g.P);
+        const int64_t row = (int64_t)(g.S - 1) * Kk;
+        if (row > INT32_MAX / 2) return fail(c, SAF_EUNSUPPORTED, "index row of %lld entries", (long long)row);
+        Kc = (int32_t)row;
+    } else {
+        Kk = Kc = (int32_t)std::min<int64_t>(K, (int64_t)(g.S - 1) * g.P);
+        if (Kc > 1024) return fail(c, SAF_EUNSUPPORTED, "K %d > 1024", Kc);
+    }
+    if ((st = ensure_corr_storage(c, Kc)) != SAF_OK) return st;
+    const int32_t cap = per_frame ? 0 : saf::corr_capacity(g, Kc);
+    const int32_t chunk_rows = per_frame ? saf::corr_frame_chunk_rows(g) : 0;
+    const size_t sb = per_frame ? saf::corr_frame_scratch_bytes(g, chunk_rows) : saf::corr_scratch_bytes(g, Kc, cap);
+    if ((st = ensure_corr_scratch(c, sb)) != SAF_OK) return st;
+    const size_t es = g.dtype == saf::BF16 ? 2 : 4;
+    saf::CorrBuild B{};
+    B.g = g;
+    B.dino = (const char *)q + (size_t)head * lay.head_stride * es;
+    B.dino_cols = (const char *)k + (size_t)head * lay.head_stride * es;
+    B.tok_map = 1;
+    B.raw_dot = 1;
+    B.dino_dtype = g.dtype;
+    B.Df = g.d;
+    B.row_stride = lay.token_stride;
+    B.K = Kk;
+    B.cap = cap;
+    B.per_frame = per_frame ? 1 : 0;
+    B.chunk_rows = chunk_rows;
+    B.idx_out = c->corr_idx;
+    B.scratch = c->corr_scratch;
+    B.mark = mark_launch;
+    B.mark_user = c;
+    hipError_t e;
+    {
+        Timed tm(c, as_stream(stream), "corr_index_qk");
+        e = saf::launch_corr_build(B, as_stream(stream));
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "logit index kernels");
+    c->corr_k = Kc;
+    c->corr_build_k = Kk;
+    return SAF_OK;
+}
+
 saf_status_t saf_build_corr_index_blocks(saf_ctx_t *c, const void *dino, int32_t dino_dtype, int32_t Df,
                                          int64_t row_stride, int32_t block, int32_t K, int32_t mode,
                                          void *stream) {

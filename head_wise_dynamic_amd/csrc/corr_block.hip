@@ -145,6 +145,7 @@ hipError_t launch_corr_blocks(const CorrBlockBuild &B, hipStream_t stream) {
     I.per_frame = B.per_frame;
     I.chunk_rows = corr_frame_chunk_rows(gb);
     I.raw_dot = 1;
+    I.total_by_frames = B.per_frame ? 0 : 1;
     I.idx_out = bidx;
     I.scratch = p;
     hipError_t e = launch_corr_build(I, stream);

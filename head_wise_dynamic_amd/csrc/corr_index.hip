@@ -83,7 +83,15 @@ struct Args {
     float *chunk;            // STORE mode: cosines of rows [row_lo, row_hi) x all columns
     int32_t guess_k;         // compaction: also set theta_g from the guess_k-th best (0: no)
     int32_t raw_dot;         // scores are plain dot products (unit "norms")
+    const void *Fc;          // column operand (== F for the symmetric cosine)
+    int32_t tok_map;         // row u of F / Fc is token (u / P) T + ns + u % P (patches of a token layout)
 };
+
+// element offset of patch row u in F / Fc
+__device__ __forceinline__ int64_t frow(const Args &A, int64_t u) {
+    const int64_t r = A.tok_map ? (u / A.g.P) * A.g.T + A.g.ns + u % A.g.P : u;
+    return r * A.stride;
+}
 
 template <typename T> __device__ inline float ldf(const T *p, int64_t i);
 template <> __device__ inline float ldf<float>(const float *p, int64_t i) { return p[i]; }
@@ -96,7 +104,7 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
     const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (u >= A.g.Np) return;
-    const T *f = (const T *)A.F + u * A.stride;
+    const T *f = (const T *)A.F + frow(A, u);
     float acc = 0.f;
     for (int c = lane; c < A.Df; c += 64) {
         const float x = ldf<T>(f, c);
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         row_hi = A.row_hi;
         col_hi = A.col_hi;
     }
-    const uint16_t *F = (const uint16_t *)A.F;
+    const uint16_t *F = (const uint16_t *)A.F, *Fc = (const uint16_t *)A.Fc;
 
     if (tid < CT) {
         const int64_t u = row0 + tid;
@@ -244,8 +252,8 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         for (int i = 0; i < 4; ++i) {
             const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
             const int64_t u = row0 + row, v = col0 + row;
-            ar[i] = u < row_hi ? *(const u32x4 *)(F + u * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
-            br[i] = v < col_hi ? *(const u32x4 *)(F + v * A.stride + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            ar[i] = u < row_hi ? *(const u32x4 *)(F + frow(A, u) + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            br[i] = v < col_hi ? *(const u32x4 *)(Fc + frow(A, v) + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto store = [&](int buf) {
@@ -631,7 +639,7 @@ constexpr int kStoreTile = 64, kStoreK = 16;
 template <typename T> __global__ __launch_bounds__(256) void cos_store_tiled(const Args A) {
     __shared__ float As[kStoreK][kStoreTile + 4], Bs[kStoreK][kStoreTile + 4];
     const Geom &g = A.g;
-    const T *F = (const T *)A.F;
+    const T *F = (const T *)A.F, *Fc = (const T *)A.Fc;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const int64_t r0 = A.row_lo + (int64_t)blockIdx.y * kStoreTile, c0 = (int64_t)blockIdx.x * kStoreTile;
     float acc[4][4];
@@ -645,8 +653,8 @@ template <typename T> __global__ __launch_bounds__(256) void cos_store_tiled(con
             const int e = tid + 256 * i, r = e / kStoreK, k = e % kStoreK;
             const int64_t u = r0 + r, v = c0 + r;
             const bool kin = k0 + k < A.Df;
-            As[k][r] = (u < A.row_hi && kin) ? ldf<T>(F, u * A.stride + k0 + k) : 0.f;
-            Bs[k][r] = (v < g.Np && kin) ? ldf<T>(F, v * A.stride + k0 + k) : 0.f;
+            As[k][r] = (u < A.row_hi && kin) ? ldf<T>(F, frow(A, u) + k0 + k) : 0.f;
+            Bs[k][r] = (v < g.Np && kin) ? ldf<T>(Fc, frow(A, v) + k0 + k) : 0.f;
         }
         __syncthreads();
 #pragma unroll
@@ -798,17 +806,17 @@ template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(cons
     __shared__ float fu[4096];
     const Geom &g = A.g;
     float *row = A.s.rowbuf + (int64_t)blockIdx.x * g.Np;
-    const T *F = (const T *)A.F;
+    const T *F = (const T *)A.F, *Fc = (const T *)A.Fc;
     for (int64_t u = blockIdx.x; u < g.Np; u += gridDim.x) {
         if (!A.s.over[u]) continue;
         __syncthreads();
-        for (int c = threadIdx.x; c < A.Df; c += 1024) fu[c] = ldf<T>(F + u * A.stride, c);
+        for (int c = threadIdx.x; c < A.Df; c += 1024) fu[c] = ldf<T>(F + frow(A, u), c);
         __syncthreads();
         const float iu = A.s.invn[u];
         const int64_t fr = u / g.P;
         for (int64_t v = threadIdx.x; v < g.Np; v += 1024) {
             float acc = 0.f;
-            const T *fv = F + v * A.stride;
+            const T *fv = Fc + frow(A, v);
             for (int c = 0; c < A.Df; ++c) acc = fmaf(fu[c], ldf<T>(fv, c), acc);
             // own-frame patches can never be selected: the candidate count
             // (S-1)P is >= K, so they are given the lowest possible score
@@ -933,6 +941,8 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     Args A{};
     A.g = B.g;
     A.F = B.dino;
+    A.Fc = B.dino_cols ? B.dino_cols : B.dino;
+    A.tok_map = B.tok_map;
     A.stride = B.row_stride;
     A.Df = B.Df;
     A.K = B.K;
@@ -953,7 +963,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             hipLaunchKernelGGL(init_rows<float>, dim3(rb), dim3(256), 0, stream, A);
         return launch_corr_frames(A, B, false, stream);
     }
-    if (B.raw_dot) {
+    if (B.total_by_frames) {
         // Total mode by way of frames: the K best overall lie among the
         // min(K, P) best of each frame, so every row's per-frame top lists
         // become its candidates and finalize selects exactly among them.
@@ -984,7 +994,8 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
         return hipGetLastError();
     }
     A.seed_cols = std::min<int64_t>(Np, 2 * (int64_t)B.g.P);
-    A.sym_lo = corr_sym_start(B.g);
+    // the symmetric square needs one operand for rows and columns
+    A.sym_lo = (A.Fc == A.F) ? corr_sym_start(B.g) : Np;
     const unsigned rb = (unsigned)((Np + 3) / 4);
     if (B.dino_dtype == BF16)
         hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);

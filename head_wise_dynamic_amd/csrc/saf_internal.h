@@ -122,6 +122,9 @@ struct CorrBuild {
     int32_t per_frame;  // 1: the K best of every other frame, [Np, (S-1) K]
     int32_t chunk_rows; // per-frame mode: rows whose cosines are materialised at once
     int32_t raw_dot;    // 1: rank by the plain dot product f_u . f_v (no normalisation)
+    const void *dino_cols;  // column operand (nullptr: the rows' own features, symmetric)
+    int32_t tok_map;    // 1: patch row u lives at token (u / P) T + ns + u % P of a token layout
+    int32_t total_by_frames;  // total mode as per-frame candidates + exact selection (short rows)
     int32_t *idx_out;   // [Np, K] or [Np, (S-1) K]
     void *scratch;      // corr_scratch_bytes() / corr_frame_scratch_bytes()
     // optional tracing hook: called with begin = 1 / 0 around every cosine
@@ -134,7 +137,7 @@ int32_t corr_capacity(const Geom &g, int32_t K);
 constexpr int32_t kFrameMaxP = 4096;  // per-frame mode: patches per frame the selection holds
 int32_t corr_frame_chunk_rows(const Geom &g);
 size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows);
-// raw_dot total mode (per-frame candidates, then an exact selection)
+// total_by_frames total mode (per-frame candidates, then an exact selection)
 size_t corr_raw_total_scratch_bytes(const Geom &g, int32_t K);
 hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream);
 

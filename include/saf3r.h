@@ -153,6 +153,21 @@ saf_status_t saf_build_corr_index(saf_ctx_t *ctx, const void *dino, int32_t dino
                                   int32_t Df, int64_t dino_row_stride, int32_t K,
                                   int32_t mode, void *stream);
 
+/* Correspondence index taken from one head's own attention logits instead
+ * of DINO features (the first direction the paper names for improving the
+ * DINO Top-K kernel: indices from the first correspondence head).  For every
+ * patch u (token i) the patch tokens j of other frames are ranked by
+ * (q_i . k_j desc, token asc) -- the 1/sqrt(d) scale does not change the
+ * order -- using head `head` of q and k (context dtype, layout as for
+ * attention); TOTAL keeps the first min(K, (S-1)P) (at most 1024), PER_FRAME
+ * the first min(K, P) of every other frame.  The result replaces the cached
+ * index exactly like saf_build_corr_index and serves every later
+ * correspondence head.
+ * Errors: SAF_EINVAL (S < 2, bad head/K/mode/layout/pointer),
+ * SAF_EUNSUPPORTED (TOTAL with Kc > 1024, PER_FRAME with P > 4096), SAF_ENOMEM. */
+saf_status_t saf_build_corr_index_qk(saf_ctx_t *ctx, const void *q, const void *k, saf_layout_t layout,
+                                     int32_t head, int32_t K, int32_t mode, void *stream);
+
 /* Block-wise variant of the correspondence index (Sec. 4.3: block-level
  * similarities averaged over tokens, a cheaper build).  A block is `block`
  * consecutive patches of one frame (block must divide P; block = the patch

@@ -158,6 +158,25 @@ def test_build_corr_index_blocks_validation():
         saf.saf_destroy(c)
 
 
+def test_build_corr_index_qk_validation():
+    c = _ctx()
+    try:
+        b = saf.saf_build_corr_index_qk
+        assert b(c, None, FAKE, LAY, 0, 8, 0, None) == saf.SAF_EINVAL
+        assert b(c, FAKE, FAKE, LAY, 16, 8, 0, None) == saf.SAF_EINVAL     # head
+        assert b(c, FAKE, FAKE, LAY, -1, 8, 0, None) == saf.SAF_EINVAL
+        assert b(c, FAKE, FAKE, LAY, 0, 0, 0, None) == saf.SAF_EINVAL      # K
+        assert b(c, FAKE, FAKE, LAY, 0, 8, 3, None) == saf.SAF_EINVAL      # mode
+    finally:
+        saf.saf_destroy(c)
+    c = _ctx(S=9)
+    try:   # 2000 of 8 x 256 candidates in one total-mode row
+        lay = saf.saf_layout_t(9 * 261 * 64, 64)
+        assert saf.saf_build_corr_index_qk(c, FAKE, FAKE, lay, 0, 2000, 0, None) == saf.SAF_EUNSUPPORTED
+    finally:
+        saf.saf_destroy(c)
+
+
 def test_vertical_index_validation():
     c = _ctx()
     try:
