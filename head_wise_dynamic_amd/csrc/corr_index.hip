@@ -36,6 +36,7 @@ namespace {
 
 constexpr int kRowWaves = 4;  // rows per block in the per-row wave kernels
 constexpr int kFallbackBlocks = 256;
+constexpr int kFixBatches = 4;  // flagged rows recomputed on the matrix cores: 4 x 256
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -45,6 +46,8 @@ struct Scratch {
     float *theta_g;   // [Np] filter threshold of the symmetric pass (a guess, checked at the end)
     uint32_t *cnt;    // [Np]
     uint32_t *over;   // [Np] row needs the exact per-row engine
+    int32_t *row_list;    // [Np] flagged rows, for the matrix-core recomputation
+    uint32_t *row_count;  // [1] entries in row_list
     float2 *cand;     // [Np * cap] (score, patch index as float bits)
     float *rowbuf;    // [kFallbackBlocks * Np] fallback scores
 };
@@ -62,6 +65,10 @@ __host__ __device__ inline Scratch carve(void *base, int64_t Np, int32_t cap) {
     p += align256(sizeof(uint32_t) * Np);
     s.over = (uint32_t *)p;
     p += align256(sizeof(uint32_t) * Np);
+    s.row_list = (int32_t *)p;
+    p += align256(sizeof(int32_t) * Np);
+    s.row_count = (uint32_t *)p;
+    p += 256;
     s.cand = (float2 *)p;
     p += align256(sizeof(float2) * (size_t)Np * cap);
     s.rowbuf = (float *)p;
@@ -85,6 +92,7 @@ struct Args {
     int32_t raw_dot;         // scores are plain dot products (unit "norms")
     const void *Fc;          // column operand (== F for the symmetric cosine)
     int32_t tok_map;         // row u of F / Fc is token (u / P) T + ns + u % P (patches of a token layout)
+    int32_t use_list;        // STORE: tile rows are positions in s.row_list (flagged rows)
 };
 
 // element offset of patch row u in F / Fc
@@ -116,6 +124,7 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
         A.s.invn[u] = A.raw_dot ? 1.f : (acc > 0.f ? 1.f / sqrtf(acc) : 0.f);
         A.s.theta[u] = -INFINITY;
         A.s.theta_g[u] = -INFINITY;
+        if (u == 0) *A.s.row_count = 0u;
         // the seed phase fills slots [0, seed_cols minus the own frame)
         const int64_t fr = u / A.g.P;
         A.s.cnt[u] = A.all_rows_fallback ? 0u
@@ -220,12 +229,20 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         col_hi = A.col_hi;
     }
     const uint16_t *F = (const uint16_t *)A.F, *Fc = (const uint16_t *)A.Fc;
+    // STORE over a row list: tile rows are list positions; nothing to do past the list
+    const uint32_t nlist = (MODE == STORE && A.use_list) ? *A.s.row_count : 0u;
+    if (MODE == STORE && A.use_list && row0 >= (int64_t)nlist) return;
+    auto actual_row = [&](int64_t pos) -> int64_t {
+        if (pos >= row_hi) return -1;
+        if (MODE == STORE && A.use_list) return pos < (int64_t)nlist ? (int64_t)A.s.row_list[pos] : -1;
+        return pos;
+    };
 
     if (tid < CT) {
-        const int64_t u = row0 + tid;
+        const int64_t u = actual_row(row0 + tid);
         float thr = INFINITY, iu = 0.f;
         int32_t fr = -1;
-        if (u < row_hi) {
+        if (u >= 0) {
             iu = A.s.invn[u];
             fr = (int32_t)(u / g.P);
             thr = scaled_threshold(MODE == SYM ? A.s.theta_g[u] : A.s.theta[u], iu);
@@ -246,14 +263,22 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, col_hi) - 1) / g.P);
     const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
+    // element offsets of the rows this thread loads (0xFFFFFFFF: none)
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = (tid + kCosThreads * i) >> 3;
+        const int64_t u = actual_row(row0 + row), v = col0 + row;
+        aoff[i] = u >= 0 ? (uint32_t)frow(A, u) : 0xFFFFFFFFu;
+        boff[i] = v < col_hi ? (uint32_t)frow(A, v) : 0xFFFFFFFFu;
+    }
     u32x4 ar[4], br[4];
     auto load = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
-            const int64_t u = row0 + row, v = col0 + row;
-            ar[i] = u < row_hi ? *(const u32x4 *)(F + frow(A, u) + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
-            br[i] = v < col_hi ? *(const u32x4 *)(Fc + frow(A, v) + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            const int seg = (tid + kCosThreads * i) & 7;
+            ar[i] = aoff[i] != 0xFFFFFFFFu ? *(const u32x4 *)(F + aoff[i] + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            br[i] = boff[i] != 0xFFFFFFFFu ? *(const u32x4 *)(Fc + boff[i] + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto store = [&](int buf) {
@@ -801,6 +826,32 @@ __global__ __launch_bounds__(256) void frame_topk(const Args A) {
     }
 }
 
+// ---- flagged rows (overflow or a failed guess check) into a list
+__global__ __launch_bounds__(256) void list_flagged(const Args A) {
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= A.g.Np || !A.s.over[u]) return;
+    const uint32_t pos = atomicAdd(A.s.row_count, 1u);
+    A.s.row_list[pos] = (int32_t)u;
+}
+
+// ---- exact selection of listed rows [batch0, batch0 + gridDim.x) whose
+// cosines a row-list STORE pass wrote to A.chunk; clears their flag
+__global__ __launch_bounds__(1024) void select_listed(const Args A, int64_t batch0) {
+    const Geom &g = A.g;
+    const int64_t pos = batch0 + blockIdx.x;
+    if (pos >= (int64_t)*A.s.row_count) return;
+    const int64_t u = A.s.row_list[pos];
+    float *row = A.chunk + (int64_t)blockIdx.x * g.Np;
+    const int64_t f0 = (u / g.P) * g.P;  // own-frame patches can never be selected
+    for (int64_t j = threadIdx.x; j < g.P; j += 1024) row[f0 + j] = -INFINITY;
+    __syncthreads();
+    int32_t *out = A.idx_out + u * A.K;
+    block_topk_ascending(row, g.Np, A.K, [&](int64_t p, int64_t v) {
+        out[p] = (int32_t)((v / g.P) * g.T + g.ns + (v % g.P));
+    });
+    if (threadIdx.x == 0) A.s.over[u] = 0u;
+}
+
 // ---- exact per-row engine: one 1024-thread block per flagged row
 template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(const Args A) {
     __shared__ float fu[4096];
@@ -834,21 +885,21 @@ template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(cons
 }  // namespace
 
 // Start of the symmetric square: the first doubling boundary W (2P, 4P, ...)
-// with Np - W <= 12 W, so that every row's threshold comes from at least a
-// thirteenth of the columns before the square is visited in one pass.
+// with Np - W <= 24 W, so that every row's guess of its K-th best comes from
+// at least a twenty-fifth of the columns before the square is visited once.
 int64_t corr_sym_start(const Geom &g) {
     int64_t b = std::min<int64_t>(g.Np, 2 * (int64_t)g.P);
-    while (b < g.Np && g.Np - b > 12 * b) b *= 2;
+    while (b < g.Np && g.Np - b > 24 * b) b *= 2;
     return std::min<int64_t>(b, g.Np);
 }
 
 int32_t corr_capacity(const Geom &g, int32_t K) {
     // the seed phase stores two frames' candidates; a doubling phase adds
-    // ~K; the symmetric pass adds ~K (Np - W) / W with thresholds from W
-    const int64_t W = corr_sym_start(g);
-    const int64_t ratio = W < g.Np ? (g.Np - W + W - 1) / W : 0;
+    // ~K; the symmetric pass, filtering with a guess near 2.5 x the K-th
+    // best's rank, adds ~2.5 K per direction.  A row that still overflows is
+    // flagged and recomputed exactly.
     int64_t cap = std::max<int64_t>(2 * (int64_t)g.P, 8 * (int64_t)K);
-    cap = std::max<int64_t>(cap, (int64_t)K * (2 * ratio + 1) + 256);
+    cap = std::max<int64_t>(cap, 6 * (int64_t)K + 256);
     cap = (cap + 63) / 64 * 64;
     return (int32_t)cap;
 }
@@ -856,7 +907,7 @@ int32_t corr_capacity(const Geom &g, int32_t K) {
 // bytes carve() lays out before rowbuf
 static size_t carve_head_bytes(int64_t Np, int32_t cap) {
     return align256(sizeof(float) * Np) * 3 + align256(sizeof(uint32_t) * Np) * 2 +
-           align256(sizeof(float2) * (size_t)Np * cap);
+           align256(sizeof(int32_t) * Np) + 256 + align256(sizeof(float2) * (size_t)Np * cap);
 }
 
 size_t corr_scratch_bytes(const Geom &g, int32_t K, int32_t cap) {
@@ -1051,6 +1102,23 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
         }
         hipLaunchKernelGGL(finalize_rows<16>, dim3(cb), dim3(256), 0, stream, A, 0u, small);
         hipLaunchKernelGGL(finalize_rows<64>, dim3(cb), dim3(256), 0, stream, A, small, 0xFFFFFFFFu);
+        // rows flagged for an exact recomputation: the first kFixBatches x
+        // kFallbackBlocks on the matrix cores (cosines of a batch of listed
+        // rows into the fallback rows, then an exact block selection), the
+        // rest, if any, on the per-row engine below
+        hipLaunchKernelGGL(list_flagged, dim3((unsigned)((Np + 255) / 256)), dim3(256), 0, stream, A);
+        Args L = A;
+        L.use_list = 1;
+        L.col_lo = 0;
+        L.col_hi = Np;
+        L.chunk = A.s.rowbuf;
+        const int64_t ct = (Np + CT - 1) / CT;
+        for (int b = 0; b < kFixBatches; ++b) {
+            L.row_lo = (int64_t)b * kFallbackBlocks;
+            L.row_hi = L.row_lo + kFallbackBlocks;
+            hipLaunchKernelGGL(cos_phase<STORE>, dim3((unsigned)(8 * ((ct + 7) / 8))), dim3(kCosThreads), 0, stream, L);
+            hipLaunchKernelGGL(select_listed, dim3(kFallbackBlocks), dim3(1024), 0, stream, L, L.row_lo);
+        }
     }
     const unsigned fb = (unsigned)std::min<int64_t>(kFallbackBlocks, Np);
     if (B.dino_dtype == BF16)
