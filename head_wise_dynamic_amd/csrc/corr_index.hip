@@ -21,8 +21,10 @@
 //      exact K-th best must reach theta_g_u, else the row is recomputed;
 //   5. a final wave per row selects the exact top-K, sorts it by token and
 //      writes it.
-//   A row whose buffer overflows is flagged and recomputed exactly by the
-//   per-row engine at the end.
+//   A row whose buffer overflows or whose guess check fails is flagged and
+//   recomputed exactly: up to 1,024 such rows by the cosine GEMM over a list
+//   of rows (cosines stored, then an exact block selection), any further ones
+//   by the per-row engine.
 // fp32 features (and flagged rows): one 1024-thread block per row computes
 //   every cosine with VALU FMAs into a scratch row and runs an exact block
 //   top-K (radix select + ordered compaction).

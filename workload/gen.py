@@ -307,3 +307,24 @@ def make_front_loaded_dino(S: int, P: int, Df: int, first_frames: int, n_rows: i
     for r, sl in zip(rows, slots):
         F[sl] = F[r] + np.float32(0.05) * rng.standard_normal((copies, Df), dtype=np.float32)
     return bf16_round(F), rows
+
+
+def make_grouped_front_dino(S: int, P: int, Df: int, first_frames: int, groups: int, group_size: int,
+                            copies: int, seed: int) -> Tuple[np.ndarray, np.ndarray]:
+    """bf16 features [S*P, Df] of i.i.d. N(0, 1) draws, except for `groups`
+    latent directions z_g ~ N(0, I): group g puts `group_size` noisy copies
+    (z_g + N(0, 0.05^2)) at random patches of frames >= first_frames and
+    `copies` more at random patches of frames [0, first_frames).  Returns
+    (features as bf16 bits, the late patches of every group, sorted)."""
+    rng = np.random.default_rng(seed)
+    F = rng.standard_normal((S * P, Df), dtype=np.float32)
+    front = first_frames * P
+    if groups * copies > front or groups * group_size > S * P - front:
+        raise ValueError("not enough patches for the groups")
+    early = rng.permutation(front)[:groups * copies].reshape(groups, copies)
+    late = (front + rng.permutation(S * P - front)[:groups * group_size]).reshape(groups, group_size)
+    for gi in range(groups):
+        z = rng.standard_normal(Df, dtype=np.float32)
+        for idx in (early[gi], late[gi]):
+            F[idx] = z + np.float32(0.05) * rng.standard_normal((idx.size, Df), dtype=np.float32)
+    return bf16_round(F), np.sort(late.reshape(-1))
