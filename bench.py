@@ -78,6 +78,8 @@ def parse():
                     help="also time the layer with its correspondence heads united with this stride (0: skip)")
     ap.add_argument("--no-qk-index", action="store_true",
                     help="skip timing the index built from the first correspondence head's logits")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip timing the 24-layer stack (index built once, the stack's per-layer plans)")
     ap.add_argument("--no-profile", action="store_true",
                     help="skip timing one offline-profiling pass (Sec. 4.2) over this sequence")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -221,6 +223,45 @@ def main():
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1))
     del scrub
+
+    # per-step spread: every step timed on its own (warm caches)
+    single = []
+    for _ in range(max(10, args.reps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        single.append(e0.elapsed_time(e1))
+    single.sort()
+    pct = lambda p: single[min(len(single) - 1, int(round(p * (len(single) - 1))))]
+    step_spread = {"p10": round(pct(0.1), 3), "p50": round(pct(0.5), 3), "p90": round(pct(0.9), 3),
+                   "n": len(single)}
+
+    # the 24-layer stack of the same geometry: the index built once, then the
+    # stack's 24 per-layer plans (roles permuted per layer; layers 10-16 with
+    # six correspondence heads) run on this sequence's Q/K/V
+    stack = None
+    if not args.no_stack and args.config == 3:
+        from workload import layer_roles
+        plans = []
+        for l in range(24):
+            roles, budgets = layer_roles(4, l)
+            plans.append([(r, b, 0, 0) for r, b in zip(roles, budgets)])
+        ctx.build_corr_index(dino, w.corr_K)
+        for pl in plans:
+            ctx.sparse_attention(pl, q, k, v, o=o)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        ctx.build_corr_index(dino, w.corr_K)
+        e1.record(stream)
+        for pl in plans:
+            ctx.sparse_attention(pl, q, k, v, o=o)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        stack = {"layers": 24, "index_ms": round(e0.elapsed_time(e1), 3), "layers_ms": round(e1.elapsed_time(e2), 3),
+                 "total_ms": round(e0.elapsed_time(e2), 3)}
 
     dense_ms = None
     if not args.no_dense:
@@ -416,6 +457,8 @@ def main():
         "wall_s_timed_region": round(wall, 3),
         "attn_only_ms": round(attn_ms, 4),
         "cold_step_ms_median": round(statistics.median(cold), 4),
+        "step_ms_spread": step_spread,
+        "stack_24_layers": stack,
         "breakdown_ms": breakdown,
         "corr_index_tflops": round(corr_flops / (corr_ms * 1e-3) / 1e12, 2) if corr_ms else None,
         "dense_ms": round(dense_ms, 3) if dense_ms else None,

@@ -245,21 +245,30 @@ def make_geometry_inputs(geom: Geometry, dtype: str, roles: Sequence[int],
                     dino=dino_arr, Df=Df, corr_K=corr_K, lat=lat, salient=salient, seed=seed)
 
 
+def layer_roles(cid: int, layer: int = 0) -> Tuple[List[int], List[int]]:
+    """(roles, budgets) of the 16 heads of one measured configuration (one
+    layer of config 4's stack: roles permuted by rng(4000 + layer))."""
+    c = CONFIGS[cid]
+    roles = list(c["roles"])
+    if cid == 4:
+        if layer in c["corr_layers"]:
+            roles = list(c["corr_roles"])
+        roles = [roles[i] for i in np.random.default_rng(4000 + layer).permutation(len(roles))]
+    budgets = [_budget(r, c["vert_K"], c["corr_K"], c["scan_s"]) for r in roles]
+    return roles, budgets
+
+
 def make_layer(cid: int, layer: int = 0, dino: bool = True,
                heads: Optional[Sequence[int]] = None) -> Workload:
     """Inputs of one measured configuration (one layer of config 4's stack)."""
     c = CONFIGS[cid]
     geom = Geometry(S=c["S"], ns=c["ns"], P=c["P"])
-    roles = list(c["roles"])
+    roles, budgets = layer_roles(cid, layer)
     qkv_seed = None
     name = c["name"]
     if cid == 4:
-        if layer in c["corr_layers"]:
-            roles = list(c["corr_roles"])
-        roles = [roles[i] for i in np.random.default_rng(4000 + layer).permutation(len(roles))]
         qkv_seed = 100 + layer
         name = f"{name}_L{layer}"
-    budgets = [_budget(r, c["vert_K"], c["corr_K"], c["scan_s"]) for r in roles]
     return make_geometry_inputs(geom, c["dtype"], roles, budgets, c["M"], c["Df"], seed=cid,
                                 qkv_seed=qkv_seed, corr_K=c["corr_K"], name=name, dino=dino, heads=heads)
 
