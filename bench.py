@@ -35,15 +35,15 @@ PEAK_BF16_TFLOPS = 2500.0
 # FETCH_SIZE, then WRITE_SIZE, in separate runs; KiB per dispatch averaged per
 # kernel and summed over the step's 1 seed + 6 filtered + 1 symmetric launches).
 # Each counter is scaled by what it reads for a plain 1 GiB device copy in the
-# same run (FETCH_SIZE 524309.2 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
+# same run (FETCH_SIZE 524308.7 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
 # for the kernel source with this digest only; after any change the traffic is
 # reported as null until the counters are taken again.
 COSINE_GEMM_COUNTERS = {
     "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-    "sha256": "440b24a504bfe5dc1c18c3aae408cc23b5cf5149be4bef4444b73670722fa1dc",
-    "fetch_kib_per_step": 789195.15 + 6 * 680913.03 + 32132252.50,
-    "write_kib_per_step": 2901361.27 + 6 * 119786.09 + 1413809.89,
-    "fetch_scale": 1048576.0 / 524309.19,
+    "sha256": "8e4e285d1e868b31dd35990723ec6e99176240435e259b89af8d126c45e70925",
+    "fetch_kib_per_step": 800405.31 + 6 * 320407.89 + 34993488.23,
+    "write_kib_per_step": 2901377.13 + 6 * 67044.11 + 1566687.89,
+    "fetch_scale": 1048576.0 / 524308.66,
     "write_scale": 1048576.0 / 1048576.0,
 }
 
