@@ -22,7 +22,7 @@ struct saf_ctx {
     std::string err;
     int32_t *corr_idx = nullptr;  // [Np, corr_k]
     int32_t corr_k = 0;
-    int32_t corr_build_k = 0;  // K the index was built with (per frame in per-frame mode)
+    int32_t corr_build_k = 0;  // K requested for the index (per frame or per block set), before clamping
     size_t corr_bytes = 0;
     void *corr_scratch = nullptr;
     size_t corr_scratch_bytes = 0;
@@ -382,7 +382,7 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     }
     if (e != hipSuccess) return hip_fail(c, e, "correspondence index kernels");
     c->corr_k = Kc;
-    c->corr_build_k = Kk;
+    c->corr_build_k = K;
     return SAF_OK;
 }
 
@@ -440,7 +440,7 @@ saf_status_t saf_build_corr_index_qk(saf_ctx_t *c, const void *q, const void *k,
     }
     if (e != hipSuccess) return hip_fail(c, e, "logit index kernels");
     c->corr_k = Kc;
-    c->corr_build_k = Kk;
+    c->corr_build_k = K;
     return SAF_OK;
 }
 
@@ -491,7 +491,7 @@ saf_status_t saf_build_corr_index_blocks(saf_ctx_t *c, const void *dino, int32_t
     }
     if (e != hipSuccess) return hip_fail(c, e, "block correspondence index kernels");
     c->corr_k = Kc;
-    c->corr_build_k = B.K;
+    c->corr_build_k = K;
     return SAF_OK;
 }
 

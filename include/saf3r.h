@@ -107,8 +107,8 @@ typedef struct {
     int32_t role;          /* saf_role_t */
     int32_t budget;        /* VERTICAL: K >= 1 (clamped to N); SCANNING: stride >= 1;
                               CORRESPONDENCE: 0, the cached index's row length Kc
-                              or the K it was built with; CORR_STRIDE: stride >= 1;
-                              others: 0 */
+                              or the K requested when it was built (before
+                              clamping); CORR_STRIDE: stride >= 1; others: 0 */
     int32_t anchor_frame;  /* POSITION: anchor frame in [0, S); others ignored */
     int32_t flags;         /* must be 0 */
 } saf_head_plan_t;
