@@ -95,6 +95,7 @@ struct Args {
     const void *Fc;          // column operand (== F for the symmetric cosine)
     int32_t tok_map;         // row u of F / Fc is token (u / P) T + ns + u % P (patches of a token layout)
     int32_t use_list;        // STORE: tile rows are positions in s.row_list (flagged rows)
+    uint32_t f_bytes;        // bytes of F (and of Fc) that rows 0..Np-1 span; 0: over 0xFFFF0000
 };
 
 // element offset of patch row u in F / Fc
@@ -175,7 +176,7 @@ __device__ __forceinline__ float scaled_threshold(float th, float inv_self) {
     return th <= 0.f ? -INFINITY : INFINITY;  // zero-norm row: every cosine is 0
 }
 
-template <int MODE>
+template <int MODE, int NK>
 __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     constexpr int kRowCap = MODE == SYM ? 24 : 48;  // survivors staged per row per tile
     // operand tiles: As[2], Bs[2]; after the k-loop the same memory stages the
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
 
     if (tid < CT) {
         const int64_t u = actual_row(row0 + tid);
-        float thr = INFINITY, iu = 0.f;
+        float thr = INFINITY, iu = __builtin_nanf("");  // NaN: no comparison passes
         int32_t fr = -1;
         if (u >= 0) {
             iu = A.s.invn[u];
@@ -265,33 +266,6 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, col_hi) - 1) / g.P);
     const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
-    // element offsets of the rows this thread loads (0xFFFFFFFF: none)
-    uint32_t aoff[4], boff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = (tid + kCosThreads * i) >> 3;
-        const int64_t u = actual_row(row0 + row), v = col0 + row;
-        aoff[i] = u >= 0 ? (uint32_t)frow(A, u) : 0xFFFFFFFFu;
-        boff[i] = v < col_hi ? (uint32_t)frow(A, v) : 0xFFFFFFFFu;
-    }
-    u32x4 ar[4], br[4];
-    auto load = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int seg = (tid + kCosThreads * i) & 7;
-            ar[i] = aoff[i] != 0xFFFFFFFFu ? *(const u32x4 *)(F + aoff[i] + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
-            br[i] = boff[i] != 0xFFFFFFFFu ? *(const u32x4 *)(Fc + boff[i] + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
-            *(u32x4 *)(&As[buf][row * CROW + 8 * seg]) = ar[i];
-            *(u32x4 *)(&Bs[buf][row * CROW + 8 * seg]) = br[i];
-        }
-    };
-
     f32x16 acc[2][4];
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
@@ -299,14 +273,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         for (int bj = 0; bj < 4; ++bj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
-
-    const int nk = A.Df / CK;
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nk) load((t + 1) * CK);
+    auto mma = [&](int buf) {
 #pragma unroll
         for (int kk = 0; kk < CK / 16; ++kk) {
             __builtin_amdgcn_iglp_opt(0);  // interleave LDS reads with the MFMA chain
@@ -323,8 +290,91 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                 for (int bj = 0; bj < 4; ++bj)
                     acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
         }
-        if (t + 1 < nk) store(buf ^ 1);
+    };
+    if constexpr (NK > 0) {  // NK = Df / CK
+        // Channel count known at compile time: the stage loop is unrolled
+        // completely and no load sits behind a branch, so the compiler waits
+        // only for the stage it stores (a run-time loop with guarded loads
+        // waited for everything and ran the same tiles ~20 % slower).  Loads
+        // go through buffer resources: a scalar base plus a 32-bit lane
+        // offset, and an offset past the buffer reads as zero.
+        const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc((void *)F, (short)0, (int)A.f_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void *)Fc, (short)0, (int)A.f_bytes, 0x00020000);
+        // rows past the tile's end start at the buffer's end: with f_bytes
+        // <= 0xFFFF0000 every stage offset added stays past it (no wrap)
+        const uint32_t kNone = A.f_bytes;
+        uint32_t aoff[4], boff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (tid + kCosThreads * i) >> 3, seg = (tid + kCosThreads * i) & 7;
+            const int64_t u = actual_row(row0 + row), v = col0 + row;
+            aoff[i] = u >= 0 ? 2u * ((uint32_t)frow(A, u) + 8u * seg) : kNone;
+            boff[i] = v < col_hi ? 2u * ((uint32_t)frow(A, v) + 8u * seg) : kNone;
+        }
+        u32x4 ar[4], br[4];
+        auto load = [&](int st) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ar[i] = __builtin_amdgcn_raw_buffer_load_b128(rf, aoff[i] + 2 * CK * st, 0, 0);
+                br[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, boff[i] + 2 * CK * st, 0, 0);
+            }
+        };
+        auto store = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
+                *(u32x4 *)(&As[buf][row * CROW + 8 * seg]) = ar[i];
+                *(u32x4 *)(&Bs[buf][row * CROW + 8 * seg]) = br[i];
+            }
+        };
+        load(0);
+        store(0);
         __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NK; ++t) {
+            if (t + 1 < NK) load(t + 1);
+            mma(t & 1);
+            if (t + 1 < NK) store((t + 1) & 1);
+            __syncthreads();
+        }
+    } else {
+        // element offsets of the rows this thread loads (0xFFFFFFFF: none)
+        uint32_t aoff[4], boff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = (tid + kCosThreads * i) >> 3;
+            const int64_t u = actual_row(row0 + row), v = col0 + row;
+            aoff[i] = u >= 0 ? (uint32_t)frow(A, u) : 0xFFFFFFFFu;
+            boff[i] = v < col_hi ? (uint32_t)frow(A, v) : 0xFFFFFFFFu;
+        }
+        u32x4 ar[4], br[4];
+        auto load = [&](int k0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int seg = (tid + kCosThreads * i) & 7;
+                ar[i] = aoff[i] != 0xFFFFFFFFu ? *(const u32x4 *)(F + aoff[i] + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+                br[i] = boff[i] != 0xFFFFFFFFu ? *(const u32x4 *)(Fc + boff[i] + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        auto store = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
+                *(u32x4 *)(&As[buf][row * CROW + 8 * seg]) = ar[i];
+                *(u32x4 *)(&Bs[buf][row * CROW + 8 * seg]) = br[i];
+            }
+        };
+        const int nk = A.Df / CK;
+        load(0);
+        store(0);
+        __syncthreads();
+        for (int t = 0; t < nk; ++t) {
+            const int buf = t & 1;
+            if (t + 1 < nk) load((t + 1) * CK);
+            mma(buf);
+            if (t + 1 < nk) store(buf ^ 1);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: lane holds column n of each block, rows per register.
@@ -945,6 +995,27 @@ size_t corr_raw_total_scratch_bytes(const Geom &g, int32_t K) {
     return carve_head_bytes(g.Np, cap) + align256(sizeof(float) * (size_t)rows * g.Np);
 }
 
+// elements of F (and Fc) that rows 0..Np-1 span; the matrix-core kernels
+// address them with 32-bit offsets
+static int64_t feature_span(const CorrBuild &B) {
+    const int64_t last = B.tok_map ? (int64_t)(B.g.S - 1) * B.g.T + B.g.ns + B.g.P - 1 : B.g.Np - 1;
+    return last * B.row_stride + B.Df;
+}
+
+// cos_phase launch with the stage count fixed at compile time for the usual
+// feature widths (ViT-S/B/L: 384, 768, 1024 channels)
+template <int MODE> static void launch_cos(dim3 grid, hipStream_t stream, const Args &A) {
+    const bool fixed = A.f_bytes != 0;  // byte offsets fit 32 bits
+    if (fixed && A.Df == 1024)
+        hipLaunchKernelGGL((cos_phase<MODE, 16>), grid, dim3(kCosThreads), 0, stream, A);
+    else if (fixed && A.Df == 768)
+        hipLaunchKernelGGL((cos_phase<MODE, 12>), grid, dim3(kCosThreads), 0, stream, A);
+    else if (fixed && A.Df == 384)
+        hipLaunchKernelGGL((cos_phase<MODE, 6>), grid, dim3(kCosThreads), 0, stream, A);
+    else
+        hipLaunchKernelGGL((cos_phase<MODE, 0>), grid, dim3(kCosThreads), 0, stream, A);
+}
+
 // cand = false: per-frame index into A.idx_out.  cand = true: every row's
 // per-frame top-A.K as (score, patch) candidates in A.s.cand (A.cap =
 // (S-1) A.K per row), for an exact selection over all frames afterwards.
@@ -953,7 +1024,7 @@ static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, bool cand, hip
     const int64_t Np = g.Np;
     if (B.chunk_rows < 1) return hipErrorInvalidValue;
     A.chunk = A.s.rowbuf;  // the chunk follows the per-row arrays and candidates
-    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0;
+    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && feature_span(B) < 0xFFFFFFFFll;
     for (int64_t r0 = 0; r0 < Np; r0 += B.chunk_rows) {
         A.row_lo = r0;
         A.row_hi = std::min<int64_t>(Np, r0 + B.chunk_rows);
@@ -963,8 +1034,7 @@ static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, bool cand, hip
         if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
         if (gemm) {
             const int64_t tiles = ((rows + CT - 1) / CT) * ((Np + CT - 1) / CT);
-            hipLaunchKernelGGL(cos_phase<STORE>, dim3((unsigned)(8 * ((tiles + 7) / 8))), dim3(kCosThreads), 0,
-                               stream, A);
+            launch_cos<STORE>(dim3((unsigned)(8 * ((tiles + 7) / 8))), stream, A);
         } else {
             const dim3 grid((unsigned)((Np + kStoreTile - 1) / kStoreTile),
                             (unsigned)((rows + kStoreTile - 1) / kStoreTile));
@@ -1002,7 +1072,9 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.cap = B.cap;
     A.idx_out = B.idx_out;
     A.raw_dot = B.raw_dot;
-    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024;
+    const int64_t span = feature_span(B);
+    A.f_bytes = 2 * span <= 0xFFFF0000ll ? (uint32_t)(2 * span) : 0u;
+    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024 && span < 0xFFFFFFFFll;
     A.all_rows_fallback = gemm ? 0 : 1;
     A.s = carve(B.scratch, B.g.Np, B.per_frame ? 0 : B.cap);
     const int64_t Np = B.g.Np;
@@ -1072,9 +1144,9 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
             if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
             if (mode == SEED)
-                hipLaunchKernelGGL(cos_phase<SEED>, grid, dim3(kCosThreads), 0, stream, A);
+                launch_cos<SEED>(grid, stream, A);
             else
-                hipLaunchKernelGGL(cos_phase<FILTER>, grid, dim3(kCosThreads), 0, stream, A);
+                launch_cos<FILTER>(grid, stream, A);
             if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
             // the compaction after every row has seen [0, W) sets the
             // symmetric pass's thresholds
@@ -1097,8 +1169,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             A.row_lo = W;
             A.row_hi = Np;
             if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
-            hipLaunchKernelGGL(cos_phase<SYM>, dim3((unsigned)(8 * ((tiles + 7) / 8))), dim3(kCosThreads), 0,
-                               stream, A);
+            launch_cos<SYM>(dim3((unsigned)(8 * ((tiles + 7) / 8))), stream, A);
             if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
             compact();
         }
@@ -1118,7 +1189,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
         for (int b = 0; b < kFixBatches; ++b) {
             L.row_lo = (int64_t)b * kFallbackBlocks;
             L.row_hi = L.row_lo + kFallbackBlocks;
-            hipLaunchKernelGGL(cos_phase<STORE>, dim3((unsigned)(8 * ((ct + 7) / 8))), dim3(kCosThreads), 0, stream, L);
+            launch_cos<STORE>(dim3((unsigned)(8 * ((ct + 7) / 8))), stream, L);
             hipLaunchKernelGGL(select_listed, dim3(kFallbackBlocks), dim3(1024), 0, stream, L, L.row_lo);
         }
     }
