@@ -35,23 +35,27 @@ PEAK_BF16_TFLOPS = 2500.0
 # FETCH_SIZE, then WRITE_SIZE, in separate runs; KiB per dispatch averaged per
 # kernel and summed over the step's 1 seed + 6 filtered + 1 symmetric launches).
 # Each counter is scaled by what it reads for a plain 1 GiB device copy in the
-# same run (FETCH_SIZE 524308.7 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
+# same run (FETCH_SIZE 524310.1 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
 # for the kernel source with this digest only; after any change the traffic is
 # reported as null until the counters are taken again.
 COSINE_GEMM_COUNTERS = {
+    "config": 3,  # the workload the counters were taken on (S = 100)
     "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-    "sha256": "8e4e285d1e868b31dd35990723ec6e99176240435e259b89af8d126c45e70925",
-    "fetch_kib_per_step": 800405.31 + 6 * 320407.89 + 34993488.23,
-    "write_kib_per_step": 2901377.13 + 6 * 67044.11 + 1566687.89,
-    "fetch_scale": 1048576.0 / 524308.66,
+    "sha256": "eaef8ab3c536e2afd820b3b2d0d2285464e4b18ad64c45b9705f3720c89b9edb",
+    "fetch_kib_per_step": 776094.08 + 6 * 320993.52 + 34923805.42,
+    "write_kib_per_step": 2901374.30 + 6 * 68384.84 + 1581383.84,
+    "fetch_scale": 1048576.0 / 524310.09,
     "write_scale": 1048576.0 / 1048576.0,
 }
 
 
-def counters_traffic_gb(rec):
-    """HBM bytes (GB) per step from the recorded counters, or None when the
-    kernel source no longer matches the one they were taken on."""
+def counters_traffic_gb(rec, config):
+    """HBM bytes (GB) per step from the recorded counters, or None for another
+    workload or when the kernel source no longer matches the one they were
+    taken on."""
     import hashlib
+    if config != rec["config"]:
+        return None
     try:
         with open(os.path.join(ROOT, rec["source"]), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
@@ -419,7 +423,7 @@ def main():
                                    launches=launch_counts.get("cosine_gemm", 0))
     dom = max(cand, key=lambda n: cand[n]["ms"])
     r = cand[dom]
-    traffic = counters_traffic_gb(COSINE_GEMM_COUNTERS) if dom == "cosine_gemm" else None
+    traffic = counters_traffic_gb(COSINE_GEMM_COUNTERS, args.config) if dom == "cosine_gemm" else None
     roofline = {"kernel": dom, "bound": r["bound"], "achieved": round(r["achieved"], 2), "peak": r["peak"],
                 "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4),
                 "traffic": round(traffic, 2) if traffic is not None else None,
