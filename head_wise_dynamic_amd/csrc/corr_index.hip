@@ -96,6 +96,7 @@ struct Args {
     int32_t tok_map;         // row u of F / Fc is token (u / P) T + ns + u % P (patches of a token layout)
     int32_t use_list;        // STORE: tile rows are positions in s.row_list (flagged rows)
     uint32_t f_bytes;        // bytes of F (and of Fc) that rows 0..Np-1 span; 0: over 0xFFFF0000
+    int32_t fallback_list_from;  // >= 0: the per-row engine takes s.row_list[from, row_count); -1: every row
 };
 
 // element offset of patch row u in F / Fc
@@ -910,7 +911,12 @@ template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(cons
     const Geom &g = A.g;
     float *row = A.s.rowbuf + (int64_t)blockIdx.x * g.Np;
     const T *F = (const T *)A.F, *Fc = (const T *)A.Fc;
-    for (int64_t u = blockIdx.x; u < g.Np; u += gridDim.x) {
+    // after the matrix-core recomputation only listed rows past its batches
+    // can still be flagged: walk that part of the list, not every row
+    const bool listed = A.fallback_list_from >= 0;
+    const int64_t n = listed ? (int64_t)*A.s.row_count : g.Np;
+    for (int64_t p = (listed ? A.fallback_list_from : 0) + blockIdx.x; p < n; p += gridDim.x) {
+        const int64_t u = listed ? (int64_t)A.s.row_list[p] : p;
         if (!A.s.over[u]) continue;
         __syncthreads();
         for (int c = threadIdx.x; c < A.Df; c += 1024) fu[c] = ldf<T>(F + frow(A, u), c);
@@ -1072,6 +1078,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.cap = B.cap;
     A.idx_out = B.idx_out;
     A.raw_dot = B.raw_dot;
+    A.fallback_list_from = -1;
     const int64_t span = feature_span(B);
     A.f_bytes = 2 * span <= 0xFFFF0000ll ? (uint32_t)(2 * span) : 0u;
     const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024 && span < 0xFFFFFFFFll;
@@ -1192,6 +1199,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             launch_cos<STORE>(dim3((unsigned)(8 * ((ct + 7) / 8))), stream, L);
             hipLaunchKernelGGL(select_listed, dim3(kFallbackBlocks), dim3(1024), 0, stream, L, L.row_lo);
         }
+        A.fallback_list_from = kFixBatches * kFallbackBlocks;
     }
     const unsigned fb = (unsigned)std::min<int64_t>(kFallbackBlocks, Np);
     if (B.dino_dtype == BF16)

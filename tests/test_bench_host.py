@@ -1,6 +1,6 @@
-"""Host logic of bench.py that needs no GPU: the recorded HBM counters are
-reported only for the workload and kernel source they were taken on."""
-import copy
+"""Host logic of bench.py that needs no GPU: recorded HBM counters are
+reported only for the workload and the kernel source they were taken on."""
+import hashlib
 import importlib.util
 import os
 
@@ -14,17 +14,21 @@ def _bench():
     return mod
 
 
-def test_traffic_only_for_recorded_workload_and_source():
+def test_traffic_only_for_recorded_workload_and_source(tmp_path):
     b = _bench()
-    rec = b.COSINE_GEMM_COUNTERS
+    src = tmp_path / "kernel.hip"
+    src.write_bytes(b"// some kernel source\n")
+    rec = dict(b.COSINE_GEMM_COUNTERS)
+    rec["source"] = str(src)  # absolute: os.path.join keeps it
+    rec["sha256"] = hashlib.sha256(src.read_bytes()).hexdigest()
     t = b.counters_traffic_gb(rec, rec["config"])
-    assert t is not None and t > 0
-    # the same figure from the record's own terms (KiB x calibration scale)
     want = (rec["fetch_kib_per_step"] * rec["fetch_scale"] + rec["write_kib_per_step"] * rec["write_scale"]) * 1024 / 1e9
-    assert abs(t - want) < 1e-9
+    assert t is not None and abs(t - want) < 1e-9
     # another workload: no figure
     assert b.counters_traffic_gb(rec, rec["config"] + 2) is None
-    # another kernel source: no figure
-    bad = copy.deepcopy(rec)
-    bad["sha256"] = "0" * 64
-    assert b.counters_traffic_gb(bad, rec["config"]) is None
+    # the source changed since: no figure
+    src.write_bytes(b"// edited\n")
+    assert b.counters_traffic_gb(rec, rec["config"]) is None
+    # the source is missing: no figure
+    rec["source"] = str(tmp_path / "missing.hip")
+    assert b.counters_traffic_gb(rec, rec["config"]) is None
