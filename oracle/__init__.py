@@ -20,7 +20,12 @@ assembles per-head key sets the way the pages describe them:
 * dense           -- every key (full global attention);
 * corr + stride   -- a patch query's correspondence keys united with the
   scanning set of a given stride (the combination the paper proposes for
-  scenes where DINO features miss regions); special queries attend to all.
+  scenes where DINO features miss regions); special queries attend to all;
+* broadcast       -- the static pattern that broadcasts the first frame's
+  local attention map to the other frames (Sec. 4.1 "Static Kernel", named
+  there as an example): a patch query attends, in every frame, to the patches
+  within a window around its own grid position, plus every special token;
+  special queries attend to all.
 
 Parity pins: see tests/test_oracle_pins.py.  Every function has at least one
 pin independent of its own code (brute force, closed form, printed values).
@@ -42,6 +47,10 @@ ROLE_POSITION, ROLE_VERTICAL, ROLE_CORRESPONDENCE, ROLE_SCANNING, ROLE_DENSE = 0
 # correspondence top-K united with the uniform stride set (Sec. 5, the second
 # direction named for the DINO Top-K kernel): budget = the stride
 ROLE_CORR_STRIDE = 5
+# static broadcast of a local window to every frame: budget = the window
+# radius r, anchor = the patch grid's width in patches (0: a window along the
+# patch index)
+ROLE_BROADCAST = 6
 MODE_TOTAL, MODE_PER_FRAME = 0, 1
 
 
@@ -124,6 +133,29 @@ def scan_set(S: int, ns: int, P: int, stride: int) -> np.ndarray:
     out = np.empty(n, dtype=np.int64)
     lib().oracle_scan_set(S, ns, P, stride, _p(out))
     return out
+
+
+def broadcast_set(S: int, ns: int, P: int, radius: int, grid_w: int, patch: int) -> np.ndarray:
+    """Keys of the patch query at position `patch` under the broadcast static
+    pattern (Sec. 4.1 "Static Kernel": the first frame's local attention map
+    broadcast to the other frames).  Reading: frame 0's local map lets patch p
+    see the patches near p; broadcast, every frame contributes its patches
+    near p, so the query meets the same spatial neighbourhood in every view.
+    Near = Chebyshev distance <= radius on a grid `grid_w` patches wide (rows
+    of grid_w patches, row-major), or |p' - p| <= radius along the patch index
+    when grid_w = 0.  Every special token is included, as in every static set.
+    Written as a filter over all patches, not as a window walk."""
+    T = ns + P
+    pp = np.arange(P)
+    if grid_w > 0:
+        y, x = divmod(patch, grid_w)
+        near = (np.abs(pp // grid_w - y) <= radius) & (np.abs(pp % grid_w - x) <= radius)
+    else:
+        near = np.abs(pp - patch) <= radius
+    frames = np.arange(S, dtype=np.int64)[:, None] * T
+    specials = (frames + np.arange(ns, dtype=np.int64)[None, :]).ravel()
+    patches = (frames + ns + pp[near][None, :]).ravel()
+    return np.union1d(specials, patches)
 
 
 def topk(scores: np.ndarray, K: int, ids: Optional[np.ndarray] = None):
@@ -393,6 +425,18 @@ def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int =
         elif role == ROLE_DENSE:
             sets = [np.arange(N, dtype=np.int64)]
             row_set = np.zeros(rows.size, dtype=np.int64)
+        elif role == ROLE_BROADCAST:
+            # special queries have no grid position: every key
+            sets = [np.arange(N, dtype=np.int64)]
+            row_set = np.zeros(rows.size, dtype=np.int64)
+            pos = rows % T - ns
+            seen = {}
+            for r_i in np.nonzero(~is_special)[0]:
+                p_ = int(pos[r_i])
+                if p_ not in seen:
+                    seen[p_] = len(sets)
+                    sets.append(broadcast_set(S, ns, P, budget, anchor, p_))
+                row_set[r_i] = seen[p_]
         else:
             raise ValueError(f"unknown role {role}")
         out[h] = (row_set, sets)

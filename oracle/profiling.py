@@ -19,8 +19,8 @@ from typing import Dict, List, Sequence, Tuple
 
 import numpy as np
 
-from . import (ROLE_CORRESPONDENCE, ROLE_DENSE, ROLE_POSITION, ROLE_SCANNING, ROLE_VERTICAL, MODE_TOTAL,
-               corr_index, layer)
+from . import (ROLE_BROADCAST, ROLE_CORRESPONDENCE, ROLE_DENSE, ROLE_POSITION, ROLE_SCANNING,
+               ROLE_VERTICAL, MODE_TOTAL, broadcast_set, corr_index, layer)
 
 Config = Tuple[int, int, int]   # (role, budget, anchor frame)
 
@@ -56,6 +56,9 @@ def head_pairs(geom, cfg: Config) -> int:
         return N * min(budget, N)
     if role == ROLE_CORRESPONDENCE:
         return S * P * min(budget, (S - 1) * P) + ns * S * N
+    if role == ROLE_BROADCAST:
+        # a patch query's set depends on its position only; special rows see all
+        return S * sum(broadcast_set(S, ns, P, budget, anchor, p).size for p in range(P)) + ns * S * N
     raise ValueError(f"unknown role {role}")
 
 

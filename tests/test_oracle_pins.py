@@ -479,3 +479,79 @@ def test_qk_index_on_unit_features_is_the_cosine_index():
     want, _, _ = oracle.corr_index(F, S, ns, P, 4, np.arange(S * P))
     got, _ = oracle.qk_index(q, q, S, ns, P, 4, np.arange(S * P))
     np.testing.assert_array_equal(got, want)
+
+
+# ---- static broadcast of a local window (Sec. 4.1 "Static Kernel")
+def _bcast_mask(geom, radius, grid_w):
+    """Brute force over token pairs: patch query (f, p) sees token (f', p') iff
+    p' is within `radius` of p on the grid (or along the patch index), in any
+    frame; every special token; special queries see everything."""
+    T, ns = geom.T, geom.ns
+    j = np.arange(geom.N)
+    t = j % T
+    sp = t < ns
+    p = t - ns
+    if grid_w > 0:
+        dy = np.abs(p[:, None] // grid_w - p[None, :] // grid_w)
+        dx = np.abs(p[:, None] % grid_w - p[None, :] % grid_w)
+        near = (dy <= radius) & (dx <= radius)
+    else:
+        near = np.abs(p[:, None] - p[None, :]) <= radius
+    return sp[:, None] | sp[None, :] | near
+
+
+@pytest.mark.parametrize("S,ns,P", [(3, 2, 12), (1, 0, 7), (4, 5, 20)])
+@pytest.mark.parametrize("grid_w", [0, 1, 4])
+def test_broadcast_radius_zero_is_the_same_position_in_every_frame(S, ns, P, grid_w):
+    if grid_w and P % grid_w:
+        pytest.skip("grid width must divide P")
+    T = ns + P
+    for p in range(P):
+        want = sorted([f * T + t for f in range(S) for t in range(ns)] + [f * T + ns + p for f in range(S)])
+        np.testing.assert_array_equal(oracle.broadcast_set(S, ns, P, 0, grid_w, p), want)
+
+
+def test_broadcast_window_sizes_closed_form():
+    S, ns, P, gw = 3, 2, 20, 5          # a 4 x 5 grid
+    size = lambda r, p, g=gw: oracle.broadcast_set(S, ns, P, r, g, p).size - ns * S
+    assert size(1, 0) == S * 4          # corner: 2 x 2
+    assert size(1, 2) == S * 6          # top edge: 2 x 3
+    assert size(1, 6) == S * 9          # interior: 3 x 3
+    assert size(2, 12) == S * 4 * 5     # rows 0..3, columns 0..4: the whole grid
+    assert size(0, 13) == S
+    assert size(2, 0, 0) == S * 3       # along the index: 0..2
+    assert size(2, 10, 0) == S * 5      # 8..12
+    assert size(3, 19, 0) == S * 4      # 16..19
+
+
+def test_broadcast_window_moves_with_the_query():
+    S, ns, P, gw = 2, 1, 30, 6          # a 5 x 6 grid
+    T = ns + P
+    a = oracle.broadcast_set(S, ns, P, 1, gw, 8)   # (1, 2)
+    b = oracle.broadcast_set(S, ns, P, 1, gw, 9)   # (1, 3): one column right
+    c = oracle.broadcast_set(S, ns, P, 1, gw, 14)  # (2, 2): one row down
+    pa, pb, pc = (x[x % T >= ns] for x in (a, b, c))
+    np.testing.assert_array_equal(pb, pa + 1)
+    np.testing.assert_array_equal(pc, pa + gw)
+
+
+@pytest.mark.parametrize("radius,grid_w", [(0, 0), (1, 4), (2, 0), (1, 5)])
+def test_layer_broadcast_heads_against_brute_force_mask(radius, grid_w):
+    geom = Geometry(S=3, ns=2, P=20)
+    w = make_geometry_inputs(geom, "f32", [oracle.ROLE_BROADCAST] * 16, [radius] * 16, M=80, Df=16,
+                             seed=31, anchors=[grid_w] * 16)
+    outs, _, _ = oracle.layer(geom, w.plan, w.q, w.k, w.v, heads=[0, 5])
+    mask = _bcast_mask(geom, radius, grid_w)
+    for h in (0, 5):
+        want = _masked_dense(w.q[h], w.k[h], w.v[h], mask)
+        np.testing.assert_allclose(outs[h], want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("radius,grid_w", [(4, 5), (19, 0)])
+def test_broadcast_covering_window_is_dense(radius, grid_w):
+    geom = Geometry(S=3, ns=5, P=20)
+    w = make_geometry_inputs(geom, "f32", [oracle.ROLE_BROADCAST] * 16, [radius] * 16, M=80, Df=16, seed=32,
+                             anchors=[grid_w] * 16)
+    outs, _, _ = oracle.layer(geom, w.plan, w.q, w.k, w.v, heads=[0])
+    want = _masked_dense(w.q[0], w.k[0], w.v[0], np.ones((geom.N, geom.N), dtype=bool))
+    np.testing.assert_allclose(outs[0], want, rtol=0, atol=1e-12)

@@ -30,7 +30,7 @@ def test_baseline_stride(sigma, stride):
 @pytest.mark.parametrize("cfg", [(ROLE_POSITION, 0, 0), (ROLE_POSITION, 0, 2), (ROLE_SCANNING, 3, 0),
                                  (ROLE_SCANNING, 7, 0), (ROLE_VERTICAL, 9, 0), (ROLE_VERTICAL, 10000, 0),
                                  (ROLE_CORRESPONDENCE, 5, 0), (ROLE_CORRESPONDENCE, 10000, 0),
-                                 (ROLE_DENSE, 0, 0)])
+                                 (ROLE_DENSE, 0, 0), (6, 0, 0), (6, 1, 5), (6, 2, 0), (6, 7, 5)])
 def test_head_pairs_count_the_actual_key_sets(cfg):
     geom = Geometry(S=3, ns=2, P=10)
     w = make_geometry_inputs(geom, "f32", [ROLE_DENSE] * 16, [0] * 16, M=40, Df=16, seed=4)

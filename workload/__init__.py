@@ -6,7 +6,7 @@ arithmetic (no key sets, no scores, no attention).
 """
 from .gen import (  # noqa: F401
     ROLE_POSITION, ROLE_VERTICAL, ROLE_CORRESPONDENCE, ROLE_SCANNING, ROLE_DENSE,
-    ROLE_NAMES, Geometry, Workload, CONFIGS, config, make_inputs, make_layer,
+    ROLE_CORR_STRIDE, ROLE_BROADCAST, ROLE_NAMES, Geometry, Workload, CONFIGS, config, make_inputs, make_layer,
     make_geometry_inputs, bf16_round, bf16_to_f32, sample_rows, make_front_loaded_dino,
     make_grouped_front_dino, layer_roles,
 )

@@ -42,7 +42,10 @@ ROLE_VERTICAL = 1
 ROLE_CORRESPONDENCE = 2
 ROLE_SCANNING = 3
 ROLE_DENSE = 4
-ROLE_NAMES = {0: "position", 1: "vertical", 2: "correspondence", 3: "scanning", 4: "dense"}
+ROLE_CORR_STRIDE = 5
+ROLE_BROADCAST = 6
+ROLE_NAMES = {0: "position", 1: "vertical", 2: "correspondence", 3: "scanning", 4: "dense", 5: "corr_stride",
+              6: "broadcast"}
 
 N_SALIENT = 24
 
