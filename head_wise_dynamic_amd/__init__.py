@@ -25,6 +25,7 @@ SAF_OK, SAF_EINVAL, SAF_ENOMEM, SAF_EHIP, SAF_EUNSUPPORTED, SAF_ESTATE = 0, -1, 
 SAF_F32, SAF_BF16 = 0, 1
 SAF_POSITION, SAF_VERTICAL, SAF_CORRESPONDENCE, SAF_SCANNING, SAF_DENSE = 0, 1, 2, 3, 4
 SAF_CORR_STRIDE = 5
+SAF_BROADCAST = 6
 SAF_CORR_TOTAL, SAF_CORR_PER_FRAME = 0, 1
 
 _STATUS_NAMES = {0: "SAF_OK", -1: "SAF_EINVAL", -2: "SAF_ENOMEM", -3: "SAF_EHIP",

@@ -139,7 +139,7 @@ saf_status_t check_tensors(saf_ctx_t *c, const void *q, const void *k, const voi
 }
 
 struct PlanInfo {
-    int nvert = 0, ncorr = 0, nunion = 0;
+    int nvert = 0, ncorr = 0, nunion = 0, nbcast = 0;
     int64_t vert_ws = 0;      // bytes for in-call vertical index builds
     int64_t split_ws = 0;     // bytes for dense-row split partials
     int64_t union_ws = 0;     // bytes for the records of correspondence + stride heads
@@ -200,15 +200,23 @@ saf_status_t check_plan(saf_ctx_t *c, const saf_head_plan_t *plan, PlanInfo *pi)
             break;
         case SAF_DENSE:
             break;
+        case SAF_BROADCAST:
+            if (p.budget < 0) return fail(c, SAF_EINVAL, "head %d: broadcast radius %d < 0", h, p.budget);
+            if (p.anchor_frame < 0 || (p.anchor_frame > 0 && g.P % p.anchor_frame != 0))
+                return fail(c, SAF_EINVAL, "head %d: grid width %d does not divide P = %d", h, p.anchor_frame, g.P);
+            ++pi->nbcast;
+            break;
         default:
             return fail(c, SAF_EINVAL, "head %d: unknown role %d", h, p.role);
         }
     }
     pi->vert_ws = (int64_t)pi->nvert * (int64_t)(align256(saf::vertical_ws_bytes(g.N)) +
                                                  align256(sizeof(int32_t) * g.N));
-    if (pi->ncorr && g.dtype == saf::BF16) {
+    // heads whose special-token rows attend to every key on the matrix cores
+    const int ndense_specials = pi->ncorr + pi->nbcast;
+    if (ndense_specials && g.dtype == saf::BF16) {
         pi->corr_splits = corr_special_splits(g);
-        if (pi->corr_splits > 1) pi->split_ws = (int64_t)pi->ncorr * split_part_bytes(g, pi->corr_splits);
+        if (pi->corr_splits > 1) pi->split_ws = (int64_t)ndense_specials * split_part_bytes(g, pi->corr_splits);
         pi->union_ws = (int64_t)pi->nunion * union_rec_bytes(g);
     }
     return SAF_OK;
@@ -624,7 +632,7 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
                 w = saf::HeadWork{};
                 w.head = h;
                 w.role = plan[h].role;
-                w.budget = plan[h].budget;
+                w.budget = plan[h].role == SAF_BROADCAST ? std::min(plan[h].budget, g.P) : plan[h].budget;
                 w.anchor = plan[h].anchor_frame;
                 w.list = vlist[h];
                 w.list_len = plan[h].role == SAF_VERTICAL ? (int32_t)std::min<int64_t>(plan[h].budget, g.N) : 0;
@@ -790,6 +798,27 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
             it.tiles = ((int64_t)g.ns * g.S + QT - 1) / QT;
             it.cost = (double)g.N / w.nsplit;
             break;
+        case SAF_BROADCAST: {
+            // patch rows grouped by patch position: one key set per position
+            w.budget = std::min(plan[h].budget, g.P);
+            w.rows = saf::ROWS_BY_POSITION;
+            it.tiles = (int64_t)g.P * ((g.S + QT - 1) / QT);
+            const int64_t gw = plan[h].anchor_frame > 0 ? plan[h].anchor_frame : g.P, gh = g.P / gw;
+            const int64_t side = 2 * (int64_t)w.budget + 1;
+            it.cost = (double)g.ns * g.S + (double)g.S * std::min(side, gw) * std::min(side, gh);
+            if (g.ns > 0) {  // special-token rows attend to every key
+                saf::HeadWork sw = w;
+                sw.role = saf::DENSE;
+                sw.rows = saf::ROWS_SPECIALS;
+                sw.nsplit = pi.corr_splits;
+                Item si{};
+                si.w = sw;
+                si.tiles = ((int64_t)g.ns * g.S + QT - 1) / QT;
+                si.cost = (double)g.N / sw.nsplit;
+                items.push_back(si);
+            }
+            break;
+        }
         }
         it.w = w;
         items.push_back(it);
@@ -1030,6 +1059,23 @@ saf_status_t saf_head_pairs(const saf_ctx_t *cc, const saf_head_plan_t *head, in
         if (head->budget < 1) return fail(c, SAF_EINVAL, "K %d < 1", head->budget);
         *pairs = N * std::min<int64_t>(head->budget, N);
         return SAF_OK;
+    case SAF_BROADCAST: {
+        const int64_t r = head->budget, gw = head->anchor_frame > 0 ? head->anchor_frame : P;
+        if (r < 0) return fail(c, SAF_EINVAL, "radius %lld < 0", (long long)r);
+        if (head->anchor_frame < 0 || P % gw != 0)
+            return fail(c, SAF_EINVAL, "grid width %d does not divide P", head->anchor_frame);
+        // a patch row sees the specials and, in every frame, its window;
+        // special rows attend to every key
+        const int64_t gh = P / gw;
+        int64_t win = 0;
+        for (int64_t p = 0; p < P; ++p) {
+            const int64_t y = p / gw, x = p % gw;
+            win += (std::min(gh - 1, y + r) - std::max<int64_t>(0, y - r) + 1) *
+                   (std::min(gw - 1, x + r) - std::max<int64_t>(0, x - r) + 1);
+        }
+        *pairs = S * (P * ns * S + S * win) + ns * S * N;
+        return SAF_OK;
+    }
     case SAF_CORRESPONDENCE: {
         const int64_t kc = corr_kc > 0 ? corr_kc : c->corr_k;
         if (kc < 1) return fail(c, SAF_ESTATE, "no index row length given and no cached index");

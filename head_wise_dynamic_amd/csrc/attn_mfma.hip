@@ -35,9 +35,10 @@ __device__ __forceinline__ int swap_bits23(int m) {
 
 struct RowMap {
     int32_t valid;     // rows in this tile
-    int32_t qframe;    // query frame (position heads)
+    int32_t qsel;      // key-set selector: query frame (position), patch position (broadcast)
     int64_t row0;      // first row (FRAME/ALL)
     int32_t specials;  // row index m -> (m/ns)*T + m%ns
+    int32_t by_pos;    // row index m -> m*T + ns + qsel (frames of one patch position)
     int32_t m0;
 };
 
@@ -46,6 +47,7 @@ __device__ __forceinline__ int64_t tile_row(const RowMap &rm, const Geom &g, int
         const int m = rm.m0 + r;
         return (int64_t)(m / g.ns) * g.T + (m % g.ns);
     }
+    if (rm.by_pos) return (int64_t)(rm.m0 + r) * g.T + g.ns + rm.qsel;
     return rm.row0 + r;
 }
 
@@ -54,9 +56,15 @@ __device__ __forceinline__ RowMap make_rowmap(const HeadWork &w, const Geom &g, 
     if (w.rows == ROWS_FRAME) {
         const int tpf = (g.T + QT - 1) / QT;
         const int f = tile / tpf, t0 = (tile % tpf) * QT;
-        rm.qframe = f;
+        rm.qsel = f;
         rm.row0 = (int64_t)f * g.T + t0;
         rm.valid = min(QT, g.T - t0);
+    } else if (w.rows == ROWS_BY_POSITION) {
+        const int tps = (g.S + QT - 1) / QT;
+        rm.by_pos = 1;
+        rm.qsel = tile / tps;
+        rm.m0 = (tile % tps) * QT;
+        rm.valid = min(QT, g.S - rm.m0);
     } else if (w.rows == ROWS_ALL) {
         rm.row0 = (int64_t)tile * QT;
         rm.valid = (int)min<int64_t>(QT, g.N - rm.row0);
@@ -96,7 +104,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const uint16_t *K = (const uint16_t *)L.k + hoff;
     const uint16_t *V = (const uint16_t *)L.v + hoff;
 
-    const int64_t count = key_count(w, g, rm.qframe);
+    const int64_t count = key_count(w, g, rm.qsel);
     const int64_t per = ((count + w.nsplit - 1) / w.nsplit + KT - 1) / KT * KT;
     const int64_t kbeg = (int64_t)split * per;
     const int64_t kend = min<int64_t>(count, kbeg + per);
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
             for (int i = 0; i < 2; ++i) {
                 const int64_t m = kt + 2 * lp + i;
                 int64_t tok = -1;
-                if (m < kend) tok = key_token(w, g, m, rm.qframe);
+                if (m < kend) tok = key_token(w, g, m, rm.qsel);
                 kval[j][i] = tok >= 0;
                 if (tok >= 0) {
                     kreg[j][i] = *(const u32x4 *)(K + tok * ts + 8 * lseg);

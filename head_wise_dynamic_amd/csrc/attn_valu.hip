@@ -71,7 +71,7 @@ __device__ void row_init(const ValuLaunch &L, const HeadWork &w, int64_t qtok, i
 // else the m-th key of w's key set.  skip > 0 drops listed keys on that
 // stride (they are counted by another key list of the same row).
 template <typename T>
-__device__ void row_accumulate(const ValuLaunch &L, const HeadWork &w, int32_t qframe, const int32_t *idx_row,
+__device__ void row_accumulate(const ValuLaunch &L, const HeadWork &w, int32_t qsel, const int32_t *idx_row,
                                int64_t count, int64_t skip, int lane, RowAcc<T> &a) {
     using E = Lanes<T>;
     constexpr int EPL = E::EPL, LPR = E::LPR, RPP = E::RPP, CH = NP * RPP;
@@ -89,7 +89,14 @@ __device__ void row_accumulate(const ValuLaunch &L, const HeadWork &w, int32_t q
         for (int p = 0; p < NP; ++p) {
             const int64_t m = c0 + p * RPP + grp;
             tok[p] = -1;
-            if (m < count) tok[p] = idx_row ? (int64_t)idx_row[m] : key_token(w, g, m, qframe);
+            if (m < count) {
+                if (idx_row)
+                    tok[p] = (int64_t)idx_row[m];
+                else if constexpr (sizeof(T) == 4)
+                    tok[p] = key_token(w, g, m, qsel);
+                else
+                    tok[p] = m;  // bf16 rows gather listed keys only (checked at launch)
+            }
             if (skip > 0 && tok[p] >= 0 && tok[p] % skip == 0) tok[p] = -1;
         }
         float kx[NP][EPL];
@@ -201,6 +208,7 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(const ValuLaunch L, int6
         HeadWork kw = w;
         const int32_t *idx_row = nullptr, *second = nullptr;
         int64_t count = 0, skip = 0;
+        int32_t qsel = qframe;
         bool record = false;
         if (w.role == CORRESPONDENCE || w.role == CORR_STRIDE) {
             if (u < 0) {  // special-token query: every key
@@ -220,11 +228,19 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(const ValuLaunch L, int6
                 count = key_count(kw, g, qframe);
                 second = L.corr_idx + u * L.corr_k;
             }
+        } else if (w.role == BROADCAST) {
+            if (u < 0) {  // special-token query: every key
+                kw.role = DENSE;
+                count = g.N;
+            } else {
+                qsel = (int32_t)(tok % g.T) - g.ns;  // the query's patch position
+                count = key_count(w, g, qsel);
+            }
         } else {
             count = key_count(w, g, qframe);
         }
         for (int ph = 0; ph < 2; ++ph) {
-            row_accumulate<T>(L, kw, qframe, idx_row, count, skip, lane, acc);
+            row_accumulate<T>(L, kw, qsel, idx_row, count, skip, lane, acc);
             if (!second) break;
             kw = w;
             idx_row = second;
@@ -264,6 +280,14 @@ __global__ __launch_bounds__(256) void union_merge_kernel(const UnionMerge U) {
 
 hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t stream) {
     if (nrows <= 0 || L.nwork <= 0) return hipSuccess;
+    // bf16: the row kernel gathers the correspondence keys of patch rows; the
+    // static key sets of the other roles run on the matrix cores
+    if (L.g.dtype == BF16) {
+        if (!L.patch_rows_only) return hipErrorInvalidValue;
+        for (int i = 0; i < L.nwork; ++i)
+            if (!(L.work[i].role == CORRESPONDENCE || (L.work[i].role == CORR_STRIDE && L.work[i].rec_out)))
+                return hipErrorInvalidValue;
+    }
     const dim3 grid((unsigned)((nrows + 3) / 4));
     if (L.g.dtype == BF16)
         hipLaunchKernelGGL(valu_attn_kernel<uint16_t>, grid, dim3(256), 0, stream, L, nrows);

@@ -37,10 +37,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // smallest normal may flush, which only affects weights < 2^-126).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Window of a broadcast head around patch position p: patches
+// (y0 + j / wx) * gw + x0 + j % wx for j < n.  gw = 0 is a single row of P
+// patches (a window along the patch index).
+struct BcastWindow {
+    int32_t y0, x0, wx, n, gw;
+};
+__device__ __forceinline__ BcastWindow bcast_window(const HeadWork &w, const Geom &g, int32_t p) {
+    const int32_t r = w.budget, gw = w.anchor > 0 ? w.anchor : g.P, gh = g.P / gw;
+    const int32_t y = p / gw, x = p % gw;
+    BcastWindow b;
+    b.gw = gw;
+    b.y0 = max(0, y - r);
+    b.x0 = max(0, x - r);
+    b.wx = min(gw - 1, x + r) - b.x0 + 1;
+    b.n = (min(gh - 1, y + r) - b.y0 + 1) * b.wx;
+    return b;
+}
+
 // Token index of the m-th key of a head's key set (see HeadWork); -1 marks a
-// masked slot (a special token already on the scanning stride).
+// masked slot (a special token already on the scanning stride).  qsel selects
+// the query's set: its frame for POSITION, its patch position for BROADCAST.
 __device__ __forceinline__ int64_t key_token(const HeadWork &w, const Geom &g, int64_t m,
-                                             int32_t qframe) {
+                                             int32_t qsel) {
     switch (w.role) {
     case POSITION: {
         const int64_t nsS = (int64_t)g.ns * g.S;
@@ -48,7 +67,7 @@ __device__ __forceinline__ int64_t key_token(const HeadWork &w, const Geom &g, i
         m -= nsS;
         if (m < g.P) return (int64_t)w.anchor * g.T + g.ns + m;
         m -= g.P;
-        return (int64_t)qframe * g.T + g.ns + m;
+        return (int64_t)qsel * g.T + g.ns + m;
     }
     case SCANNING: {
         const int64_t s = w.budget;
@@ -60,19 +79,29 @@ __device__ __forceinline__ int64_t key_token(const HeadWork &w, const Geom &g, i
     }
     case VERTICAL:
         return w.list[m];
+    case BROADCAST: {
+        const int64_t nsS = (int64_t)g.ns * g.S;
+        if (m < nsS) return (m / g.ns) * g.T + (m % g.ns);
+        m -= nsS;
+        const BcastWindow b = bcast_window(w, g, qsel);
+        const int32_t f = (int32_t)(m / b.n), j = (int32_t)(m % b.n);
+        return (int64_t)f * g.T + g.ns + (int64_t)(b.y0 + j / b.wx) * b.gw + b.x0 + j % b.wx;
+    }
     default:
         return m;
     }
 }
 
-__device__ __forceinline__ int64_t key_count(const HeadWork &w, const Geom &g, int32_t qframe) {
+__device__ __forceinline__ int64_t key_count(const HeadWork &w, const Geom &g, int32_t qsel) {
     switch (w.role) {
     case POSITION:
-        return (int64_t)g.ns * g.S + g.P + (qframe != w.anchor ? g.P : 0);
+        return (int64_t)g.ns * g.S + g.P + (qsel != w.anchor ? g.P : 0);
     case SCANNING:
         return (g.N + w.budget - 1) / w.budget + (int64_t)g.ns * g.S;
     case VERTICAL:
         return w.list_len;
+    case BROADCAST:
+        return (int64_t)g.ns * g.S + (int64_t)g.S * bcast_window(w, g, qsel).n;
     default:
         return g.N;
     }

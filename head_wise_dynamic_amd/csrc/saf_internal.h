@@ -7,7 +7,9 @@
 
 namespace saf {
 
-enum Role : int32_t { POSITION = 0, VERTICAL = 1, CORRESPONDENCE = 2, SCANNING = 3, DENSE = 4, CORR_STRIDE = 5 };
+enum Role : int32_t {
+    POSITION = 0, VERTICAL = 1, CORRESPONDENCE = 2, SCANNING = 3, DENSE = 4, CORR_STRIDE = 5, BROADCAST = 6
+};
 enum Dtype : int32_t { F32 = 0, BF16 = 1 };
 
 // Geometry with derived sizes.  Token j = f * T + t; special iff t < ns.
@@ -22,7 +24,10 @@ struct Geom {
 //               set depends on the query frame, so tiles never cross frames)
 //   ALL      -- rows 0 .. N-1
 //   SPECIALS -- the ns*S special-token rows, m -> (m / ns) * T + m % ns
-enum RowSpace : int32_t { ROWS_FRAME = 0, ROWS_ALL = 1, ROWS_SPECIALS = 2 };
+//   BY_POSITION -- patch rows grouped by patch position: ceil(S / 256) tiles
+//               per position p, tile rows = frames, row f -> f*T + ns + p
+//               (broadcast heads: the key set depends on p only)
+enum RowSpace : int32_t { ROWS_FRAME = 0, ROWS_ALL = 1, ROWS_SPECIALS = 2, ROWS_BY_POSITION = 3 };
 
 // One head's key-set description as the attention kernels see it.
 //   POSITION: specials (ns*S) ++ anchor-frame patches (P) ++ own-frame
@@ -30,7 +35,11 @@ enum RowSpace : int32_t { ROWS_FRAME = 0, ROWS_ALL = 1, ROWS_SPECIALS = 2 };
 //   SCANNING: tokens m*stride for m < ceil(N/stride) ++ specials, where a
 //             special that already lies on the stride is a masked slot
 //   VERTICAL: list[0 .. list_len)
-//   DENSE:    every token (also the special rows of correspondence heads)
+//   DENSE:    every token (also the special rows of correspondence and
+//             broadcast heads)
+//   BROADCAST: specials (ns*S) ++ for every frame, the patches of the window
+//             of radius budget around the query's patch position, row-major
+//             over a grid anchor patches wide (anchor = 0: one row of P)
 struct HeadWork {
     int32_t head;       // head index (pointer offsets)
     int32_t role;       // key-set rule, see above

@@ -31,6 +31,16 @@
  *                      paper names, in its analysis of the DINO Top-K kernel,
  *                      to cover regions DINO features miss); special queries
  *                      attend to every key.
+ *   SAF_BROADCAST      static set that broadcasts the first frame's local
+ *                      attention map to the other frames (Sec. 4.1 "Static
+ *                      Kernel", given there as an example): a patch query at
+ *                      grid position (y, x) attends, in every frame, to the
+ *                      patches (y', x') with |y' - y| <= r and |x' - x| <= r,
+ *                      plus every special token.  r = `budget`; the grid is
+ *                      `anchor_frame` patches wide (rows of that many patches,
+ *                      row-major), or, with anchor_frame = 0, one row of P
+ *                      patches (a window along the patch index).  Special
+ *                      queries attend to every key.
  *
  * Token layout: frame f holds T = ns + P tokens, the ns special tokens
  * (camera, registers) first, then P patch tokens; token j = f * T + t.  Patch
@@ -82,7 +92,8 @@ typedef enum {
     SAF_CORRESPONDENCE = 2,
     SAF_SCANNING = 3,
     SAF_DENSE = 4,
-    SAF_CORR_STRIDE = 5
+    SAF_CORR_STRIDE = 5,
+    SAF_BROADCAST = 6
 } saf_role_t;
 
 /* Correspondence top-K per query: over all other frames together, or K per
@@ -108,8 +119,10 @@ typedef struct {
     int32_t budget;        /* VERTICAL: K >= 1 (clamped to N); SCANNING: stride >= 1;
                               CORRESPONDENCE: 0, the cached index's row length Kc
                               or the K requested when it was built (before
-                              clamping); CORR_STRIDE: stride >= 1; others: 0 */
-    int32_t anchor_frame;  /* POSITION: anchor frame in [0, S); others ignored */
+                              clamping); CORR_STRIDE: stride >= 1; BROADCAST:
+                              window radius r >= 0; others: 0 */
+    int32_t anchor_frame;  /* POSITION: anchor frame in [0, S); BROADCAST: patch
+                              grid width, a divisor of P, or 0; others ignored */
     int32_t flags;         /* must be 0 */
 } saf_head_plan_t;
 
@@ -257,8 +270,9 @@ saf_status_t saf_head_nmse(saf_ctx_t *ctx, const void *o_full, const void *o_spa
 /* Query-key pairs one head computes under *head at this geometry (its
  * floating-point work, the cost of Eq. 2, is 4 head_dim per pair).  For a
  * correspondence head corr_kc is the index row length (<= 0: the cached
- * index's).  Host only.  Errors: SAF_EINVAL (bad role/budget/anchor),
- * SAF_ESTATE (correspondence with no row length). */
+ * index's).  Host only.  Errors: SAF_EINVAL (bad role/budget/anchor, a
+ * broadcast grid width that does not divide P), SAF_ESTATE (correspondence
+ * with no row length). */
 saf_status_t saf_head_pairs(const saf_ctx_t *ctx, const saf_head_plan_t *head, int32_t corr_kc,
                             int64_t *pairs);
 

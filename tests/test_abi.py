@@ -69,6 +69,9 @@ def _call(c, plan, ws_bytes=1 << 30, lay=LAY, q=FAKE, o=FAKE, ws=FAKE):
     ((3, 0, 0, 0), saf.SAF_EINVAL),          # stride < 1
     ((0, 0, 4, 0), saf.SAF_EINVAL),          # anchor outside [0, S)
     ((0, 0, -1, 0), saf.SAF_EINVAL),
+    ((6, -1, 0, 0), saf.SAF_EINVAL),         # broadcast radius < 0
+    ((6, 1, 3, 0), saf.SAF_EINVAL),          # broadcast grid width not dividing P = 256
+    ((6, 1, -16, 0), saf.SAF_EINVAL),
     ((0, 0, 0, 1), saf.SAF_EUNSUPPORTED),    # flags
     ((2, 0, 0, 0), saf.SAF_ESTATE),          # correspondence head, no index yet
 ])

@@ -25,6 +25,10 @@ def test_head_pairs_match_oracle(S, ns, P):
         cfgs = [(saf.SAF_DENSE, 0, 0), (saf.SAF_POSITION, 0, 0), (saf.SAF_POSITION, 0, S - 1),
                 (saf.SAF_VERTICAL, 64, 0), (saf.SAF_VERTICAL, 10 ** 9, 0), (saf.SAF_CORRESPONDENCE, 32, 0),
                 (saf.SAF_CORRESPONDENCE, 10 ** 9, 0)] + [(saf.SAF_SCANNING, s, 0) for s in (1, 2, 3, 7, 16, 33)]
+        gw = {10: 5, 256: 16, 1369: 37, 1296: 36, 7: 7}[P]   # the patch grid's width
+        cfgs += [(saf.SAF_BROADCAST, 0, 0), (saf.SAF_BROADCAST, 1, gw), (saf.SAF_BROADCAST, 2, 0)]
+        if P <= 256:
+            cfgs += [(saf.SAF_BROADCAST, P, gw), (saf.SAF_BROADCAST, 3, 1)]
         for role, budget, anchor in cfgs:
             n = C.c_int64()
             h = saf.saf_head_plan_t(role, budget, anchor, 0)
@@ -33,6 +37,12 @@ def test_head_pairs_match_oracle(S, ns, P):
         n = C.c_int64()
         bad = saf.saf_head_plan_t(saf.SAF_POSITION, 0, S, 0)
         assert saf.saf_head_pairs(c, C.byref(bad), 0, C.byref(n)) == saf.SAF_EINVAL
+        for bad_b in (saf.saf_head_plan_t(saf.SAF_BROADCAST, -1, 0, 0),
+                      saf.saf_head_plan_t(saf.SAF_BROADCAST, 1, -2, 0)):
+            assert saf.saf_head_pairs(c, C.byref(bad_b), 0, C.byref(n)) == saf.SAF_EINVAL
+        if P % 3:
+            b3 = saf.saf_head_plan_t(saf.SAF_BROADCAST, 1, 3, 0)   # grid width not dividing P
+            assert saf.saf_head_pairs(c, C.byref(b3), 0, C.byref(n)) == saf.SAF_EINVAL
         corr = saf.saf_head_plan_t(saf.SAF_CORRESPONDENCE, 0, 0, 0)
         assert saf.saf_head_pairs(c, C.byref(corr), 0, C.byref(n)) == saf.SAF_ESTATE    # no cached index
     finally:
