@@ -35,16 +35,16 @@ PEAK_BF16_TFLOPS = 2500.0
 # FETCH_SIZE, then WRITE_SIZE, in separate runs; KiB per dispatch averaged per
 # kernel and summed over the step's 1 seed + 6 filtered + 1 symmetric launches).
 # Each counter is scaled by what it reads for a plain 1 GiB device copy in the
-# same run (FETCH_SIZE 524310.1 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
+# same run (FETCH_SIZE 524309.3 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
 # for the kernel source with this digest only; after any change the traffic is
 # reported as null until the counters are taken again.
 COSINE_GEMM_COUNTERS = {
     "config": 3,  # the workload the counters were taken on (S = 100)
     "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-    "sha256": "eaef8ab3c536e2afd820b3b2d0d2285464e4b18ad64c45b9705f3720c89b9edb",
-    "fetch_kib_per_step": 776094.08 + 6 * 320993.52 + 34923805.42,
-    "write_kib_per_step": 2901374.30 + 6 * 68384.84 + 1581383.84,
-    "fetch_scale": 1048576.0 / 524310.09,
+    "sha256": "74e85a25aaaeeec6baade8eb7e3743b52ab5e544c1b0ea23bd0bddcef6938c4d",
+    "fetch_kib_per_step": 773886.32 + 6 * 321123.70 + 34966340.71,
+    "write_kib_per_step": 2901373.47 + 6 * 68375.71 + 1575411.84,
+    "fetch_scale": 1048576.0 / 524309.34,
     "write_scale": 1048576.0 / 1048576.0,
 }
 
@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--block-k", type=int, default=7, help="blocks kept per query block for --block")
     ap.add_argument("--corr-stride", type=int, default=64,
                     help="also time the layer with its correspondence heads united with this stride (0: skip)")
+    ap.add_argument("--broadcast-radius", type=int, default=1,
+                    help="also time the layer with its position heads as broadcast heads of this window "
+                         "radius on the patch grid (-1: skip)")
     ap.add_argument("--no-qk-index", action="store_true",
                     help="skip timing the index built from the first correspondence head's logits")
     ap.add_argument("--no-stack", action="store_true",
@@ -340,6 +343,28 @@ def main():
             ct.append(e0.elapsed_time(e1))
         corr_stride = {"stride": args.corr_stride, "attn_only_ms": round(statistics.median(ct), 4)}
 
+    # the layer with its position heads as broadcast heads (the local window
+    # of every frame around the query's grid position); not part of the step
+    broadcast = None
+    if args.broadcast_radius >= 0:
+        gw = math.isqrt(g.P) if math.isqrt(g.P) ** 2 == g.P else 0
+        bplan = [(6, args.broadcast_radius, gw, f) if r == 0 else (r, b, a, f) for (r, b, a, f) in w.plan]
+        ctx.sparse_attention(bplan, q, k, v, o=o)
+        torch.cuda.synchronize()
+        bt = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            ctx.sparse_attention(bplan, q, k, v, o=o)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            bt.append(e0.elapsed_time(e1))
+        side = 2 * args.broadcast_radius + 1
+        broadcast = {"radius": args.broadcast_radius, "grid_width": gw,
+                     "heads": sum(1 for p in w.plan if p[0] == 0),
+                     "keys_per_interior_patch_query": g.ns * g.S + g.S * (side * side if gw else side),
+                     "attn_only_ms": round(statistics.median(bt), 4)}
+
     # block-wise index (blocks of --block patches, --block-k blocks per query
     # block) and the layer on it, in a context of its own; not part of the step
     block = None
@@ -472,6 +497,7 @@ def main():
         "per_frame_index": per_frame,
         "block_index": block,
         "corr_stride_layer": corr_stride,
+        "broadcast_layer": broadcast,
         "qk_index": qk,
         "offline_profiling": prof,
         "sparsity": round(1.0 - (shared_pairs + gather_pairs) / (g.H * g.N * g.N), 4),
