@@ -633,18 +633,29 @@ __global__ __launch_bounds__(256) void compact_rows(const Args A) {
                 if (R.kept(e, lane)) buf[pos++] = make_float2(R.sc[e], __int_as_float(R.id[e]));
             break;
         }
-        // in-place ordered filter: the write position never passes the read one
+        // in-place ordered filter: the write position never passes the read
+        // one.  Four 64-entry chunks are loaded before any is written back (all
+        // four are then held in registers, and writes land below the next
+        // group), so four loads are in flight instead of one.
         const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         uint32_t pos = 0;
-        for (uint32_t i0 = 0; i0 < total; i0 += 64) {
-            const uint32_t i = i0 + lane;
-            float2 x = make_float2(-INFINITY, 0.f);
-            if (i < total) x = buf[i];
-            const bool keep = i < total && order_key(x.x) >= thr;
-            const uint64_t m = __ballot(keep);
+        constexpr int kChunks = 4;
+        for (uint32_t i0 = 0; i0 < total; i0 += 64 * kChunks) {
+            float2 x[kChunks];
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) {
+                const uint32_t i = i0 + 64 * c + lane;
+                x[c] = i < total ? buf[i] : make_float2(-INFINITY, 0.f);
+            }
             __builtin_amdgcn_wave_barrier();
-            if (keep) buf[pos + (uint32_t)__popcll(m & below)] = x;
-            pos += (uint32_t)__popcll(m);
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) {
+                const uint32_t i = i0 + 64 * c + lane;
+                const bool keep = i < total && order_key(x[c].x) >= thr;
+                const uint64_t m = __ballot(keep);
+                if (keep) buf[pos + (uint32_t)__popcll(m & below)] = x[c];
+                pos += (uint32_t)__popcll(m);
+            }
         }
         total = pos;
     }
