@@ -709,15 +709,33 @@ __global__ __launch_bounds__(256) void finalize_rows(const Args A, uint32_t lo_c
 #pragma unroll
     for (int e = 0; e < MAXE; ++e)
         if (R.kept(e, lane)) s[pos++] = R.id[e];
+    // ascending order: bitonic sort of the K ids padded to a power of two
+    // (K <= 1024) with a sentinel above every id, in the wave's LDS slice
+    int n = 1;
+    while (n < A.K) n <<= 1;
+    for (int i = A.K + lane; i < n; i += 64) s[i] = INT32_MAX;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    for (int k = 2; k <= n; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = lane; i < n; i += 64) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const int32_t a = s[i], b = s[l];
+                    if ((a > b) == ((i & k) == 0)) {
+                        s[i] = b;
+                        s[l] = a;
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        }
     int32_t *out = A.idx_out + u * A.K;
     const Geom &g = A.g;
     for (int i = lane; i < A.K; i += 64) {
         const int32_t v = s[i];
-        int rank = 0;
-        for (int j = 0; j < A.K; ++j) rank += s[j] < v ? 1 : 0;
-        out[rank] = (int32_t)((v / g.P) * g.T + g.ns + (v % g.P));
+        out[i] = (int32_t)((v / g.P) * g.T + g.ns + (v % g.P));
     }
 }
 
