@@ -391,13 +391,16 @@ def main():
         bctx.close()
 
     # one offline-profiling pass (Sec. 4.2) with this sequence as the single
-    # calibration sample: dense reference, baseline at sigma = 0.85 and seven
-    # candidates, per-head errors and the selection; not part of the step
+    # calibration sample: dense reference, baseline at sigma = 0.85 and eight
+    # candidates (the broadcast one on the patch grid), per-head errors and the
+    # selection; not part of the step
     prof = None
     if not args.no_profile:
         from head_wise_dynamic_amd import profiling
         pctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
-        cands = [(1, 1024, 0), (1, 2048, 0), (1, 4096, 0), (2, 128, 0), (2, 256, 0), (0, 0, 0), (3, 16, 0)]
+        grid_w = math.isqrt(g.P) if math.isqrt(g.P) ** 2 == g.P else 0
+        cands = [(1, 1024, 0), (1, 2048, 0), (1, 4096, 0), (2, 128, 0), (2, 256, 0), (0, 0, 0), (3, 16, 0),
+                 (6, 1, grid_w)]
         smp = dict(q=q, k=k, v=v, dino=dino)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -413,7 +416,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         nmse_ms = e0.elapsed_time(e1)
-        names = {0: "position", 1: "vertical", 2: "correspondence", 3: "scanning", 4: "dense"}
+        names = {0: "position", 1: "vertical", 2: "correspondence", 3: "scanning", 4: "dense", 6: "broadcast"}
         prof = {"sigma": 0.85, "configs": [f"{names[r]}:{b}" for r, b, _ in res["configs"]],
                 "choice_per_head": [int(c) for c in res["choice"]], "wall_ms": round(t_prof * 1e3, 1),
                 "error_kernel_ms": round(nmse_ms, 4),

@@ -106,7 +106,8 @@ def test_profile_generated_workload_matches_oracle():
     ws = [make_geometry_inputs(geom, "f32", roles, [0, 0, 0, 0, 24, 24, 24, 24, 8, 8, 8, 8, 4, 4, 4, 4],
                                M=120, Df=32, seed=s) for s in (11, 12)]
     cands = [(ROLE_VERTICAL, 24, 0), (ROLE_VERTICAL, 48, 0), (ROLE_CORRESPONDENCE, 8, 0),
-             (ROLE_CORRESPONDENCE, 16, 0), (ROLE_POSITION, 0, 0), (ROLE_SCANNING, 8, 0)]
+             (ROLE_CORRESPONDENCE, 16, 0), (ROLE_POSITION, 0, 0), (ROLE_SCANNING, 8, 0),
+             (oracle.ROLE_BROADCAST, 1, 8), (oracle.ROLE_BROADCAST, 0, 0)]   # P = 40: a 5 x 8 grid
     ctx = saf.Context(geom.S, geom.ns, geom.P, geom.H, geom.d, torch.float32)
     say("profile generated workload, 2 samples")
     smps = [dict(q=to_dev(w.q), k=to_dev(w.k), v=to_dev(w.v), dino=to_dev(w.dino)) for w in ws]
