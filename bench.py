@@ -35,16 +35,16 @@ PEAK_BF16_TFLOPS = 2500.0
 # FETCH_SIZE, then WRITE_SIZE, in separate runs; KiB per dispatch averaged per
 # kernel and summed over the step's 1 seed + 6 filtered + 1 symmetric launches).
 # Each counter is scaled by what it reads for a plain 1 GiB device copy in the
-# same run (FETCH_SIZE 524309.3 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
+# same run (FETCH_SIZE 524309.0 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
 # for the kernel source with this digest only; after any change the traffic is
 # reported as null until the counters are taken again.
 COSINE_GEMM_COUNTERS = {
     "config": 3,  # the workload the counters were taken on (S = 100)
     "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-    "sha256": "74e85a25aaaeeec6baade8eb7e3743b52ab5e544c1b0ea23bd0bddcef6938c4d",
-    "fetch_kib_per_step": 773886.32 + 6 * 321123.70 + 34966340.71,
-    "write_kib_per_step": 2901373.47 + 6 * 68375.71 + 1575411.84,
-    "fetch_scale": 1048576.0 / 524309.34,
+    "sha256": "1d45644d41a3870883bd2892bf54dc84ec5588331bc7491fb7963f0e9825b971",
+    "fetch_kib_per_step": 776425.90 + 6 * 321005.06 + 34941441.72,
+    "write_kib_per_step": 2901375.20 + 6 * 68432.40 + 1573157.61,
+    "fetch_scale": 1048576.0 / 524309.00,
     "write_scale": 1048576.0 / 1048576.0,
 }
 
