@@ -99,3 +99,32 @@ def test_broadcast_pairs_match_the_oracle():
     for r, gw in [(0, 0), (1, 5), (2, 0), (3, 4), (50, 10)]:
         assert ctx.head_pairs(BC, r, gw) == oprof.head_pairs(g, (BC, r, gw)), (r, gw)
     ctx.close()
+
+
+def test_s100_broadcast_layer_sampled():
+    """The bench's S = 100 layer with its position heads as broadcast heads
+    (radius 1 on the 37 x 37 patch grid), in the bench's launch configuration:
+    the broadcast heads' outputs on sampled rows (every special row, frame 0,
+    frame boundaries) against the oracle."""
+    saf = _saf()
+    from workload import make_inputs, sample_rows
+    w = make_inputs(3)
+    g = w.geom
+    plan = [(BC, 1, 37, 0) if p[0] == ROLE_POSITION else p for p in w.plan]
+    heads = [h for h, p in enumerate(plan) if p[0] == BC]
+    assert len(heads) == 4 and g.P == 37 * 37
+    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+    say("S=100 broadcast layer: index build")
+    ctx.build_corr_index(to_dev(w.dino), w.corr_K)
+    say("S=100 broadcast layer")
+    o = ctx.sparse_attention(plan, to_dev(w.q), to_dev(w.k), to_dev(w.v))
+    torch.cuda.synchronize()
+    rows = sample_rows(g, 1024, seed=6)
+    # only the broadcast heads are compared: the oracle's other heads are dense placeholders
+    oplan = [p if p[0] == BC else (ROLE_DENSE, 0, 0, 0) for p in plan]
+    outs, _, _ = oracle.layer(g, oplan, w.q, w.k, w.v, rows=rows, heads=heads)
+    got = to_host_f64(o)
+    for h in heads:
+        err = np.max(np.abs(got[h][rows] - outs[h]))
+        assert err <= tol(w), (h, err)
+    ctx.close()
