@@ -126,7 +126,7 @@ def key_counts(w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py runs on one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -80,7 +80,7 @@ typedef enum {
     SAF_EINVAL = -1,        /* bad argument (null pointer, size, role, budget, layout) */
     SAF_ENOMEM = -2,        /* device or host allocation failed */
     SAF_EHIP = -3,          /* the HIP runtime reported an error */
-    SAF_EUNSUPPORTED = -4,  /* valid request outside what this build implements */
+    SAF_EUNSUPPORTED = -4,  /* valid request outside what the library implements */
     SAF_ESTATE = -5         /* call out of order (e.g. no correspondence index yet) */
 } saf_status_t;
 
