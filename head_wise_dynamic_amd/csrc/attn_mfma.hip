@@ -29,6 +29,8 @@ constexpr int KROW = 72;   // K tile row in LDS: 64 bf16 + 8 pad
 constexpr int VROW = 72;   // V^T tile row in LDS: 64 keys + 8 pad
 constexpr int PSTRIDE = kRecStride;  // split partial record: m, l, o[64]
 
+__device__ __forceinline__ int kswz(int row) { return 4 * ((row >> 3) & 1); }
+
 __device__ __forceinline__ int swap_bits23(int m) {
     return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
@@ -86,6 +88,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const Geom &g = L.g;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, gq = lane >> 5;
+    // LDS swizzles (bank-conflict-free stores and reads): K rows r >= 8 of
+    // each group of 16 hold their 16-byte channel chunks XOR 4; the key-pair
+    // words of V^T row c are XOR 4 * ((c >> 3) & 7)
+    const int kx = 4 * ((n >> 2) & 1);  // K rows are read as swap_bits23(n): bit 3 of the row = bit 2 of n
+    const int vx = 4 * (n >> 3);
 
     // ---- locate this work-group's head, query tile and key split
     const int b = blockIdx.x;
@@ -167,8 +174,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         for (int j = 0; j < kUnits; ++j) {
             const int unit = tid + kAttnThreads * j, lp = unit >> 3, lseg = unit & 7;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * lseg]) = kreg[j][i];
-            uint32_t *vt = (uint32_t *)&Vt[buf][(8 * lseg) * VROW + 2 * lp];
+            for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * (lseg ^ kswz(2 * lp + i))]) = kreg[j][i];
+            uint32_t *vt = (uint32_t *)&Vt[buf][(8 * lseg) * VROW] + (lp ^ (4 * lseg));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // channels 2e and 2e+1 of the two keys
@@ -203,10 +210,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[bb][qb][r] = 0.f;
-            const uint16_t *krow = &Ks[buf][(32 * bb + swap_bits23(n)) * KROW + 8 * gq];
+            const uint16_t *krow = &Ks[buf][(32 * bb + swap_bits23(n)) * KROW];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bf16x8 a = *(const bf16x8 *)(krow + 16 * c);
+                const bf16x8 a = *(const bf16x8 *)(krow + 8 * ((2 * c + gq) ^ kx));
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
                     s[bb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][c], s[bb][qb], 0, 0, 0);
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
             }
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                const bf16x8 a = *(const bf16x8 *)(&Vt[buf][(32 * db + n) * VROW + 16 * e + 8 * gq]);
+                const bf16x8 a = *(const bf16x8 *)(&Vt[buf][(32 * db + n) * VROW + 2 * ((8 * e + 4 * gq) ^ (16 * db + vx))]);
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
                     oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
