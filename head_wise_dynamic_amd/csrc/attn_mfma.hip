@@ -153,19 +153,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
 #pragma unroll
         for (int j = 0; j < kUnits; ++j) {
             const int unit = tid + kAttnThreads * j, lp = unit >> 3, lseg = unit & 7;
+            // both keys' tokens first (a vertical head reads them from its
+            // list), then every gather unconditionally: a slot without a key
+            // reads token 0 and is zeroed when the tile is stored.  Guarded
+            // loads would make the compiler wait for them before the current
+            // tile's first MFMA, which defeats the prefetch.
+            int64_t tk[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int64_t m = kt + 2 * lp + i;
-                int64_t tok = -1;
-                if (m < kend) tok = key_token(w, g, m, rm.qsel);
-                kval[j][i] = tok >= 0;
-                if (tok >= 0) {
-                    kreg[j][i] = *(const u32x4 *)(K + tok * ts + 8 * lseg);
-                    vreg[j][i] = *(const u32x4 *)(V + tok * ts + 8 * lseg);
-                } else {
-                    kreg[j][i] = u32x4{0u, 0u, 0u, 0u};
-                    vreg[j][i] = u32x4{0u, 0u, 0u, 0u};
-                }
+                tk[i] = (m < kend) ? key_token(w, g, m, rm.qsel) : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                kval[j][i] = tk[i] >= 0;
+                const int64_t tc = kval[j][i] ? tk[i] : 0;
+                kreg[j][i] = *(const u32x4 *)(K + tc * ts + 8 * lseg);
+                vreg[j][i] = *(const u32x4 *)(V + tc * ts + 8 * lseg);
             }
         }
     };
@@ -173,14 +177,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
 #pragma unroll
         for (int j = 0; j < kUnits; ++j) {
             const int unit = tid + kAttnThreads * j, lp = unit >> 3, lseg = unit & 7;
+            u32x4 kz[2], vz[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * (lseg ^ kswz(2 * lp + i))]) = kreg[j][i];
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kz[i][e] = kval[j][i] ? kreg[j][i][e] : 0u;
+                    vz[i][e] = kval[j][i] ? vreg[j][i][e] : 0u;
+                }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * (lseg ^ kswz(2 * lp + i))]) = kz[i];
             uint32_t *vt = (uint32_t *)&Vt[buf][(8 * lseg) * VROW] + (lp ^ (4 * lseg));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 // channels 2e and 2e+1 of the two keys
-                vt[(2 * e) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[j][1][e], vreg[j][0][e], 0x05040100u);
-                vt[(2 * e + 1) * (VROW / 2)] = __builtin_amdgcn_perm(vreg[j][1][e], vreg[j][0][e], 0x07060302u);
+                vt[(2 * e) * (VROW / 2)] = __builtin_amdgcn_perm(vz[1][e], vz[0][e], 0x05040100u);
+                vt[(2 * e + 1) * (VROW / 2)] = __builtin_amdgcn_perm(vz[1][e], vz[0][e], 0x07060302u);
             }
             if (lseg == 0) {
                 kbias[buf][2 * lp] = kval[j][0] ? 0.f : -INFINITY;
@@ -194,6 +206,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         load_tile(kbeg);
         store_tile(0);
     }
+    // every load so far (Q, the first tile) complete on every path: the
+    // compiler's wait analysis is not path-sensitive, and a Q load it
+    // believes pending at the loop head makes it wait for all loads in
+    // flight, the next tile's prefetch included, before each tile's MFMAs
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt at their maxima
     __syncthreads();
 
     for (int64_t t = 0; t < ntiles; ++t) {
