@@ -85,30 +85,38 @@ __device__ void row_accumulate(const ValuLaunch &L, const HeadWork &w, int32_t q
     for (int64_t c0 = 0; c0 < count; c0 += CH) {
         int64_t tok[NP];
         float s[NP];
+        // Every load of a chunk is unconditional (a slot past the end reads
+        // the last key, a slot without a key token 0; both are masked
+        // afterwards by select), so that all of them are in flight together:
+        // guarded loads make the compiler wait for each one on its own.
+        // (the list reads go out together before any test on their values)
+        if (idx_row) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int64_t m = c0 + p * RPP + grp;
-            tok[p] = -1;
-            if (m < count) {
-                if (idx_row)
-                    tok[p] = (int64_t)idx_row[m];
-                else if constexpr (sizeof(T) == 4)
-                    tok[p] = key_token(w, g, m, qsel);
-                else
-                    tok[p] = m;  // bf16 rows gather listed keys only (checked at launch)
+            for (int p = 0; p < NP; ++p) {
+                const int64_t m = c0 + p * RPP + grp;
+                tok[p] = (int64_t)idx_row[m < count ? m : count - 1];
             }
-            if (skip > 0 && tok[p] >= 0 && tok[p] % skip == 0) tok[p] = -1;
+        } else {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int64_t m = c0 + p * RPP + grp, mc = m < count ? m : count - 1;
+                if constexpr (sizeof(T) == 4)
+                    tok[p] = key_token(w, g, mc, qsel);
+                else
+                    tok[p] = mc;  // bf16 rows gather listed keys only (checked at launch)
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            if (c0 + p * RPP + grp >= count) tok[p] = -1;
+        if (skip > 0) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                if (tok[p] >= 0 && tok[p] % skip == 0) tok[p] = -1;
         }
         float kx[NP][EPL];
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            if (tok[p] >= 0) {
-                E::load(K + tok[p] * ts + sub * EPL, kx[p]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) kx[p][e] = 0.f;
-            }
-        }
+        for (int p = 0; p < NP; ++p) E::load(K + (tok[p] >= 0 ? tok[p] : 0) * ts + sub * EPL, kx[p]);
         float cm = -INFINITY;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -135,14 +143,14 @@ __device__ void row_accumulate(const ValuLaunch &L, const HeadWork &w, int32_t q
         a.m = m_new;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) a.o[e] *= alpha;
+        float vx[NP][EPL];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) E::load(V + (tok[p] >= 0 ? tok[p] : 0) * ts + sub * EPL, vx[p]);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            if (tok[p] >= 0) {
-                float vx[EPL];
-                E::load(V + tok[p] * ts + sub * EPL, vx);
+            const bool ok = tok[p] >= 0;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) a.o[e] = fmaf(s[p], vx[e], a.o[e]);
-            }
+            for (int e = 0; e < EPL; ++e) a.o[e] = ok ? fmaf(s[p], vx[p][e], a.o[e]) : a.o[e];
         }
     }
 }
