@@ -42,9 +42,9 @@ COSINE_GEMM_COUNTERS = {
     "config": 3,  # the workload the counters were taken on (S = 100)
     "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
     "sha256": "1d45644d41a3870883bd2892bf54dc84ec5588331bc7491fb7963f0e9825b971",
-    "fetch_kib_per_step": 776425.90 + 6 * 321005.06 + 34941441.72,
-    "write_kib_per_step": 2901375.20 + 6 * 68432.40 + 1573157.61,
-    "fetch_scale": 1048576.0 / 524309.00,
+    "fetch_kib_per_step": 773525.04 + 6 * 321151.26 + 34893116.01,
+    "write_kib_per_step": 2901376.88 + 6 * 68417.83 + 1587359.72,
+    "fetch_scale": 1048576.0 / 524303.31,
     "write_scale": 1048576.0 / 1048576.0,
 }
 
