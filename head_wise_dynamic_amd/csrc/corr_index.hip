@@ -813,10 +813,15 @@ __global__ __launch_bounds__(256) void frame_topk(const Args A) {
     const float *src = A.chunk + (u - A.row_lo) * g.Np + (int64_t)gf * g.P;
     const int ne = (g.P + 63) / 64;
     uint32_t key[MAXE];  // order_key of the cosine; 0 marks an empty slot
+    // unconditional loads (a slot past the frame reads its last patch and is
+    // emptied afterwards), so that all of them are in flight together
+    float x[MAXE];
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) x[e] = src[min(e * 64 + lane, g.P - 1)];
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) {
         const int i = e * 64 + lane;
-        key[e] = (e < ne && i < g.P) ? max(order_key(src[i]), 1u) : 0u;
+        key[e] = (e < ne && i < g.P) ? max(order_key(x[e]), 1u) : 0u;
     }
     const uint32_t K = (uint32_t)A.K;
     uint64_t keep = 0;  // bit e: slot e is selected
