@@ -41,10 +41,10 @@ PEAK_BF16_TFLOPS = 2500.0
 COSINE_GEMM_COUNTERS = {
     "config": 3,  # the workload the counters were taken on (S = 100)
     "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-    "sha256": "1d45644d41a3870883bd2892bf54dc84ec5588331bc7491fb7963f0e9825b971",
-    "fetch_kib_per_step": 773525.04 + 6 * 321151.26 + 34893116.01,
-    "write_kib_per_step": 2901376.88 + 6 * 68417.83 + 1587359.72,
-    "fetch_scale": 1048576.0 / 524303.31,
+    "sha256": "cd197770baff661334665295e7c2c0fe449ff093387bffe820d56e61c36e620d",
+    "fetch_kib_per_step": 772083.44 + 6 * 321386.92 + 34976657.32,
+    "write_kib_per_step": 2901378.60 + 6 * 68748.16 + 1568637.80,
+    "fetch_scale": 1048576.0 / 524303.41,
     "write_scale": 1048576.0 / 1048576.0,
 }
 

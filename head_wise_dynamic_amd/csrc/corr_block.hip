@@ -45,10 +45,13 @@ __global__ __launch_bounds__(kMeanThreads) void block_means(const T *F, int64_t 
         const int64_t u = blk * b + i;
         float x[kMeanPer];
         float ss = 0.f;
+        // unconditional loads (a channel past Df reads the last one and is
+        // zeroed afterwards), so that all of them are in flight together
+#pragma unroll
+        for (int e = 0; e < kMeanPer; ++e) x[e] = load_feat<T>(F, u * stride + min(tid + e * kMeanThreads, Df - 1));
 #pragma unroll
         for (int e = 0; e < kMeanPer; ++e) {
-            const int c = tid + e * kMeanThreads;
-            x[e] = c < Df ? load_feat<T>(F, u * stride + c) : 0.f;
+            if (tid + e * kMeanThreads >= Df) x[e] = 0.f;
             ss = fmaf(x[e], x[e], ss);
         }
 #pragma unroll
