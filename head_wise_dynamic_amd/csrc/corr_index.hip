@@ -519,10 +519,13 @@ template <int MAXE> struct RowSel {
         for (int e = 0; e < MAXE; ++e) {
             sc[e] = -INFINITY;
             id[e] = INT32_MAX;
-            if (e < ne) {
+            if (e < ne) {  // wave-uniform
+                // unconditional load (a lane past the end reads entry n - 1,
+                // or entry 0 of an empty row, and is masked): guarded loads
+                // make the compiler wait for each one on its own
                 const int i = e * 64 + lane;
+                const float2 x = buf[min(i, max(n - 1, 0))];
                 if (i < n) {
-                    const float2 x = buf[i];
                     sc[e] = x.x;
                     id[e] = __float_as_int(x.y);
                 }
@@ -645,7 +648,8 @@ __global__ __launch_bounds__(256) void compact_rows(const Args A) {
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 const uint32_t i = i0 + 64 * c + lane;
-                x[c] = i < total ? buf[i] : make_float2(-INFINITY, 0.f);
+                x[c] = buf[min(i, total - 1)];  // unconditional, masked below
+                if (i >= total) x[c] = make_float2(-INFINITY, 0.f);
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
