@@ -41,10 +41,10 @@ PEAK_BF16_TFLOPS = 2500.0
 COSINE_GEMM_COUNTERS = {
     "config": 3,  # the workload the counters were taken on (S = 100)
     "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-    "sha256": "cd197770baff661334665295e7c2c0fe449ff093387bffe820d56e61c36e620d",
-    "fetch_kib_per_step": 772083.44 + 6 * 321386.92 + 34976657.32,
-    "write_kib_per_step": 2901378.60 + 6 * 68748.16 + 1568637.80,
-    "fetch_scale": 1048576.0 / 524303.41,
+    "sha256": "5a060c0484a7166e92b37ad27a562527a3a78e2b18db6c5dfa9bf32154ccdbc5",
+    "fetch_kib_per_step": 771903.62 + 6 * 321064.45 + 34938508.72,
+    "write_kib_per_step": 2901375.22 + 6 * 68530.72 + 1570484.69,
+    "fetch_scale": 1048576.0 / 524303.62,
     "write_scale": 1048576.0 / 1048576.0,
 }
 
