@@ -65,14 +65,17 @@ _PROTOS = {
     "saf_build_corr_index_blocks": (C.c_int, [_VP, _VP, _I32, _I32, _I64, _I32, _I32, _I32, _VP]),
     "saf_build_corr_index_qk": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _I32, _VP]),
     "saf_head_nmse": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _VP, _VP]),
+    "saf_head_nmse_accumulate": (C.c_int, [_VP, _VP, _VP, saf_layout_t, C.c_double, _VP, _I64, _VP]),
     "saf_head_pairs": (C.c_int, [_VP, C.POINTER(saf_head_plan_t), _I32, C.POINTER(C.c_int64)]),
     "saf_profile_select": (C.c_int32, [C.POINTER(C.c_double), C.POINTER(C.c_double), _I32]),
     "saf_baseline_stride": (C.c_int32, [C.c_double]),
     "saf_set_corr_index": (C.c_int, [_VP, _VP, _I32, _VP]),
     "saf_get_corr_index": (C.c_int, [_VP, _VP, C.POINTER(_I32), _VP]),
+    "saf_corr_recomputed_rows": (C.c_int, [_VP, _VP, _I32, C.POINTER(_I32), _VP]),
     "saf_build_vertical_index": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _VP, _VP, _SZ, _VP]),
     "saf_sparse_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _I64, _VP, _SZ, _VP]),
     "saf_dense_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _SZ, _VP]),
+    "saf_debug_fail_alloc": (C.c_int, [_I32]),
     "saf_set_kernel_timing": (C.c_int, [_VP, _I32]),
     "saf_read_kernel_timing": (C.c_int, [_VP, _I32, C.POINTER(C.c_char_p), C.POINTER(C.c_float),
                                          C.POINTER(_I32)]),
@@ -132,6 +135,10 @@ def saf_head_nmse(ctx, o_full, o_sparse, layout, dev_out, stream) -> int:
     return lib().saf_head_nmse(ctx, o_full, o_sparse, layout, dev_out, stream)
 
 
+def saf_head_nmse_accumulate(ctx, o_full, o_sparse, layout, weight, dev_err, err_stride, stream) -> int:
+    return lib().saf_head_nmse_accumulate(ctx, o_full, o_sparse, layout, weight, dev_err, err_stride, stream)
+
+
 def saf_head_pairs(ctx, head, corr_kc, pairs) -> int:
     return lib().saf_head_pairs(ctx, head, corr_kc, pairs)
 
@@ -152,6 +159,10 @@ def saf_get_corr_index(ctx, dev_out, Kc: C.c_int32, stream) -> int:
     return lib().saf_get_corr_index(ctx, dev_out, C.byref(Kc), stream)
 
 
+def saf_corr_recomputed_rows(ctx, host_rows, max_rows, count: C.c_int32, stream) -> int:
+    return lib().saf_corr_recomputed_rows(ctx, host_rows, max_rows, C.byref(count), stream)
+
+
 def saf_build_vertical_index(ctx, q, k, layout, head, K, dev_idx_out, ws, ws_bytes, stream) -> int:
     return lib().saf_build_vertical_index(ctx, q, k, layout, head, K, dev_idx_out, ws, ws_bytes, stream)
 
@@ -162,6 +173,10 @@ def saf_sparse_attention(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, ws, w
 
 def saf_dense_attention(ctx, q, k, v, o, layout, ws, ws_bytes, stream) -> int:
     return lib().saf_dense_attention(ctx, q, k, v, o, layout, ws, ws_bytes, stream)
+
+
+def saf_debug_fail_alloc(allowed) -> int:
+    return lib().saf_debug_fail_alloc(allowed)
 
 
 def saf_set_kernel_timing(ctx, enable) -> int:
@@ -231,6 +246,35 @@ class Context:
             return saf_layout_t(t.stride(1), t.stride(0))
         raise ValueError(f"tensor shape {tuple(t.shape)} is neither [H,N,d] nor [N,H,d]")
 
+    def _tensors(self, q: torch.Tensor, *others) -> saf_layout_t:
+        """Layout of q after checking q and every (name, tensor) in others.
+
+        The library takes one layout and one dtype for q, k, v and o, so every
+        tensor must match q's shape and strides, carry the context's dtype and
+        live on q's GPU; any mismatch would read or write out of bounds.
+        Checked in that order (shapes, dtypes, devices), for all tensors."""
+        if not isinstance(q, torch.Tensor) or not all(isinstance(t, torch.Tensor) for _, t in others):
+            raise TypeError("q, k, v and o must be torch tensors")
+        lay = self.layout_of(q)
+        named = [("q", q)] + list(others)
+        for name, t in named[1:]:
+            if tuple(t.shape) != tuple(q.shape) or tuple(t.stride()) != tuple(q.stride()):
+                raise ValueError(f"{name} has shape {tuple(t.shape)} / strides {tuple(t.stride())}; expected "
+                                 f"{tuple(q.shape)} / {tuple(q.stride())} like q")
+        for name, t in named:
+            if t.dtype != self.dtype:
+                raise ValueError(f"{name} has dtype {t.dtype}, the context computes in {self.dtype}")
+        for name, t in named:
+            if t.device != q.device or t.device.type != "cuda":
+                raise ValueError(f"{name} is on {t.device}; expected q's GPU (q is on {q.device})")
+        return lay
+
+    def _rows_of(self, t: torch.Tensor, name: str, rows: int, device=None) -> None:
+        if t.shape[0] != rows:
+            raise ValueError(f"{name} has {t.shape[0]} rows; expected {rows}")
+        if t.device.type != "cuda" or (device is not None and t.device != device):
+            raise ValueError(f"{name} must be a GPU tensor" + (f" on {device}" if device is not None else ""))
+
     def workspace(self, nbytes: int, device) -> torch.Tensor:
         if self._ws is None or self._ws.numel() < nbytes or self._ws.device != device:
             self._ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -245,6 +289,7 @@ class Context:
     def build_corr_index(self, dino: torch.Tensor, K: int, mode: int = SAF_CORR_TOTAL, stream=None):
         if dino.dim() != 2 or dino.stride(1) != 1:
             raise ValueError("dino must be [S*P, Df] with contiguous channels")
+        self._rows_of(dino, "dino", self.Np)
         self._check(saf_build_corr_index(self._ctx, C.c_void_p(dino.data_ptr()), _DT.get(dino.dtype, 99),
                                          dino.shape[1], dino.stride(0), K, mode, _stream(stream)))
 
@@ -252,18 +297,20 @@ class Context:
                                 stream=None):
         if dino.dim() != 2 or dino.stride(1) != 1:
             raise ValueError("dino must be [S*P, Df] with contiguous channels")
+        self._rows_of(dino, "dino", self.Np)
         self._check(saf_build_corr_index_blocks(self._ctx, C.c_void_p(dino.data_ptr()), _DT.get(dino.dtype, 99),
                                                 dino.shape[1], dino.stride(0), block, K, mode, _stream(stream)))
 
     def build_corr_index_qk(self, q: torch.Tensor, k: torch.Tensor, head: int, K: int, mode: int = SAF_CORR_TOTAL,
                             stream=None):
-        lay = self.layout_of(q)
+        lay = self._tensors(q, ("k", k))
         self._check(saf_build_corr_index_qk(self._ctx, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()), lay, head,
                                             K, mode, _stream(stream)))
 
     def set_corr_index(self, idx: torch.Tensor, stream=None):
         if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():
             raise ValueError("index must be a contiguous int32 [S*P, Kc] tensor")
+        self._rows_of(idx, "index", self.Np)
         self._check(saf_set_corr_index(self._ctx, C.c_void_p(idx.data_ptr()), idx.shape[1], _stream(stream)))
 
     def corr_k(self) -> int:
@@ -277,8 +324,17 @@ class Context:
         self._check(saf_get_corr_index(self._ctx, C.c_void_p(out.data_ptr()), C.c_int32(), _stream(stream)))
         return out
 
+    def recomputed_rows(self, stream=None):
+        """Patch numbers the last total-mode index build recomputed exactly (sorted)."""
+        cnt = C.c_int32()
+        self._check(saf_corr_recomputed_rows(self._ctx, None, 0, cnt, _stream(stream)))
+        n = cnt.value
+        buf = (C.c_int32 * max(n, 1))()
+        self._check(saf_corr_recomputed_rows(self._ctx, buf, n, cnt, _stream(stream)))
+        return sorted(buf[i] for i in range(min(n, cnt.value)))
+
     def build_vertical_index(self, q: torch.Tensor, k: torch.Tensor, head: int, K: int, stream=None):
-        lay = self.layout_of(q)
+        lay = self._tensors(q, ("k", k))
         plan = [(SAF_VERTICAL, K, 0, 0)] + [(SAF_DENSE, 0, 0, 0)] * (self.H - 1)
         ws = self.workspace(self.workspace_size(plan), q.device)
         out = torch.empty(min(K, self.N), dtype=torch.int32, device=q.device)
@@ -290,9 +346,11 @@ class Context:
     # -- attention ----------------------------------------------------------
     def sparse_attention(self, plan, q, k, v, o=None, vert_idx: Optional[torch.Tensor] = None,
                          stream=None) -> torch.Tensor:
-        lay = self.layout_of(q)
+        if len(plan) != self.H:
+            raise ValueError(f"plan has {len(plan)} entries; the context has {self.H} heads")
         if o is None:
             o = torch.empty_like(q)
+        lay = self._tensors(q, ("k", k), ("v", v), ("o", o))
         cplan = make_plan(plan)
         need = self.workspace_size(plan)
         ws = self.workspace(need, q.device)
@@ -300,6 +358,7 @@ class Context:
         if vert_idx is not None:
             if vert_idx.dtype != torch.int32 or vert_idx.dim() != 2 or not vert_idx.is_contiguous():
                 raise ValueError("vert_idx must be a contiguous int32 [H, ld] tensor")
+            self._rows_of(vert_idx, "vert_idx", self.H, q.device)
             vptr, vld = C.c_void_p(vert_idx.data_ptr()), vert_idx.shape[1]
         self._check(saf_sparse_attention(self._ctx, cplan, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
                                          C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), lay, vptr, vld,
@@ -319,14 +378,29 @@ class Context:
 
     def head_nmse(self, o_full: torch.Tensor, o_sparse: torch.Tensor, out: torch.Tensor = None, stream=None):
         """[H, 2] float64 (device): per head sum (o_full - o_sparse)^2 and sum o_full^2."""
-        lay, l2 = self.layout_of(o_full), self.layout_of(o_sparse)
-        if (lay.head_stride, lay.token_stride) != (l2.head_stride, l2.token_stride) or o_full.dtype != o_sparse.dtype:
-            raise ValueError("outputs must share a layout and dtype")
+        lay = self._tensors(o_full, ("o_sparse", o_sparse))
         if out is None:
             out = torch.empty((self.H, 2), dtype=torch.float64, device=o_full.device)
+        if out.dtype != torch.float64 or out.numel() < 2 * self.H or not out.is_contiguous() or \
+                out.device != o_full.device:
+            raise ValueError("out must be a contiguous float64 GPU tensor of at least 2H elements")
         self._check(saf_head_nmse(self._ctx, C.c_void_p(o_full.data_ptr()), C.c_void_p(o_sparse.data_ptr()), lay,
                                   C.c_void_p(out.data_ptr()), _stream(stream)))
         return out
+
+    def head_nmse_accumulate(self, o_full: torch.Tensor, o_sparse: torch.Tensor, err: torch.Tensor,
+                             weight: float, stream=None) -> torch.Tensor:
+        """err[h] += weight * ||o_full[h] - o_sparse[h]||^2 / ||o_full[h]||^2 (Eq. 1,
+        in the library).  err: float64 GPU tensor of H elements (any stride, e.g.
+        a column of an [H, configurations] table)."""
+        lay = self._tensors(o_full, ("o_sparse", o_sparse))
+        if err.dtype != torch.float64 or err.dim() != 1 or err.shape[0] != self.H or err.stride(0) < 1 or \
+                err.device != o_full.device:
+            raise ValueError("err must be a float64 GPU vector of H elements")
+        self._check(saf_head_nmse_accumulate(self._ctx, C.c_void_p(o_full.data_ptr()),
+                                             C.c_void_p(o_sparse.data_ptr()), lay, float(weight),
+                                             C.c_void_p(err.data_ptr()), err.stride(0), _stream(stream)))
+        return err
 
     def head_pairs(self, role: int, budget: int = 0, anchor: int = 0, corr_kc: int = 0) -> int:
         n = C.c_int64()
@@ -335,9 +409,9 @@ class Context:
         return n.value
 
     def dense_attention(self, q, k, v, o=None, stream=None) -> torch.Tensor:
-        lay = self.layout_of(q)
         if o is None:
             o = torch.empty_like(q)
+        lay = self._tensors(q, ("k", k), ("v", v), ("o", o))
         self._check(saf_dense_attention(self._ctx, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
                                         C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), lay, None, 0,
                                         _stream(stream)))

@@ -7,6 +7,7 @@ does not know the feature, which is harmless.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -24,8 +25,29 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src: str) -> str:
+def _deps(path: str, seen=None) -> set:
+    """The file and every quoted #include it reaches (csrc/ and include/)."""
+    seen = set() if seen is None else seen
+    if path in seen or not os.path.exists(path):
+        return seen
+    seen.add(path)
+    for line in open(path, errors="replace"):
+        m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+        if m:
+            for base in (os.path.dirname(path), CSRC, os.path.join(ROOT, "include")):
+                cand = os.path.normpath(os.path.join(base, m.group(1)))
+                if os.path.exists(cand):
+                    _deps(cand, seen)
+                    break
+    return seen
+
+
+def _compile(src: str, force: bool = True) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not force and os.path.exists(obj):
+        newest = max([os.path.getmtime(f) for f in _deps(os.path.join(CSRC, src))] + [os.path.getmtime(__file__)])
+        if os.path.getmtime(obj) > newest:
+            return obj
     cmd = ["hipcc"] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
@@ -35,10 +57,12 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, force: bool = True) -> str:
+    """Compile every source and link.  force=False reuses an object that is
+    newer than its source, every header and this script."""
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(lambda src: _compile(src, force), SOURCES))
     tmp = OUT + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,5 +75,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, force="--changed" not in sys.argv)
     sys.exit(0)

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -16,6 +17,7 @@
 
 #include "../../include/saf3r.h"
 #include "saf_internal.h"
+#include "api_internal.h"
 
 struct saf_ctx {
     saf::Geom g{};
@@ -26,10 +28,14 @@ struct saf_ctx {
     size_t corr_bytes = 0;
     void *corr_scratch = nullptr;
     size_t corr_scratch_bytes = 0;
+    // the last build's list of exactly recomputed rows lives in corr_scratch
+    // (carved with this candidate capacity); false when it kept none
+    bool corr_listed = false;
+    int32_t corr_list_cap = 0;
     double *nmse_part = nullptr;  // [H][kNmseBlocks][2] partial sums of the error kernel
     // side stream for the gather path (default priority), fork/join events
     hipStream_t side = nullptr;
-    hipEvent_t ev_fork = nullptr, ev_vert = nullptr, ev_join = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
     // per-launch timing
     bool timing = false;
     struct Rec {
@@ -109,6 +115,27 @@ saf_status_t hip_fail(saf_ctx_t *c, hipError_t e, const char *what) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Testing hook (saf_debug_fail_alloc): the number of device allocations
+// still allowed to succeed before the next one reports out-of-memory;
+// negative = no limit.
+std::atomic<int64_t> g_alloc_allowance{-1};
+
+// Every device allocation of the library goes through here.
+hipError_t dev_alloc(void **p, size_t bytes) {
+    *p = nullptr;
+    int64_t a = g_alloc_allowance.load();
+    while (a >= 0) {
+        if (a == 0) return hipErrorOutOfMemory;
+        if (g_alloc_allowance.compare_exchange_weak(a, a - 1)) break;
+    }
+    const hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+    }
+    return e;
+}
 
 constexpr int QT = saf::kQueryTile;  // query tile of the matrix-core kernel
 constexpr int kSplitKeys = 8192;  // keys per split for dense special rows
@@ -269,7 +296,6 @@ void saf_destroy(saf_ctx_t *c) {
     }
     if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
     if (c->ev_join) (void)hipEventDestroy(c->ev_join);
-    if (c->ev_vert) (void)hipEventDestroy(c->ev_vert);
     if (c->corr_idx || c->corr_scratch || c->nmse_part) {
         (void)hipDeviceSynchronize();
         if (c->corr_idx) (void)hipFree(c->corr_idx);
@@ -294,40 +320,58 @@ saf_status_t saf_workspace_size(const saf_ctx_t *cc, const saf_head_plan_t *plan
     return SAF_OK;
 }
 
+// Forget the cached index: a build or copy that failed after writing into it
+// leaves nothing usable, and later calls needing an index return SAF_ESTATE.
+static void drop_corr_index(saf_ctx_t *c) {
+    if (c->corr_idx) (void)hipFree(c->corr_idx);
+    c->corr_idx = nullptr;
+    c->corr_bytes = 0;
+    c->corr_k = 0;
+    c->corr_build_k = 0;
+    c->corr_listed = false;
+}
+
+// Index storage for rows of K entries.  A new buffer is allocated before the
+// old one is released, so an allocation failure leaves the cached index as
+// it was.  Once a new buffer is in place the index counts as absent
+// (corr_k = 0) until the caller's build or copy has been enqueued.
 static saf_status_t ensure_corr_storage(saf_ctx_t *c, int32_t K) {
     const size_t need = sizeof(int32_t) * (size_t)c->g.Np * (size_t)K;
     if (c->corr_idx && c->corr_bytes == need) return SAF_OK;
-    if (c->corr_idx) {
-        hipError_t e = hipFree(c->corr_idx);
-        c->corr_idx = nullptr;
-        c->corr_bytes = 0;
-        if (e != hipSuccess) return hip_fail(c, e, "hipFree(corr index)");
-    }
-    hipError_t e = hipMalloc((void **)&c->corr_idx, need);
-    if (e != hipSuccess) {
-        c->corr_idx = nullptr;
-        (void)hipGetLastError();
+    void *p = nullptr;
+    if (dev_alloc(&p, need) != hipSuccess)
         return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for the correspondence index failed", need);
+    if (c->corr_idx) {
+        const hipError_t e = hipFree(c->corr_idx);
+        c->corr_idx = nullptr;
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            drop_corr_index(c);
+            return hip_fail(c, e, "hipFree(corr index)");
+        }
     }
+    c->corr_idx = (int32_t *)p;
     c->corr_bytes = need;
+    c->corr_k = 0;
+    c->corr_build_k = 0;
+    c->corr_listed = false;
     return SAF_OK;
 }
 
-// grow the context-owned build scratch to at least sb bytes
+// grow the context-owned build scratch to at least sb bytes (the scratch
+// holds no state the cached index depends on, except the list of recomputed
+// rows, which a regrown scratch no longer has)
 static saf_status_t ensure_corr_scratch(saf_ctx_t *c, size_t sb) {
     if (c->corr_scratch_bytes >= sb) return SAF_OK;
+    c->corr_listed = false;
     if (c->corr_scratch) {
         hipError_t e = hipFree(c->corr_scratch);
         c->corr_scratch = nullptr;
         c->corr_scratch_bytes = 0;
         if (e != hipSuccess) return hip_fail(c, e, "hipFree(corr scratch)");
     }
-    hipError_t e = hipMalloc(&c->corr_scratch, sb);
-    if (e != hipSuccess) {
-        c->corr_scratch = nullptr;
-        (void)hipGetLastError();
+    if (dev_alloc(&c->corr_scratch, sb) != hipSuccess)
         return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for index scratch failed", sb);
-    }
     c->corr_scratch_bytes = sb;
     return SAF_OK;
 }
@@ -362,13 +406,12 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
         if (Kc > 1024) return fail(c, SAF_EUNSUPPORTED, "K %d > 1024", Kc);
     }
 
-    saf_status_t st = ensure_corr_storage(c, Kc);
-    if (st != SAF_OK) return st;
     const int32_t cap = per_frame ? 0 : saf::corr_capacity(g, Kc);
     const int32_t chunk_rows = per_frame ? saf::corr_frame_chunk_rows(g) : 0;
     const size_t sb = per_frame ? saf::corr_frame_scratch_bytes(g, chunk_rows) : saf::corr_scratch_bytes(g, Kc, cap);
-    st = ensure_corr_scratch(c, sb);
+    saf_status_t st = ensure_corr_scratch(c, sb);
     if (st != SAF_OK) return st;
+    if ((st = ensure_corr_storage(c, Kc)) != SAF_OK) return st;
     saf::CorrBuild B{};
     B.g = g;
     B.dino = dino;
@@ -388,9 +431,14 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
         Timed tm(c, as_stream(stream), "corr_index");
         e = saf::launch_corr_build(B, as_stream(stream));
     }
-    if (e != hipSuccess) return hip_fail(c, e, "correspondence index kernels");
+    if (e != hipSuccess) {
+        drop_corr_index(c);
+        return hip_fail(c, e, "correspondence index kernels");
+    }
     c->corr_k = Kc;
     c->corr_build_k = K;
+    c->corr_listed = saf::corr_build_lists_rows(B);
+    c->corr_list_cap = cap;
     return SAF_OK;
 }
 
@@ -418,11 +466,11 @@ saf_status_t saf_build_corr_index_qk(saf_ctx_t *c, const void *q, const void *k,
         Kk = Kc = (int32_t)std::min<int64_t>(K, (int64_t)(g.S - 1) * g.P);
         if (Kc > 1024) return fail(c, SAF_EUNSUPPORTED, "K %d > 1024", Kc);
     }
-    if ((st = ensure_corr_storage(c, Kc)) != SAF_OK) return st;
     const int32_t cap = per_frame ? 0 : saf::corr_capacity(g, Kc);
     const int32_t chunk_rows = per_frame ? saf::corr_frame_chunk_rows(g) : 0;
     const size_t sb = per_frame ? saf::corr_frame_scratch_bytes(g, chunk_rows) : saf::corr_scratch_bytes(g, Kc, cap);
     if ((st = ensure_corr_scratch(c, sb)) != SAF_OK) return st;
+    if ((st = ensure_corr_storage(c, Kc)) != SAF_OK) return st;
     const size_t es = g.dtype == saf::BF16 ? 2 : 4;
     saf::CorrBuild B{};
     B.g = g;
@@ -446,9 +494,14 @@ saf_status_t saf_build_corr_index_qk(saf_ctx_t *c, const void *q, const void *k,
         Timed tm(c, as_stream(stream), "corr_index_qk");
         e = saf::launch_corr_build(B, as_stream(stream));
     }
-    if (e != hipSuccess) return hip_fail(c, e, "logit index kernels");
+    if (e != hipSuccess) {
+        drop_corr_index(c);
+        return hip_fail(c, e, "logit index kernels");
+    }
     c->corr_k = Kc;
     c->corr_build_k = K;
+    c->corr_listed = saf::corr_build_lists_rows(B);
+    c->corr_list_cap = cap;
     return SAF_OK;
 }
 
@@ -475,10 +528,9 @@ saf_status_t saf_build_corr_index_blocks(saf_ctx_t *c, const void *dino, int32_t
     const int64_t kc64 = (int64_t)rb * block;
     if (kc64 > INT32_MAX / 2) return fail(c, SAF_EUNSUPPORTED, "index row of %lld entries", (long long)kc64);
     const int32_t Kc = (int32_t)kc64;
-    saf_status_t st = ensure_corr_storage(c, Kc);
+    saf_status_t st = ensure_corr_scratch(c, saf::corr_block_scratch_bytes(g, block, Df, K, per_frame ? 1 : 0));
     if (st != SAF_OK) return st;
-    st = ensure_corr_scratch(c, saf::corr_block_scratch_bytes(g, block, Df, K, per_frame ? 1 : 0));
-    if (st != SAF_OK) return st;
+    if ((st = ensure_corr_storage(c, Kc)) != SAF_OK) return st;
     saf::CorrBlockBuild B{};
     B.g = g;
     B.dino = dino;
@@ -497,9 +549,13 @@ saf_status_t saf_build_corr_index_blocks(saf_ctx_t *c, const void *dino, int32_t
         Timed tm(c, as_stream(stream), "corr_index_blocks");
         e = saf::launch_corr_blocks(B, as_stream(stream));
     }
-    if (e != hipSuccess) return hip_fail(c, e, "block correspondence index kernels");
+    if (e != hipSuccess) {
+        drop_corr_index(c);
+        return hip_fail(c, e, "block correspondence index kernels");
+    }
     c->corr_k = Kc;
     c->corr_build_k = K;
+    c->corr_listed = false;
     return SAF_OK;
 }
 
@@ -512,16 +568,47 @@ saf_status_t saf_set_corr_index(saf_ctx_t *c, const int32_t *dev_idx, int32_t Kc
     saf_status_t st = ensure_corr_storage(c, Kc);
     if (st != SAF_OK) return st;
     hipError_t e = hipMemcpyAsync(c->corr_idx, dev_idx, c->corr_bytes, hipMemcpyDeviceToDevice, as_stream(stream));
-    if (e != hipSuccess) return hip_fail(c, e, "hipMemcpyAsync(index)");
+    if (e != hipSuccess) {
+        drop_corr_index(c);
+        return hip_fail(c, e, "hipMemcpyAsync(index)");
+    }
     c->corr_k = Kc;
     c->corr_build_k = Kc;
+    c->corr_listed = false;
+    return SAF_OK;
+}
+
+saf_status_t saf_corr_recomputed_rows(saf_ctx_t *c, int32_t *host_rows, int32_t max_rows, int32_t *count,
+                                      void *stream) {
+    if (!c) return SAF_EINVAL;
+    if (!count) return fail(c, SAF_EINVAL, "null count pointer");
+    if (max_rows < 0 || (max_rows > 0 && !host_rows)) return fail(c, SAF_EINVAL, "bad host_rows / max_rows");
+    *count = 0;
+    if (!c->corr_idx || c->corr_k < 1 || !c->corr_listed || !c->corr_scratch)
+        return fail(c, SAF_ESTATE, "the last index build kept no list of recomputed rows");
+    int32_t *rows = nullptr;
+    uint32_t *cnt = nullptr;
+    saf::corr_recomputed_list(c->corr_scratch, c->g.Np, c->corr_list_cap, &rows, &cnt);
+    const hipStream_t s = as_stream(stream);
+    uint32_t n = 0;
+    hipError_t e = hipMemcpyAsync(&n, cnt, sizeof n, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(c, e, "reading the recomputed-row count");
+    if ((int64_t)n > c->g.Np) return fail(c, SAF_ESTATE, "recomputed-row count %u exceeds S*P", n);
+    const int32_t take = std::min<int32_t>((int32_t)n, max_rows);
+    if (take > 0) {
+        e = hipMemcpyAsync(host_rows, rows, sizeof(int32_t) * (size_t)take, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(c, e, "reading the recomputed rows");
+    }
+    *count = (int32_t)n;
     return SAF_OK;
 }
 
 saf_status_t saf_get_corr_index(const saf_ctx_t *cc, int32_t *dev_out, int32_t *Kc, void *stream) {
     saf_ctx_t *c = const_cast<saf_ctx_t *>(cc);
     if (!c) return SAF_EINVAL;
-    if (!c->corr_idx) return fail(c, SAF_ESTATE, "no correspondence index has been built");
+    if (!c->corr_idx || c->corr_k < 1) return fail(c, SAF_ESTATE, "no correspondence index has been built");
     if (Kc) *Kc = c->corr_k;
     if (!dev_out) return SAF_OK;
     hipError_t e = hipMemcpyAsync(dev_out, c->corr_idx, c->corr_bytes, hipMemcpyDeviceToDevice, as_stream(stream));
@@ -551,9 +638,13 @@ saf_status_t saf_build_vertical_index(saf_ctx_t *c, const void *q, const void *k
     return SAF_OK;
 }
 
-saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, const void *q, const void *k,
-                                  const void *v, void *o, saf_layout_t lay, const int32_t *vert_idx,
-                                  int64_t vert_ld, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+// One layer (saf_sparse_attention).  one_stream: every launch on the caller's
+// stream (no side stream, no stream or event creation).
+static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, const void *q, const void *k,
+                                     const void *v, void *o, saf_layout_t lay, const int32_t *vert_idx,
+                                     int64_t vert_ld, void *ws, size_t ws_bytes, void *stream, bool one_stream) {
     if (!c) return SAF_EINVAL;
     const saf::Geom &g = c->g;
     PlanInfo pi;
@@ -566,7 +657,7 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         if (plan[h].role == SAF_VERTICAL && vert_ld < std::min<int64_t>(plan[h].budget, g.N))
             return fail(c, SAF_EINVAL, "vert_ld %lld < head %d's key count", (long long)vert_ld, h);
     if (pi.ncorr) {
-        if (!c->corr_idx) return fail(c, SAF_ESTATE, "a correspondence head needs a built index");
+        if (!c->corr_idx || c->corr_k < 1) return fail(c, SAF_ESTATE, "a correspondence head needs a built index");
         for (int h = 0; h < g.H; ++h)
             if (plan[h].role == SAF_CORRESPONDENCE && plan[h].budget != 0 && plan[h].budget != c->corr_k &&
                 plan[h].budget != c->corr_build_k)
@@ -657,18 +748,20 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
             wp += union_rec_bytes(g);
         }
 
-    // 2. bf16.  A side stream (default priority) runs the HBM-bound work --
-    // the vertical probe + top-K, then the correspondence heads' gathered
-    // rows -- while the caller's stream runs the matrix-core kernel for the
-    // heads that do not wait for the vertical sets; the vertical heads follow
-    // once their sets exist, and the caller's stream joins the side stream at
-    // the end of the call.
+    // 2. bf16.  The vertical sets are built first, on the caller's stream
+    // (a few tens of microseconds on an idle GPU: its small work-groups
+    // would otherwise wait for free compute units behind the attention
+    // kernels).  Then a side stream (default priority) runs the gathered
+    // correspondence rows (HBM-bound) while the caller's stream runs one
+    // matrix-core launch group for every shared-key head; the caller's
+    // stream joins the side stream at the end of the call.
+    hipError_t e = build_vertical(s);
+    if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
     bool forked = false;
-    if (pi.ncorr || !vheads.empty()) {
+    if (pi.ncorr && !one_stream) {
         if (!c->side) {
             if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
                 hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming) != hipSuccess ||
-                hipEventCreateWithFlags(&c->ev_vert, hipEventDisableTiming) != hipSuccess ||
                 hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming) != hipSuccess) {
                 (void)hipGetLastError();
                 if (c->side) (void)hipStreamDestroy(c->side);
@@ -693,9 +786,6 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         }
     } join{c, s, forked};
 
-    hipError_t e = build_vertical(ss);
-    if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
-    if (forked && !vheads.empty()) (void)hipEventRecord(c->ev_vert, ss);
     if (pi.ncorr) {
         saf::ValuLaunch L{};
         L.g = g;
@@ -739,7 +829,6 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         saf::HeadWork w;
         int64_t tiles;
         double cost;
-        bool needs_vertical;
     };
     std::vector<Item> items;
     const int64_t tpf = (g.T + QT - 1) / QT;
@@ -777,7 +866,6 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
             w.list_len = (int32_t)std::min<int64_t>(plan[h].budget, g.N);
             it.tiles = all_tiles;
             it.cost = w.list_len;
-            it.needs_vertical = !vert_idx;
             break;
         case SAF_SCANNING:
             w.rows = saf::ROWS_ALL;
@@ -832,42 +920,31 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
     M.o = o;
     M.head_stride = lay.head_stride;
     M.token_stride = lay.token_stride;
-    for (int pass = 0; pass < 2; ++pass) {
-        // pass 0: heads that need nothing; pass 1: vertical heads built here
-        std::vector<Item> sel;
-        for (const Item &it : items)
-            if (it.needs_vertical == (pass == 1)) sel.push_back(it);
-        if (sel.empty()) continue;
-        if (pass == 1 && forked) {
-            e = hipStreamWaitEvent(s, c->ev_vert, 0);
-            if (e != hipSuccess) return hip_fail(c, e, "hipStreamWaitEvent(vertical)");
+    for (size_t i0 = 0; i0 < items.size(); i0 += saf::kMaxWork) {
+        M.nwork = 0;
+        int64_t blocks = 0;
+        for (size_t i = i0; i < std::min(items.size(), i0 + saf::kMaxWork); ++i) {
+            saf::HeadWork w = items[i].w;
+            if (w.nsplit > 1) {
+                w.part = (float *)wp;
+                wp += split_part_bytes(g, w.nsplit);
+            }
+            w.block0 = (int32_t)blocks;
+            blocks += items[i].tiles * w.nsplit;
+            M.work[M.nwork++] = w;
         }
-        for (size_t i0 = 0; i0 < sel.size(); i0 += saf::kMaxWork) {
-            M.nwork = 0;
-            int64_t blocks = 0;
-            for (size_t i = i0; i < std::min(sel.size(), i0 + saf::kMaxWork); ++i) {
-                saf::HeadWork w = sel[i].w;
-                if (w.nsplit > 1) {
-                    w.part = (float *)wp;
-                    wp += split_part_bytes(g, w.nsplit);
-                }
-                w.block0 = (int32_t)blocks;
-                blocks += sel[i].tiles * w.nsplit;
-                M.work[M.nwork++] = w;
-            }
-            if (blocks >= ((int64_t)1 << 31)) return fail(c, SAF_EINVAL, "launch too large");
-            M.total_blocks = (int32_t)blocks;
-            {
-                Timed tm(c, s, "shared_attention");
-                e = saf::launch_mfma_attention(M, s);
-            }
-            if (e != hipSuccess) return hip_fail(c, e, "matrix-core attention kernel");
-            {
-                Timed tm(c, s, "split_combine");
-                e = saf::launch_split_combine(M, s);
-            }
-            if (e != hipSuccess) return hip_fail(c, e, "split combine kernel");
+        if (blocks >= ((int64_t)1 << 31)) return fail(c, SAF_EINVAL, "launch too large");
+        M.total_blocks = (int32_t)blocks;
+        {
+            Timed tm(c, s, "shared_attention");
+            e = saf::launch_mfma_attention(M, s);
         }
+        if (e != hipSuccess) return hip_fail(c, e, "matrix-core attention kernel");
+        {
+            Timed tm(c, s, "split_combine");
+            e = saf::launch_split_combine(M, s);
+        }
+        if (e != hipSuccess) return hip_fail(c, e, "split combine kernel");
     }
     if (pi.nunion) {
         // both records exist once the side stream's gather is done
@@ -900,6 +977,14 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
         }
     }
     return SAF_OK;
+}
+
+extern "C" {
+
+saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, const void *q, const void *k,
+                                  const void *v, void *o, saf_layout_t lay, const int32_t *vert_idx,
+                                  int64_t vert_ld, void *ws, size_t ws_bytes, void *stream) {
+    return sparse_attention(c, plan, q, k, v, o, lay, vert_idx, vert_ld, ws, ws_bytes, stream, false);
 }
 
 saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, const void *v, void *o,
@@ -972,6 +1057,11 @@ saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, con
     return SAF_OK;
 }
 
+saf_status_t saf_debug_fail_alloc(int32_t allowed) {
+    g_alloc_allowance.store(allowed < 0 ? -1 : (int64_t)allowed);
+    return SAF_OK;
+}
+
 saf_status_t saf_set_kernel_timing(saf_ctx_t *c, int32_t enable) {
     if (!c) return SAF_EINVAL;
     c->timing = enable != 0;
@@ -1002,31 +1092,67 @@ saf_status_t saf_read_kernel_timing(saf_ctx_t *c, int32_t max, const char **name
 
 }  // extern "C"
 
-// ------------------------------------------------------------ offline profiling
-saf_status_t saf_head_nmse(saf_ctx_t *c, const void *o_full, const void *o_sparse, saf_layout_t lay,
-                           double *dev_out, void *stream) {
+// ------------------------------------------------ entry points in other files
+saf_status_t saf_layer_internal(saf_ctx_t *c, const saf_head_plan_t *plan, const void *q, const void *k,
+                                const void *v, void *o, saf_layout_t lay, const int32_t *vert_idx, int64_t vert_ld,
+                                void *ws, size_t ws_bytes, void *stream, size_t ws_cap, size_t *ws_need) {
     if (!c) return SAF_EINVAL;
-    if (!o_full || !o_sparse || !dev_out) return fail(c, SAF_EINVAL, "null pointer");
+    PlanInfo pi;
+    saf_status_t st = check_plan(c, plan, &pi);
+    if (st != SAF_OK) return st;
+    *ws_need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws) + 256;
+    if (*ws_need > ws_cap)
+        return fail(c, SAF_EUNSUPPORTED, "this plan needs %zu bytes of workspace; the static scratch holds %zu",
+                    *ws_need, ws_cap);
+    if (!ws) return SAF_OK;  // size query
+    // one stream and no timing events: the call creates nothing
+    const bool timing = c->timing;
+    c->timing = false;
+    st = sparse_attention(c, plan, q, k, v, o, lay, vert_idx, vert_ld, ws, ws_bytes, stream, true);
+    c->timing = timing;
+    return st;
+}
+
+saf_status_t saf_fail_internal(saf_ctx_t *c, int32_t status, const char *msg) {
+    return fail(c, (saf_status_t)status, "%s", msg);
+}
+
+// ------------------------------------------------------------ offline profiling
+static saf_status_t head_nmse(saf_ctx_t *c, const void *o_full, const void *o_sparse, saf_layout_t lay,
+                              double *sums, double *acc, int64_t acc_stride, double weight, void *stream) {
     saf_status_t st = check_layout(c, lay);
     if (st != SAF_OK) return st;
     if (!aligned16(o_full) || !aligned16(o_sparse)) return fail(c, SAF_EINVAL, "outputs must be 16-byte aligned");
     if (!c->nmse_part) {
         const size_t bytes = sizeof(double) * 2 * (size_t)c->g.H * saf::kNmseBlocks;
-        hipError_t e = hipMalloc((void **)&c->nmse_part, bytes);
-        if (e != hipSuccess) {
-            c->nmse_part = nullptr;
-            (void)hipGetLastError();
+        if (dev_alloc((void **)&c->nmse_part, bytes) != hipSuccess)
             return fail(c, SAF_ENOMEM, "hipMalloc(%zu) for error partials failed", bytes);
-        }
     }
     hipError_t e;
     {
         Timed tm(c, as_stream(stream), "head_nmse");
-        e = saf::launch_head_nmse(c->g, o_full, o_sparse, lay.head_stride, lay.token_stride, c->nmse_part,
-                                  dev_out, as_stream(stream));
+        e = saf::launch_head_nmse(c->g, o_full, o_sparse, lay.head_stride, lay.token_stride, c->nmse_part, sums,
+                                  acc, acc_stride, weight, as_stream(stream));
     }
     if (e != hipSuccess) return hip_fail(c, e, "error kernels");
     return SAF_OK;
+}
+
+saf_status_t saf_head_nmse(saf_ctx_t *c, const void *o_full, const void *o_sparse, saf_layout_t lay,
+                           double *dev_out, void *stream) {
+    if (!c) return SAF_EINVAL;
+    if (!o_full || !o_sparse || !dev_out) return fail(c, SAF_EINVAL, "null pointer");
+    return head_nmse(c, o_full, o_sparse, lay, dev_out, nullptr, 0, 0.0, stream);
+}
+
+saf_status_t saf_head_nmse_accumulate(saf_ctx_t *c, const void *o_full, const void *o_sparse, saf_layout_t lay,
+                                      double weight, double *dev_err, int64_t err_stride, void *stream) {
+    if (!c) return SAF_EINVAL;
+    if (!o_full || !o_sparse || !dev_err) return fail(c, SAF_EINVAL, "null pointer");
+    if (err_stride < 1) return fail(c, SAF_EINVAL, "err_stride %lld < 1", (long long)err_stride);
+    if (!(weight >= 0.0) || weight > 1e300) return fail(c, SAF_EINVAL, "weight must be finite and >= 0");
+    if (((uintptr_t)dev_err & 7u) != 0) return fail(c, SAF_EINVAL, "dev_err must be 8-byte aligned");
+    return head_nmse(c, o_full, o_sparse, lay, nullptr, dev_err, err_stride, weight, stream);
 }
 
 saf_status_t saf_head_pairs(const saf_ctx_t *cc, const saf_head_plan_t *head, int32_t corr_kc, int64_t *pairs) {

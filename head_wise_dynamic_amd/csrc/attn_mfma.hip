@@ -80,6 +80,10 @@ __device__ __forceinline__ RowMap make_rowmap(const HeadWork &w, const Geom &g, 
 
 constexpr int kAttnThreads = 256;  // 4 waves x 64 query rows
 
+// DENSE = true is the dense flash-attention kernel: every head attends to all
+// N keys, so key tiles are contiguous token ranges [kt, kt + 64): no key-set
+// enumeration, no per-key validity tests except on the ragged last tile.
+template <bool DENSE>
 __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLaunch L) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][64 * VROW];
@@ -111,11 +115,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const uint16_t *K = (const uint16_t *)L.k + hoff;
     const uint16_t *V = (const uint16_t *)L.v + hoff;
 
-    const int64_t count = key_count(w, g, rm.qsel);
+    const int64_t count = DENSE ? g.N : key_count(w, g, rm.qsel);
     const int64_t per = ((count + w.nsplit - 1) / w.nsplit + KT - 1) / KT * KT;
     const int64_t kbeg = (int64_t)split * per;
     const int64_t kend = min<int64_t>(count, kbeg + per);
-    const int64_t first_masked = key_first_masked(w, g);
+    const int64_t first_masked = DENSE ? INT64_MAX : key_first_masked(w, g);
 
     // ---- this wave's 64 query rows as two 32-row B operands (4 k-steps each)
     bool qvalid[2];
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int64_t m = kt + 2 * lp + i;
-                tk[i] = (m < kend) ? key_token(w, g, m, rm.qsel) : -1;
+                tk[i] = (m < kend) ? (DENSE ? m : key_token(w, g, m, rm.qsel)) : -1;
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -387,7 +391,15 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const MfmaLaunch L) 
 
 hipError_t launch_mfma_attention(const MfmaLaunch &L, hipStream_t stream) {
     if (L.total_blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(mfma_attn_kernel, dim3(L.total_blocks), dim3(kAttnThreads), 0, stream, L);
+    // every piece of work a dense head over all rows: the contiguous-key kernel
+    bool dense = true;
+    for (int i = 0; i < L.nwork; ++i)
+        dense = dense && L.work[i].role == DENSE && L.work[i].rows == ROWS_ALL && L.work[i].nsplit == 1 &&
+                !L.work[i].rec_out;
+    if (dense)
+        hipLaunchKernelGGL(mfma_attn_kernel<true>, dim3(L.total_blocks), dim3(kAttnThreads), 0, stream, L);
+    else
+        hipLaunchKernelGGL(mfma_attn_kernel<false>, dim3(L.total_blocks), dim3(kAttnThreads), 0, stream, L);
     return hipGetLastError();
 }
 

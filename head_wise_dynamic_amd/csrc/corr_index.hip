@@ -1104,6 +1104,20 @@ static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, bool cand, hip
     return hipGetLastError();
 }
 
+static bool corr_uses_engine(const CorrBuild &B) {
+    return B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024 && feature_span(B) < 0xFFFFFFFFll;
+}
+
+bool corr_build_lists_rows(const CorrBuild &B) {
+    return !B.per_frame && !B.total_by_frames && corr_uses_engine(B);
+}
+
+void corr_recomputed_list(void *scratch, int64_t Np, int32_t cap, int32_t **rows, uint32_t **count) {
+    const Scratch s = carve(scratch, Np, cap);
+    *rows = s.row_list;
+    *count = s.row_count;
+}
+
 hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     Args A{};
     A.g = B.g;
@@ -1119,7 +1133,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     A.fallback_list_from = -1;
     const int64_t span = feature_span(B);
     A.f_bytes = 2 * span <= 0xFFFF0000ll ? (uint32_t)(2 * span) : 0u;
-    const bool gemm = B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024 && span < 0xFFFFFFFFll;
+    const bool gemm = corr_uses_engine(B);
     A.all_rows_fallback = gemm ? 0 : 1;
     A.s = carve(B.scratch, B.g.Np, B.per_frame ? 0 : B.cap);
     const int64_t Np = B.g.Np;

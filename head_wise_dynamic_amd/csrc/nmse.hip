@@ -1,8 +1,10 @@
 // Per-head approximation error of a sparse output against the full-attention
 // output (SAF3R Sec. 4.2, Eq. 1): for every head h the sums
 //   num_h = sum_{i,c} (O_full[h,i,c] - O_sparse[h,i,c])^2,   den_h = sum O_full^2
-// in fp64, reduced in a fixed order (deterministic).  The offline profiler
-// divides and averages them over its calibration samples.
+// in fp64, reduced in a fixed order (deterministic); optionally the ratio
+// num_h / den_h of Eq. 1, weighted by 1 / (number of calibration samples),
+// added to a per-head accumulator, so that one call per sample leaves E(c),
+// the average over the calibration set, in the accumulator.
 #include "device_util.h"
 
 namespace saf {
@@ -66,7 +68,11 @@ __global__ __launch_bounds__(kNmseThreads) void nmse_partial(const T *ref, const
     }
 }
 
-__global__ void nmse_final(const double *part, int nblocks, int H, double *out) {
+// out (may be null): the two sums per head.  acc (may be null): acc[h *
+// acc_stride] += weight * num / den (IEEE division: a head whose full output
+// is all zero gets a NaN, as the definition has no value there).
+__global__ void nmse_final(const double *part, int nblocks, int H, double *out, double *acc, int64_t acc_stride,
+                           double weight) {
     const int h = blockIdx.x * blockDim.x + threadIdx.x;
     if (h >= H) return;
     double num = 0.0, den = 0.0;
@@ -74,14 +80,18 @@ __global__ void nmse_final(const double *part, int nblocks, int H, double *out) 
         num += part[((int64_t)h * nblocks + b) * 2];
         den += part[((int64_t)h * nblocks + b) * 2 + 1];
     }
-    out[2 * h] = num;
-    out[2 * h + 1] = den;
+    if (out) {
+        out[2 * h] = num;
+        out[2 * h + 1] = den;
+    }
+    if (acc) acc[h * acc_stride] += weight * (num / den);
 }
 
 }  // namespace
 
 hipError_t launch_head_nmse(const Geom &g, const void *ref, const void *test, int64_t head_stride,
-                            int64_t token_stride, double *part, double *out, hipStream_t stream) {
+                            int64_t token_stride, double *part, double *out, double *acc, int64_t acc_stride,
+                            double weight, hipStream_t stream) {
     const dim3 grid(kNmseBlocks, g.H);
     if (g.dtype == BF16)
         hipLaunchKernelGGL(nmse_partial<uint16_t>, grid, dim3(kNmseThreads), 0, stream, (const uint16_t *)ref,
@@ -89,7 +99,8 @@ hipError_t launch_head_nmse(const Geom &g, const void *ref, const void *test, in
     else
         hipLaunchKernelGGL(nmse_partial<float>, grid, dim3(kNmseThreads), 0, stream, (const float *)ref,
                            (const float *)test, head_stride, token_stride, g.N, part);
-    hipLaunchKernelGGL(nmse_final, dim3((g.H + 63) / 64), dim3(64), 0, stream, part, kNmseBlocks, g.H, out);
+    hipLaunchKernelGGL(nmse_final, dim3((g.H + 63) / 64), dim3(64), 0, stream, part, kNmseBlocks, g.H, out, acc,
+                       acc_stride, weight);
     return hipGetLastError();
 }
 

@@ -149,6 +149,10 @@ size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows);
 // total_by_frames total mode (per-frame candidates, then an exact selection)
 size_t corr_raw_total_scratch_bytes(const Geom &g, int32_t K);
 hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream);
+// Total-mode builds on the matrix-core engine list, in their scratch, the rows
+// they recomputed exactly (buffer overflow or an unconfirmed threshold guess).
+bool corr_build_lists_rows(const CorrBuild &B);
+void corr_recomputed_list(void *scratch, int64_t Np, int32_t cap, int32_t **rows, uint32_t **count);
 
 // Block-wise index: blocks of `block` consecutive patches of a frame; block
 // similarity = dot of the blocks' mean unit features (the token cosine
@@ -173,10 +177,12 @@ size_t corr_block_scratch_bytes(const Geom &g, int32_t block, int32_t Df, int32_
 hipError_t launch_corr_blocks(const CorrBlockBuild &B, hipStream_t stream);
 
 // Per-head error sums of Eq. 1 (fp64): out[2h] = sum (ref - test)^2,
-// out[2h + 1] = sum ref^2.  part: 2 * H * kNmseBlocks doubles.  d = 64,
-// rows 16-byte aligned.
+// out[2h + 1] = sum ref^2 (out may be null); acc (may be null):
+// acc[h * acc_stride] += weight * out[2h] / out[2h + 1].  part: 2 * H *
+// kNmseBlocks doubles.  d = 64, rows 16-byte aligned.
 constexpr int kNmseBlocks = 256;
 hipError_t launch_head_nmse(const Geom &g, const void *ref, const void *test, int64_t head_stride,
-                            int64_t token_stride, double *part, double *out, hipStream_t stream);
+                            int64_t token_stride, double *part, double *out, double *acc, int64_t acc_stride,
+                            double weight, hipStream_t stream);
 
 }  // namespace saf

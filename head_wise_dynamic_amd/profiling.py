@@ -7,8 +7,8 @@ each candidate configuration; Eq. 2 then keeps, by progressive
 substitution, the lowest-error configuration whose floating-point work does
 not exceed the baseline's.  Every attention output and every error sum is
 computed by the library's kernels (dense and sparse attention, the per-head
-error reduction); this module only sequences the calls and divides the
-sums.
+error of Eq. 1 averaged over the samples, the pair counts, the Eq. 2
+selection); this module only sequences the calls.
 """
 from __future__ import annotations
 
@@ -56,12 +56,13 @@ def profile_heads(ctx: Context, samples: Sequence[Dict[str, torch.Tensor]], cand
     the chosen configuration index per head."""
     configs: List[Config] = [baseline(sigma)] + [tuple(c) for c in candidates]
     H = ctx.H
-    err = np.zeros((H, len(configs)), dtype=np.float64)
-    sums = None
+    err = None
     for smp in samples:
         q, k, v = smp["q"], smp["k"], smp["v"]
         full = ctx.dense_attention(q, k, v, stream=stream)
         out = torch.empty_like(full)
+        if err is None:
+            err = torch.zeros((H, len(configs)), dtype=torch.float64, device=full.device)
         built = None
         for j, (role, budget, anchor) in enumerate(configs):
             if role == SAF_CORRESPONDENCE and built != budget:
@@ -70,9 +71,8 @@ def profile_heads(ctx: Context, samples: Sequence[Dict[str, torch.Tensor]], cand
             # a correspondence head's budget 0 means "the cached index"
             b = 0 if role == SAF_CORRESPONDENCE else budget
             ctx.sparse_attention([(role, b, anchor, 0)] * H, q, k, v, o=out, stream=stream)
-            sums = ctx.head_nmse(full, out, out=sums, stream=stream)
-            s = sums.cpu().numpy()
-            err[:, j] += s[:, 0] / s[:, 1] / len(samples)
+            ctx.head_nmse_accumulate(full, out, err[:, j], 1.0 / len(samples), stream=stream)
+    err = err.cpu().numpy() if err is not None else np.zeros((H, len(configs)), dtype=np.float64)
     costs = np.array([config_flops(ctx, c) for c in configs], dtype=np.float64)
     choice = np.array([select(err[h], costs) for h in range(H)], dtype=np.int64)
     return dict(configs=configs, errors=err, costs=costs, choice=choice)

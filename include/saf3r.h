@@ -212,6 +212,23 @@ saf_status_t saf_set_corr_index(saf_ctx_t *ctx, const int32_t *dev_idx, int32_t 
  * NULL to query Kc only).  Errors: SAF_ESTATE (no index), SAF_EINVAL. */
 saf_status_t saf_get_corr_index(const saf_ctx_t *ctx, int32_t *dev_out, int32_t *Kc, void *stream);
 
+/* Diagnostics of the last index build (saf_build_corr_index or
+ * saf_build_corr_index_qk in SAF_CORR_TOTAL mode with bf16 operands, the
+ * matrix-core engine): the patch numbers of the rows whose fast pass could not
+ * prove its result exact (a candidate buffer overflowed, or the row's top-K
+ * threshold guessed for the filtered pass was not confirmed) and which were
+ * therefore recomputed exactly.  Writes min(*count, max_rows) patch numbers,
+ * in no particular order, to host_rows (host memory; may be NULL with
+ * max_rows = 0) and the number of such rows to *count.  Unlike the other
+ * calls this one is synchronous: it waits for `stream`, on which the build
+ * must have been enqueued.  The list is the build's own bookkeeping and does
+ * not change the index (Sec. 4.3 defines only the top-K itself).
+ * Errors: SAF_EINVAL (null ctx/count, max_rows < 0, host_rows NULL with
+ * max_rows > 0), SAF_ESTATE (no build, or the last build kept no list: per
+ * frame, block-wise, fp32 features, an imported index), SAF_EHIP. */
+saf_status_t saf_corr_recomputed_rows(saf_ctx_t *ctx, int32_t *host_rows, int32_t max_rows,
+                                      int32_t *count, void *stream);
+
 /* Vertical-line key set of one head (Sec. 4.3): qbar = mean of the N query
  * rows of head `head` (fp32), r_j = qbar . k_j / sqrt(d) (fp32), the top
  * min(K, N) by (r desc, j asc), written ascending to dev_idx_out (int32).
@@ -235,8 +252,14 @@ saf_status_t saf_sparse_attention(saf_ctx_t *ctx, const saf_head_plan_t *plan, c
                                   const int32_t *vert_idx, int64_t vert_ld, void *ws,
                                   size_t ws_bytes, void *stream);
 
-/* Dense global attention over every key (the speedup baseline), all heads.
- * Errors: SAF_EINVAL, SAF_EHIP. */
+/* Dense global attention over every key, all heads: O = softmax(Q K^T /
+ * sqrt(d)) V over the N x N logits that the sparse kernels avoid (the full
+ * pre-softmax attention matrix of Sec. 4.3, whose column means the query
+ * probe reproduces; the "Full" row of Sec. 5.3, Table 6).  This is the
+ * speedup baseline and the reference output of the profiling error of
+ * Eq. 1 (Sec. 4.2).  Layout and dtype as for saf_sparse_attention; ws may be
+ * NULL (no workspace).  Errors: SAF_EINVAL (null or misaligned pointer, bad
+ * layout), SAF_EHIP. */
 saf_status_t saf_dense_attention(saf_ctx_t *ctx, const void *q, const void *k, const void *v,
                                  void *o, saf_layout_t layout, void *ws, size_t ws_bytes,
                                  void *stream);
@@ -256,6 +279,15 @@ saf_status_t saf_set_kernel_timing(saf_ctx_t *ctx, int32_t enable);
 saf_status_t saf_read_kernel_timing(saf_ctx_t *ctx, int32_t max, const char **names, float *ms,
                                     int32_t *count);
 
+/* Testing hook for the error paths: after `allowed` further successful
+ * device allocations by this library (process-wide, every context), each
+ * allocation fails as if the device were out of memory, so the calling entry
+ * point returns SAF_ENOMEM with its message.  allowed < 0 removes the limit
+ * (the default).  A failed index build or copy leaves the previously cached
+ * index untouched when the failure happens before anything is enqueued.
+ * Always returns SAF_OK.  Host only. */
+saf_status_t saf_debug_fail_alloc(int32_t allowed);
+
 /* ---- Offline head profiling (Sec. 4.2) ---------------------------------- */
 
 /* Error sums of Eq. 1 for every head: dev_out[2h] = sum over the head's N x d
@@ -266,6 +298,21 @@ saf_status_t saf_read_kernel_timing(saf_ctx_t *ctx, int32_t max, const char **na
  * Errors: SAF_EINVAL (null pointer, bad layout), SAF_ENOMEM, SAF_EHIP. */
 saf_status_t saf_head_nmse(saf_ctx_t *ctx, const void *o_full, const void *o_sparse, saf_layout_t layout,
                            double *dev_out, void *stream);
+
+/* Eq. 1 for every head, accumulated over calibration samples: with the
+ * sums above, dev_err[h * err_stride] += weight * sum (o_full - o_sparse)^2 /
+ * sum o_full^2 (fp64; a head whose full output is all zero adds NaN, where
+ * the definition has no value).  Called once per calibration sample with
+ * weight = 1 / (number of samples) on a zeroed accumulator, it leaves E(c) of
+ * Eq. 1 -- the expectation over the calibration set of each head's
+ * normalised squared error -- in dev_err (device memory, the caller's; the
+ * stride lets one [H, configurations] table collect every configuration).
+ * Stream-ordered like every other call.  Errors: SAF_EINVAL (null pointer,
+ * bad layout, err_stride < 1, a weight that is negative or not finite),
+ * SAF_ENOMEM, SAF_EHIP. */
+saf_status_t saf_head_nmse_accumulate(saf_ctx_t *ctx, const void *o_full, const void *o_sparse,
+                                      saf_layout_t layout, double weight, double *dev_err,
+                                      int64_t err_stride, void *stream);
 
 /* Query-key pairs one head computes under *head at this geometry (its
  * floating-point work, the cost of Eq. 2, is 4 head_dim per pair).  For a
