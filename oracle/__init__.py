@@ -68,10 +68,15 @@ _lib = None
 
 
 def lib():
+    """The oracle library.  SAF_ORACLE_LIB names another build of oracle.c to
+    load instead (the sanitizer test runs the pins against such a build)."""
     global _lib
     if _lib is None:
-        build(force=False)
-        L = C.CDLL(_LIB)
+        path = os.environ.get("SAF_ORACLE_LIB")
+        if not path:
+            build(force=False)
+            path = _LIB
+        L = C.CDLL(path)
         P = C.c_void_p
         i32, i64, dbl = C.c_int32, C.c_int64, C.c_double
         L.oracle_num_threads.restype = C.c_int
@@ -374,8 +379,14 @@ def block_corr_index(F: np.ndarray, S: int, ns: int, P: int, b: int, K: int, row
 # ---------------------------------------------------------------------------
 # One layer: every head by its role, on a subset of query rows.
 def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int = MODE_TOTAL,
-               rows: Optional[np.ndarray] = None, corr_rows: Optional[Dict[int, np.ndarray]] = None):
+               rows: Optional[np.ndarray] = None, corr_rows: Optional[Dict[int, np.ndarray]] = None,
+               vert_sets: Optional[Dict[int, np.ndarray]] = None):
     """Key sets per head for the given query rows, from the oracle's own selection.
+
+    corr_rows / vert_sets supply index rows (patch number -> token ids) and
+    vertical key sets (head -> token ids) selected elsewhere, e.g. sets that a
+    test has already checked against the oracle's scores; whatever is not
+    supplied is selected here.
 
     Returns (per-head (row_set, sets), corr rows dict, vertical info dict)."""
     S, ns, P, N, T = geom.S, geom.ns, geom.P, geom.N, geom.T
@@ -401,8 +412,12 @@ def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int =
             sets = [scan_set(S, ns, P, budget)]
             row_set = np.zeros(rows.size, dtype=np.int64)
         elif role == ROLE_VERTICAL:
-            ids, r, kth, nxt = vertical_index(q[h], k[h], budget)
-            vert[h] = dict(ids=ids, scores=r, kth=kth, next=nxt)
+            if vert_sets is not None and h in vert_sets:
+                ids = np.asarray(vert_sets[h], dtype=np.int64)
+                vert[h] = dict(ids=ids)
+            else:
+                ids, r, kth, nxt = vertical_index(q[h], k[h], budget)
+                vert[h] = dict(ids=ids, scores=r, kth=kth, next=nxt)
             sets = [ids]
             row_set = np.zeros(rows.size, dtype=np.int64)
         elif role == ROLE_CORR_STRIDE:
@@ -445,10 +460,10 @@ def layer_sets(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int =
 
 def layer(geom, plan, q, k, v, dino=None, corr_K: int = 0, corr_mode: int = MODE_TOTAL,
           rows: Optional[np.ndarray] = None, corr_rows: Optional[Dict[int, np.ndarray]] = None,
-          heads: Optional[Iterable[int]] = None):
+          heads: Optional[Iterable[int]] = None, vert_sets: Optional[Dict[int, np.ndarray]] = None):
     """Oracle outputs [H][nrows, d] (float64) for the listed query rows."""
     rows = np.arange(geom.N, dtype=np.int64) if rows is None else _i64(rows)
-    sets, corr, vert = layer_sets(geom, plan, q, k, v, dino, corr_K, corr_mode, rows, corr_rows)
+    sets, corr, vert = layer_sets(geom, plan, q, k, v, dino, corr_K, corr_mode, rows, corr_rows, vert_sets)
     heads = range(geom.H) if heads is None else heads
     outs = {}
     for h in heads:

@@ -5,8 +5,10 @@ passed in, correspondence index imported), so outputs compare exactly as the
 definition states; the tolerance is max-abs 2e-2 for bf16 and 1e-4 for fp32.
 Index parity: the GPU-built vertical sets and correspondence rows must equal
 the oracle's up to near-ties (|s_K - s_K+1| < 1e-5), checked as a band rule.
-End to end: with GPU-built sets, every head/row whose set matches the
-oracle's set compares element-wise as above.
+End to end: the GPU-built sets pass the band rule, the oracle evaluates
+attention on exactly those sets, and every row of every head compares
+element-wise as above.  Full-size index parity and the S = 100 / S = 500
+layers on GPU-built sets are in test_gpu_full_size.py.
 """
 import numpy as np
 import pytest
@@ -16,7 +18,8 @@ import oracle
 from workload import (Geometry, make_geometry_inputs, make_inputs, sample_rows, ROLE_CORRESPONDENCE,
                       ROLE_DENSE, ROLE_POSITION, ROLE_SCANNING, ROLE_VERTICAL)
 
-from helpers import band_check, say, to_dev, to_host_f64, tol, torch_dtype
+from helpers import (band_check, band_check_corr_rows, check_index_structure, index_rows_to_check, patch_rows_of,
+                     say, to_dev, to_host_f64, tol, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -148,9 +151,31 @@ def test_small_index_sets(S, ns, P, dtype):
     ctx.close()
 
 
+def _gpu_sets_checked(ctx, w, q, k, rows=None):
+    """GPU-built sets, each checked against the oracle's scores by the band
+    rule: the vertical sets of every vertical head and the index rows of the
+    patch rows among `rows` (default: every row).  Returns (corr rows dict,
+    vertical sets dict) for the oracle to evaluate attention on."""
+    g = w.geom
+    vsets = {}
+    for h in w.heads(ROLE_VERTICAL):
+        K = w.plan[h][1]
+        gv = ctx.build_vertical_index(q, k, h, K).cpu().numpy()
+        _, r, _, _ = oracle.vertical_index(w.q[h], w.k[h], K)
+        band_check(r, gv, K)
+        vsets[h] = gv.astype(np.int64)
+    corr = {}
+    if w.heads(ROLE_CORRESPONDENCE):
+        gidx = ctx.get_corr_index().cpu().numpy()
+        pr = np.arange(g.Np) if rows is None else patch_rows_of(g, rows)
+        corr = band_check_corr_rows(w, gidx, pr, w.corr_K)
+    return corr, vsets
+
+
 @pytest.mark.parametrize("S,ns,P,dtype", SMALL[:3])
 def test_small_layer_end_to_end(S, ns, P, dtype):
-    """GPU-built sets; heads whose sets match the oracle compare element-wise."""
+    """GPU-built sets (band-checked against the oracle's scores); the oracle
+    evaluates attention on those sets and every row of every head compares."""
     saf = _saf()
     w = _small_workload(S, ns, P, dtype)
     g = w.geom
@@ -160,28 +185,13 @@ def test_small_layer_end_to_end(S, ns, P, dtype):
     ctx.build_corr_index(to_dev(w.dino), w.corr_K)
     o = ctx.sparse_attention(w.plan, q, k, v)
     torch.cuda.synchronize()
-    gidx = ctx.get_corr_index().cpu().numpy()
+    corr, vsets = _gpu_sets_checked(ctx, w, q, k)
     rows = np.arange(g.N)
-    oidx = _full_corr_index(w)
-    same_rows = np.all(gidx == oidx, axis=1)
-    heads = []
-    for h, (role, budget, _, _) in enumerate(w.plan):
-        if role == ROLE_VERTICAL:
-            ids, _, _, _ = oracle.vertical_index(w.q[h], w.k[h], budget)
-            gv = ctx.build_vertical_index(q, k, h, budget).cpu().numpy()
-            if not np.array_equal(ids, gv):
-                continue
-        heads.append(h)
-    corr = {u: oidx[u] for u in range(g.Np)}
-    # correspondence heads: only rows whose GPU index row equals the oracle's
-    t = rows % g.T
-    ok_rows = rows[(t < g.ns) | same_rows[np.clip((rows // g.T) * g.P + t - g.ns, 0, g.Np - 1)]]
-    assert ok_rows.size > 0.9 * g.N
-    outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, corr_K=w.corr_K, rows=ok_rows,
-                              corr_rows=corr, heads=heads)
+    outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, corr_K=w.corr_K, rows=rows,
+                              corr_rows=corr, vert_sets=vsets)
     got = to_host_f64(o)
-    for h in heads:
-        err = np.max(np.abs(got[h][ok_rows] - outs[h]))
+    for h, ref in outs.items():
+        err = np.max(np.abs(got[h] - ref))
         assert err <= tol(w), (h, err)
     ctx.close()
 
@@ -233,6 +243,9 @@ def test_config1_tiny_fp32_full():
 
 
 def _big_config(cid, n_rows, n_corr_rows):
+    """Output parity with the oracle's own sets (vertical sets passed in, the
+    oracle's index rows imported for the sampled rows) in the benchmark's
+    launch configuration, after index parity on n_corr_rows index rows."""
     saf = _saf()
     w = make_inputs(cid)
     g = w.geom
@@ -240,24 +253,12 @@ def _big_config(cid, n_rows, n_corr_rows):
     ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
     q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
     dino = to_dev(w.dino)
-    # index parity: every vertical head, sampled correspondence rows
-    for h in w.heads(ROLE_VERTICAL):
-        K = w.plan[h][1]
-        say(f"config {cid} vertical head {h}")
-        gv = ctx.build_vertical_index(q, k, h, K).cpu().numpy()
-        _, r, _, _ = oracle.vertical_index(w.q[h], w.k[h], K)
-        band_check(r, gv, K)
     say(f"config {cid} corr index build")
     ctx.build_corr_index(dino, w.corr_K)
     gidx = ctx.get_corr_index().cpu().numpy()
-    crow = np.random.default_rng(cid).choice(g.Np, n_corr_rows, replace=False)
-    sc = oracle.corr_scores(w.dino, g.S, g.P, crow)
-    frame = np.arange(g.Np) // g.P
-    for i, u in enumerate(crow):
-        gp = (gidx[u] // g.T) * g.P + gidx[u] % g.T - g.ns
-        band_check(np.nan_to_num(sc[i], nan=-np.inf), gp, w.corr_K, valid=frame != frame[u])
-    # output parity with the oracle's sets (vertical passed in; the oracle's
-    # index rows are imported for the sampled rows, the GPU's elsewhere)
+    if n_corr_rows:
+        check_index_structure(g, gidx, w.corr_K)
+        band_check_corr_rows(w, gidx, index_rows_to_check(g, n_corr_rows, seed=cid), w.corr_K)
     vert, corr = _oracle_sets(w, rows)
     full = gidx.copy()
     for u, r in corr.items():
@@ -271,17 +272,20 @@ def _big_config(cid, n_rows, n_corr_rows):
 
 
 def test_config2_sampled():
-    _big_config(2, 4096, 48)
+    _big_config(2, 4096, 512)
 
 
 def test_config3_sampled():
-    _big_config(3, 1024, 24)
+    # index parity at S = 100 lives in test_gpu_full_size.py
+    _big_config(3, 1024, 0)
 
 
 def test_config4_stack_reuses_index_across_layers():
     """24-layer stack workload: the correspondence index is built once from
     the DINO features and reused by a regular layer and a correspondence-heavy
-    layer (6 correspondence heads); vertical sets are rebuilt per layer."""
+    layer (6 correspondence heads); vertical sets are rebuilt per layer.  The
+    GPU-built sets of the sampled rows pass the band rule and every sampled
+    row of every head compares with the oracle on those sets."""
     saf = _saf()
     layers = [make_inputs(4, layer=9), make_inputs(4, layer=10)]
     g = layers[0].geom
@@ -290,82 +294,20 @@ def test_config4_stack_reuses_index_across_layers():
     ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
     say("config 4: index build (once)")
     ctx.build_corr_index(to_dev(layers[0].dino), layers[0].corr_K)
-    gidx = ctx.get_corr_index().cpu().numpy()
     rows = sample_rows(g, 512, seed=4)
-    t = rows % g.T
-    pr = (rows // g.T) * g.P + t - g.ns
-    patch_rows = pr[t >= g.ns]
-    oidx, _, _ = oracle.corr_index(layers[0].dino, g.S, g.ns, g.P, layers[0].corr_K, patch_rows)
-    same = {int(u): np.array_equal(gidx[u], r) for u, r in zip(patch_rows, oidx)}
-    assert np.mean(list(same.values())) > 0.8
-    ok_rows = np.array([i for i, ti, u in zip(rows, t, pr) if ti < g.ns or same[int(u)]])
-    corr = {int(u): r for u, r in zip(patch_rows, oidx)}
+    corr = None
     for w in layers:
         q, k, v = to_dev(w.q), to_dev(w.k), to_dev(w.v)
         say(f"config 4: {w.name}")
         o = ctx.sparse_attention(w.plan, q, k, v)
         torch.cuda.synchronize()
-        heads = []
-        for h, (role, budget, _, _) in enumerate(w.plan):
-            if role == ROLE_VERTICAL:
-                ids, r, _, _ = oracle.vertical_index(w.q[h], w.k[h], budget)
-                gv = ctx.build_vertical_index(q, k, h, budget).cpu().numpy()
-                band_check(r, gv, budget)
-                if not np.array_equal(ids, gv):
-                    continue
-            heads.append(h)
-        outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, corr_K=w.corr_K, rows=ok_rows,
-                                  corr_rows=corr, heads=heads)
+        c, vsets = _gpu_sets_checked(ctx, w, q, k, rows=rows if corr is None else rows[:0])
+        corr = c if corr is None else corr
+        outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, corr_K=w.corr_K, rows=rows,
+                                  corr_rows=corr, vert_sets=vsets)
         got = to_host_f64(o)
-        for h in heads:
-            err = np.max(np.abs(got[h][ok_rows] - outs[h]))
+        for h, ref in outs.items():
+            err = np.max(np.abs(got[h][rows] - ref))
             assert err <= tol(w), (w.name, h, err)
         del q, k, v, o
-    ctx.close()
-
-
-def test_config5_long_sequence_sampled():
-    """S = 500 frames (N = 650,500): one head per role drawn, sampled rows."""
-    saf = _saf()
-    heads = [0, 4, 7, 10]  # position, vertical, correspondence, scanning
-    w = make_inputs(5, heads=heads)
-    g = w.geom
-    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
-    q, k, v, dino = to_dev(w.q), to_dev(w.k), to_dev(w.v), to_dev(w.dino)
-    say("config 5: vertical index")
-    K4 = w.plan[4][1]
-    gv = ctx.build_vertical_index(q, k, 4, K4).cpu().numpy()
-    ids, r, _, _ = oracle.vertical_index(w.q[4], w.k[4], K4)
-    band_check(r, gv, K4)
-    say("config 5: index build")
-    ctx.build_corr_index(dino, w.corr_K)
-    gidx = ctx.get_corr_index().cpu().numpy()
-    crow = np.random.default_rng(5).choice(g.Np, 12, replace=False)
-    sc = oracle.corr_scores(w.dino, g.S, g.P, crow)
-    frame = np.arange(g.Np) // g.P
-    for i, u in enumerate(crow):
-        gp = (gidx[u] // g.T) * g.P + gidx[u] % g.T - g.ns
-        band_check(np.nan_to_num(sc[i], nan=-np.inf), gp, w.corr_K, valid=frame != frame[u])
-    # rows: a few special rows, frame 0 edges, random patch rows
-    rng = np.random.default_rng(55)
-    rows = np.unique(np.concatenate([[0, 4, g.T, g.N - g.T, g.N - 1], np.arange(g.ns, g.ns + 8),
-                                     rng.choice(g.N, 192, replace=False)]))
-    t = rows % g.T
-    pr = (rows // g.T) * g.P + t - g.ns
-    oidx, _, _ = oracle.corr_index(w.dino, g.S, g.ns, g.P, w.corr_K, pr[t >= g.ns])
-    full = gidx.copy()
-    full[pr[t >= g.ns]] = oidx
-    ctx.set_corr_index(torch.from_numpy(full.astype(np.int32)).cuda())
-    vt = torch.zeros((g.H, len(ids)), dtype=torch.int32)
-    vt[4] = torch.from_numpy(ids.astype(np.int32))
-    say("config 5: layer with oracle sets")
-    o = ctx.sparse_attention(w.plan, q, k, v, vert_idx=vt.cuda())
-    torch.cuda.synchronize()
-    corr = {int(u): rr for u, rr in zip(pr[t >= g.ns], oidx)}
-    outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, corr_K=w.corr_K, rows=rows,
-                              corr_rows=corr, heads=heads)
-    got = to_host_f64(o)
-    for h in heads:
-        err = np.max(np.abs(got[h][rows] - outs[h]))
-        assert err <= tol(w), (h, err)
     ctx.close()

@@ -1,7 +1,8 @@
 """Offline head profiling on the GPU (SAF3R Sec. 4.2) vs the CPU oracle.
 
 * the per-head error sums of Eq. 1 from the library's reduction kernel equal
-  the oracle's NMSE of the same outputs (relative 1e-9);
+  the oracle's NMSE of the same outputs (relative 1e-9), and so does the
+  library's own Eq. 1 averaged over samples;
 * the whole search (baseline + candidates, errors averaged over samples,
   Eq. 2 selection) on fp32 workloads: every error within 1e-4 relative (or
   1e-7 absolute) of the oracle's, computed from the oracle's own outputs,
@@ -59,6 +60,39 @@ def test_head_error_sums_match_oracle(dtype, nhd):
         assert got == pytest.approx(want, rel=1e-9, abs=1e-15), h
     assert sums[5, 0] == 0.0
     assert sums[3, 0] / sums[3, 1] == pytest.approx(1.0, rel=1e-12)
+    ctx.close()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_head_error_accumulates_eq1_over_samples(dtype):
+    """The library's Eq. 1: per head, the normalised squared error averaged
+    over calibration samples (weight 1/n per sample), written into a strided
+    column of an [H, configurations] table, against the oracle's NMSE."""
+    saf = _saf()
+    S, ns, P, H, d = 2, 5, 150, 16, 64
+    N = S * (ns + P)
+    ctx = saf.Context(S, ns, P, H, d, dtype)
+    g = torch.Generator().manual_seed(7)
+    pairs = []
+    for i in range(3):
+        a = torch.randn(H, N, d, generator=g)
+        b = a + (0.02 + 0.05 * i) * torch.randn(H, N, d, generator=g)
+        b[2] = 0.0
+        pairs.append((a.to(dtype), b.to(dtype)))
+    table = torch.full((H, 4), 7.0, dtype=torch.float64, device="cuda")
+    table[:, 2] = 0.0
+    say(f"Eq. 1 accumulated over 3 samples {dtype}")
+    for a, b in pairs:
+        ctx.head_nmse_accumulate(a.cuda(), b.cuda(), table[:, 2], 1.0 / len(pairs))
+    got = table.cpu().numpy()
+    for h in range(H):
+        want = sum(oprof.nmse(a[h].float().double().numpy(), b[h].float().double().numpy())
+                   for a, b in pairs) / len(pairs)
+        assert got[h, 2] == pytest.approx(want, rel=1e-9, abs=1e-15), h
+    assert got[2, 2] == pytest.approx(1.0, rel=1e-12)
+    assert np.all(got[:, [0, 1, 3]] == 7.0)          # other columns untouched
+    with pytest.raises(saf.SafError):
+        ctx.head_nmse_accumulate(pairs[0][0].cuda(), pairs[0][1].cuda(), table[:, 0], -1.0)
     ctx.close()
 
 

@@ -1,8 +1,9 @@
 """Correspondence index from one head's logits (q_i . k_j) on the HIP path vs
 the CPU oracle.  Index parity: band rule on the oracle's fp64 logits with a
 band of 1e-4 (fp32 accumulation of d = 64 products of |q|, |k| ~ 10 carries
-errors ~1e-5); end to end: a layer whose correspondence heads use the index
-matches the oracle element-wise on rows whose index rows agree."""
+errors ~1e-5); end to end: a layer whose correspondence heads use the index matches the
+oracle element-wise on every row, the oracle evaluating attention on the
+GPU's band-checked rows.  The S = 100 check is in test_gpu_full_size.py."""
 import numpy as np
 import pytest
 import torch
@@ -86,33 +87,14 @@ def test_qk_index_layer_end_to_end():
     o = ctx.sparse_attention(w.plan, q, k, v)
     torch.cuda.synchronize()
     gidx = ctx.get_corr_index().cpu().numpy()
-    oidx, _ = oracle.qk_index(w.q[0], w.k[0], g.S, g.ns, g.P, 16, np.arange(g.Np))
-    same = np.all(gidx == oidx, axis=1)
+    # every row passes the band rule; the oracle then evaluates attention on
+    # the GPU's rows and every row of every head compares
+    _check(w, 0, gidx, np.arange(g.Np), 16, 0)
     rows = np.arange(g.N)
-    t = rows % g.T
-    pu = np.clip((rows // g.T) * g.P + t - g.ns, 0, g.Np - 1)
-    ok_rows = rows[(t < g.ns) | same[pu]]
-    assert ok_rows.size > 0.9 * g.N
-    corr = {u: oidx[u] for u in range(g.Np)}
-    outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, rows=ok_rows, corr_rows=corr)
+    corr = {u: gidx[u].astype(np.int64) for u in range(g.Np)}
+    outs, _, _ = oracle.layer(g, w.plan, w.q, w.k, w.v, w.dino, rows=rows, corr_rows=corr)
     got = to_host_f64(o)
     for h in outs:
-        err = np.max(np.abs(got[h][ok_rows] - outs[h]))
+        err = np.max(np.abs(got[h] - outs[h]))
         assert err <= tol(w), (h, err)
-    ctx.close()
-
-
-def test_qk_index_s100_sampled():
-    """S=100: the index from the first correspondence head, K = 256; sampled rows."""
-    saf = _saf()
-    w = make_inputs(3, dino=False)
-    g = w.geom
-    h = w.heads(ROLE_CORRESPONDENCE)[0]
-    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
-    say(f"qk index S=100 head {h}")
-    ctx.build_corr_index_qk(to_dev(w.q), to_dev(w.k), h, 256)
-    gidx = ctx.get_corr_index().cpu().numpy()
-    rows = np.sort(np.random.default_rng(2).choice(g.Np, 24, replace=False))
-    rows[0], rows[-1] = 0, g.Np - 1
-    _check(w, h, gidx, rows, 256, 0)
     ctx.close()
