@@ -15,8 +15,12 @@
 // needs one cross-lane exchange (lane ^ 32) per tile.  The key rows of the
 // S^T A-operand are read in a permuted order (bits 2 and 3 of the row index
 // swapped) so that the accumulator registers a lane feeds to the P.V product
-// cover 8 consecutive keys; V^T is then read from LDS as 16-byte rows.
-// O^T = V^T P^T accumulates in fp32 and is normalised at the end.
+// cover 8 consecutive keys.  V stays row-major in LDS and the V^T operand
+// of O^T = V^T P^T is read with the transposing LDS loads of gfx950
+// (ds_read_b64_tr_b16).  O^T accumulates in fp32 and is normalised at the
+// end; the softmax denominator is summed from the same bf16-rounded weights
+// that enter P.V (v_dot2c_f32_bf16), so the output is an exact convex
+// combination of the V rows under those weights.
 // exp is computed as exp2 with log2(e)/sqrt(d) folded into one FMA.
 #include "device_util.h"
 
@@ -26,7 +30,26 @@ namespace {
 constexpr int QT = kQueryTile;
 constexpr int KT = 64;
 constexpr int KROW = 72;   // K tile row in LDS: 64 bf16 + 8 pad
-constexpr int VROW = 72;   // V^T tile row in LDS: 64 keys + 8 pad
+constexpr int VROWS = 72;  // V tile row in LDS (keys row-major): 64 bf16 + 8 pad
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive keys of one channel from a row-major V tile in LDS
+// (ds_read_b64_tr_b16): within each 16-lane group, lane j receives element
+// j % 4 of the 8-byte pieces that lanes j / 4, j / 4 + 4, j / 4 + 8 and
+// j / 4 + 12 address; lane t addresses key row base + t / 4 at channel
+// c0 + 4 (t % 4), so lane j gets keys base .. base + 3 of channel c0 + j.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+}
+
+// sum of the two bf16 halves of w, added to acc (v_dot2c_f32_bf16 with 1.0)
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                           acc, false);
+}
 constexpr int PSTRIDE = kRecStride;  // split partial record: m, l, o[64]
 
 __device__ __forceinline__ int kswz(int row) { return 4 * ((row >> 3) & 1); }
@@ -86,17 +109,15 @@ constexpr int kAttnThreads = 256;  // 4 waves x 64 query rows
 template <bool DENSE>
 __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLaunch L) {
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][64 * VROW];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * VROWS];
     __shared__ float kbias[2][KT];
 
     const Geom &g = L.g;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, gq = lane >> 5;
-    // LDS swizzles (bank-conflict-free stores and reads): K rows r >= 8 of
-    // each group of 16 hold their 16-byte channel chunks XOR 4; the key-pair
-    // words of V^T row c are XOR 4 * ((c >> 3) & 7)
+    // LDS swizzle (bank-conflict-free stores and reads): K rows r >= 8 of
+    // each group of 16 hold their 16-byte channel chunks XOR 4
     const int kx = 4 * ((n >> 2) & 1);  // K rows are read as swap_bits23(n): bit 3 of the row = bit 2 of n
-    const int vx = 4 * (n >> 3);
 
     // ---- locate this work-group's head, query tile and key split
     const int b = blockIdx.x;
@@ -149,7 +170,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
             for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
 
     // ---- tile loader: unit = (key pair p, channel segment seg), one unit
-    // per thread; V^T is written two keys per 32-bit LDS store
+    // per thread; K and V rows are stored as loaded (16 bytes per key row)
     constexpr int kUnits = (KT / 2) * 8 / kAttnThreads;
     u32x4 kreg[kUnits][2], vreg[kUnits][2];
     bool kval[kUnits][2];
@@ -177,28 +198,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
             }
         }
     };
-    auto store_tile = [&](int buf) {
+    // full = every slot of the tile holds a key (dense tiles but the last):
+    // no zeroing of empty slots, no bias entries (wave-uniform)
+    auto store_tile = [&](int buf, bool full) {
 #pragma unroll
         for (int j = 0; j < kUnits; ++j) {
             const int unit = tid + kAttnThreads * j, lp = unit >> 3, lseg = unit & 7;
             u32x4 kz[2], vz[2];
+            if (DENSE && full) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    kz[i][e] = kval[j][i] ? kreg[j][i][e] : 0u;
-                    vz[i][e] = kval[j][i] ? vreg[j][i][e] : 0u;
+                for (int i = 0; i < 2; ++i) {
+                    kz[i] = kreg[j][i];
+                    vz[i] = vreg[j][i];
                 }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kz[i][e] = kval[j][i] ? kreg[j][i][e] : 0u;
+                        vz[i][e] = kval[j][i] ? vreg[j][i][e] : 0u;
+                    }
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i) *(u32x4 *)(&Ks[buf][(2 * lp + i) * KROW + 8 * (lseg ^ kswz(2 * lp + i))]) = kz[i];
-            uint32_t *vt = (uint32_t *)&Vt[buf][(8 * lseg) * VROW] + (lp ^ (4 * lseg));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // channels 2e and 2e+1 of the two keys
-                vt[(2 * e) * (VROW / 2)] = __builtin_amdgcn_perm(vz[1][e], vz[0][e], 0x05040100u);
-                vt[(2 * e + 1) * (VROW / 2)] = __builtin_amdgcn_perm(vz[1][e], vz[0][e], 0x07060302u);
-            }
-            if (lseg == 0) {
+            for (int i = 0; i < 2; ++i) *(u32x4 *)(&Vs[buf][(2 * lp + i) * VROWS + 8 * lseg]) = vz[i];
+            if (!(DENSE && full) && lseg == 0) {
                 kbias[buf][2 * lp] = kval[j][0] ? 0.f : -INFINITY;
                 kbias[buf][2 * lp + 1] = kval[j][1] ? 0.f : -INFINITY;
             }
@@ -208,7 +234,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const int64_t ntiles = (kend - kbeg + KT - 1) / KT;
     if (ntiles > 0) {
         load_tile(kbeg);
-        store_tile(0);
+        store_tile(0, kbeg + KT <= kend);
     }
     // every load so far (Q, the first tile) complete on every path: the
     // compiler's wait analysis is not path-sensitive, and a Q load it
@@ -227,17 +253,14 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         f32x16 s[2][2];
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[bb][qb][r] = 0.f;
             const uint16_t *krow = &Ks[buf][(32 * bb + swap_bits23(n)) * KROW];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const bf16x8 a = *(const bf16x8 *)(krow + 8 * ((2 * c + gq) ^ kx));
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
-                    s[bb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][c], s[bb][qb], 0, 0, 0);
+                    s[bb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][c], c ? s[bb][qb] : f32x16{}, 0,
+                                                                        0, 0);
             }
         }
         // masked slots: ragged tail, or specials already on the scanning stride
@@ -273,16 +296,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
                 m_run[qb] = m_new;
             }
             const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-            float lsum = 0.f;
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(fmaf(s[bb][qb][r], sc, -m_use));
-                    s[bb][qb][r] = p;
-                    lsum += p;
-                }
-            l_run[qb] += lsum;
+                for (int r = 0; r < 16; ++r) s[bb][qb][r] = fast_exp2(fmaf(s[bb][qb][r], sc, -m_use));
         }
 
         // O^T += V^T P^T, four k-steps of 16 keys; each V^T fragment feeds
@@ -299,17 +316,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
                 pk[2] = pack_bf16x2(s[bb][qb][h8 + 4], s[bb][qb][h8 + 5]);
                 pk[3] = pack_bf16x2(s[bb][qb][h8 + 6], s[bb][qb][h8 + 7]);
                 pb[qb] = __builtin_bit_cast(bf16x8, pk);
+                // the row sum from the same rounded weights the P.V product uses
+#pragma unroll
+                for (int w2 = 0; w2 < 4; ++w2) l_run[qb] = add_bf16_pair(pk[w2], l_run[qb]);
             }
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                const bf16x8 a = *(const bf16x8 *)(&Vt[buf][(32 * db + n) * VROW + 2 * ((8 * e + 4 * gq) ^ (16 * db + vx))]);
+                // keys 16 e + 8 gq .. + 7 of channel 32 db + n, as two
+                // transposing reads of four keys each (see lds_read_tr)
+                const int t16 = lane & 15;
+                const uint16_t *vp = &Vs[buf][(16 * e + 8 * gq + (t16 >> 2)) * VROWS + 32 * db + 16 * ((lane >> 4) & 1) +
+                                              4 * (t16 & 3)];
+                const s16x4 lo = lds_read_tr(vp), hi = lds_read_tr(vp + 4 * VROWS);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
                     oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
             }
         }
 
-        if (t + 1 < ntiles) store_tile(buf ^ 1);
+        if (t + 1 < ntiles) store_tile(buf ^ 1, kt + 2 * KT <= kend);
         __syncthreads();
     }
 

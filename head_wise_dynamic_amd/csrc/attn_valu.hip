@@ -21,14 +21,14 @@ namespace {
 template <typename T> struct Lanes;
 template <> struct Lanes<uint16_t> {  // bf16 bits
     static constexpr int EPL = 8, LPR = 8, RPP = 8;
-    __device__ static void load(const uint16_t *p, float *x) {
-        const u32x4 r = *(const u32x4 *)p;
+    __device__ static void unpack_raw(const u32x4 &r, float *x) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = bf16_bits_to_f32(r[i] & 0xFFFFu);
             x[2 * i + 1] = bf16_bits_to_f32(r[i] >> 16);
         }
     }
+    __device__ static void load(const uint16_t *p, float *x) { unpack_raw(*(const u32x4 *)p, x); }
     __device__ static void store(uint16_t *p, const float *x) {
         u32x4 r;
 #pragma unroll
@@ -265,6 +265,162 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(const ValuLaunch L, int6
     }
 }
 
+// Cross-lane steps on the DPP path (no LDS round trip): the sum over the 8
+// lanes of a key row (quad swaps 1 and 2, then the half-row mirror pairs
+// lane i with 7 - i), and the wave-wide maximum of a value that is uniform
+// within each 8-lane group (row rotate by 8, then the four rows' lane 0).
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x += dpp<0x141>(x);  // row_half_mirror
+    return x;
+}
+__device__ __forceinline__ float max_groups(float x) {
+    x = fmaxf(x, dpp<0x128>(x));  // row_ror 8: groups 2r and 2r + 1 of each row
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// ---- bf16 correspondence rows: every head of a group in one pass over the
+// row's index.  One wave per patch row; per chunk of NP * 8 keys the index
+// entries are read once for the group, then the K and the V rows of every
+// head of the group are requested together (unconditional loads from the
+// listed, always valid tokens; slots past the row's end are masked by select
+// afterwards), so a chunk costs one memory round trip for all NH heads.  The
+// softmax of each head runs online over the chunks; lanes of one 8-lane
+// group hold one key row, 16 bytes each.
+template <int NH, int NP>
+__device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u, int64_t tok, int lane) {
+    constexpr int RPP = 8, CH = NP * RPP;
+    const int sub = lane & 7, grp = lane >> 3;
+    const int64_t ts = L.token_stride;
+    const float sc = kLog2e * 0.125f;
+    const uint16_t *Kh[NH], *Vh[NH];
+    float q[NH][8], o[NH][8], m[NH], l[NH];
+    int32_t skip[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const int64_t hoff = (int64_t)hw[h].head * L.head_stride + sub * 8;
+        Kh[h] = (const uint16_t *)L.k + hoff;
+        Vh[h] = (const uint16_t *)L.v + hoff;
+        Lanes<uint16_t>::load((const uint16_t *)L.q + hoff + tok * ts, q[h]);
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+        skip[h] = hw[h].rec_out ? hw[h].budget : 0;
+    }
+    const int32_t *idx = L.corr_idx + u * L.corr_k;
+    const int64_t count = L.corr_k;
+    for (int64_t c0 = 0; c0 < count; c0 += CH) {
+        int32_t t[NP];
+        bool in[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int64_t mi = c0 + p * RPP + grp;
+            in[p] = mi < count;
+            t[p] = idx[in[p] ? mi : count - 1];
+        }
+        u32x4 kr[NH][NP], vr[NH][NP];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) kr[h][p] = *(const u32x4 *)(Kh[h] + (int64_t)t[p] * ts);
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) vr[h][p] = *(const u32x4 *)(Vh[h] + (int64_t)t[p] * ts);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            float s[NP], cm = -INFINITY;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                float kx[8];
+                Lanes<uint16_t>::unpack_raw(kr[h][p], kx);
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot = fmaf(q[h][e], kx[e], dot);
+                dot = sum8(dot);
+                const bool ok = in[p] && !(skip[h] > 0 && t[p] % skip[h] == 0);
+                s[p] = ok ? dot * sc : -INFINITY;
+                cm = fmaxf(cm, s[p]);
+            }
+            cm = max_groups(cm);
+            if (cm == -INFINITY) continue;  // wave-uniform: every slot masked
+            const float m_new = fmaxf(m[h], cm);
+            const float alpha = fast_exp2(m[h] - m_new);
+            float lsum = 0.f;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                s[p] = fast_exp2(s[p] - m_new);
+                lsum += s[p];
+            }
+            l[h] = l[h] * alpha + lsum;
+            m[h] = m_new;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                float vx[8];
+                Lanes<uint16_t>::unpack_raw(vr[h][p], vx);
+                const bool ok = s[p] > 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[h][e] = ok ? fmaf(s[p], vx[e], o[h][e]) : o[h][e];
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int x = 8; x < 64; x <<= 1) {
+            l[h] += __shfl_xor(l[h], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], x);
+        }
+        if (grp != 0) continue;
+        if (hw[h].rec_out) {
+            float *rec = hw[h].part + u * kRecStride;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rec[2 + sub * 8 + e] = o[h][e];
+            if (sub == 0) {
+                rec[0] = m[h];
+                rec[1] = l[h];
+            }
+        } else {
+            const float inv = 1.f / l[h];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] *= inv;
+            Lanes<uint16_t>::store((uint16_t *)L.o + (int64_t)hw[h].head * L.head_stride + tok * ts + sub * 8, o[h]);
+        }
+    }
+}
+
+constexpr int kGatherGroup = 3;  // heads per pass over a row's index
+constexpr int kGatherNP = 4;     // key rows per lane and chunk (32 keys per chunk)
+
+__global__ __launch_bounds__(256) void gather_attn_kernel(const ValuLaunch L) {
+    const Geom &g = L.g;
+    const int lane = threadIdx.x & 63;
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= g.Np) return;
+    const int64_t tok = (u / g.P) * g.T + g.ns + (u % g.P);
+    for (int i0 = 0; i0 < L.nwork; i0 += kGatherGroup) {
+        const int nh = min(kGatherGroup, L.nwork - i0);
+        if (nh == 3)
+            gather_group<3, kGatherNP>(L, L.work + i0, u, tok, lane);
+        else if (nh == 2)
+            gather_group<2, kGatherNP>(L, L.work + i0, u, tok, lane);
+        else
+            gather_group<1, kGatherNP>(L, L.work + i0, u, tok, lane);
+    }
+}
+
 // one wave per (patch row, head), lane = channel
 __global__ __launch_bounds__(256) void union_merge_kernel(const UnionMerge U) {
     const Geom &g = U.g;
@@ -300,7 +456,7 @@ hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t
     }
     const dim3 grid((unsigned)((nrows + 3) / 4));
     if (L.g.dtype == BF16)
-        hipLaunchKernelGGL(valu_attn_kernel<uint16_t>, grid, dim3(256), 0, stream, L, nrows);
+        hipLaunchKernelGGL(gather_attn_kernel, grid, dim3(256), 0, stream, L);
     else
         hipLaunchKernelGGL(valu_attn_kernel<float>, grid, dim3(256), 0, stream, L, nrows);
     return hipGetLastError();

@@ -5,7 +5,7 @@ operation in flight at the next use (`s_waitcnt vmcnt(0)`). In the gather
 kernel that serialised its list, K and V loads; in the shared-key kernel it
 made each tile wait for the next tile's just-issued prefetch before its first
 MFMA. Both kernels are compiled here to gfx950 assembly with the library's own
-flags and checked for those two patterns.
+flags and checked for those patterns.
 """
 import os
 import re
@@ -44,14 +44,26 @@ def _functions(lines):
 
 
 def test_gather_kernel_loads_not_waited_one_by_one(tmp_path):
+    """The bf16 gather kernel requests the K and V rows of a chunk for every
+    head of a group together: 3 heads x 4 rows x (K, V) = 24 loads in one run
+    with no wait between them, and no key-row load waited for on its own."""
     fns = _functions(_assembly("attn_valu.hip", tmp_path))
-    body = [v for k, v in fns.items() if "valu_attn_kernel" in k and "ItE" in k]  # the bf16 instantiation
+    body = [v for k, v in fns.items() if "gather_attn_kernel" in k]
     assert len(body) == 1
     ins = body[0]
-    loads = [i for i, t in enumerate(ins) if t.startswith("global_load")]
-    assert len(loads) >= 24  # 8 list reads, 8 K rows, 8 V rows per chunk
-    serial = [i for i in loads if i + 1 < len(ins) and ins[i + 1].startswith("s_waitcnt") and "vmcnt(0)" in ins[i + 1]]
-    assert not serial, [ins[i] for i in serial]
+    run, best = 0, 0
+    for t in ins:
+        if t.startswith("global_load_dwordx4"):
+            run += 1
+            best = max(best, run)
+        elif t.startswith("s_waitcnt") and "vmcnt" in t:
+            run = 0
+    assert best >= 24, best
+    rows = [i for i, t in enumerate(ins) if t.startswith("global_load_dwordx4")]
+    serial = [i for i in rows if i + 1 < len(ins) and ins[i + 1].startswith("s_waitcnt") and "vmcnt(0)" in ins[i + 1]
+              and not (i > 0 and ins[i - 1].startswith("global_load_dwordx4"))]
+    # a lone 16-byte load followed by a full wait may only be a head's query row
+    assert len(serial) <= 6, [ins[i] for i in serial]
 
 
 def test_shared_key_kernel_mfma_never_waits_for_all_loads(tmp_path):
