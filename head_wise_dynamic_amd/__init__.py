@@ -75,6 +75,7 @@ _PROTOS = {
     "saf_build_vertical_index": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _I32, _I32, _VP, _VP, _SZ, _VP]),
     "saf_sparse_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _I64, _VP, _SZ, _VP]),
     "saf_dense_attention": (C.c_int, [_VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _SZ, _VP]),
+    "saf_sparse_attention_noalloc": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, saf_layout_t, _VP, _I64, _VP]),
     "saf_debug_fail_alloc": (C.c_int, [_I32]),
     "saf_set_kernel_timing": (C.c_int, [_VP, _I32]),
     "saf_read_kernel_timing": (C.c_int, [_VP, _I32, C.POINTER(C.c_char_p), C.POINTER(C.c_float),
@@ -169,6 +170,10 @@ def saf_build_vertical_index(ctx, q, k, layout, head, K, dev_idx_out, ws, ws_byt
 
 def saf_sparse_attention(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, ws, ws_bytes, stream) -> int:
     return lib().saf_sparse_attention(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, ws, ws_bytes, stream)
+
+
+def saf_sparse_attention_noalloc(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, stream) -> int:
+    return lib().saf_sparse_attention_noalloc(ctx, plan, q, k, v, o, layout, vert_idx, vert_ld, stream)
 
 
 def saf_dense_attention(ctx, q, k, v, o, layout, ws, ws_bytes, stream) -> int:

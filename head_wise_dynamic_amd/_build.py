@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libsaf3r.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("SAF_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "attn_mfma.hip", "attn_valu.hip", "vertical.hip", "corr_index.hip", "corr_block.hip", "nmse.hip"]
+SOURCES = ["api.cpp", "attn_mfma.hip", "attn_valu.hip", "vertical.hip", "corr_index.hip", "corr_block.hip", "nmse.hip", "noalloc.cpp"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

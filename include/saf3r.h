@@ -252,6 +252,25 @@ saf_status_t saf_sparse_attention(saf_ctx_t *ctx, const saf_head_plan_t *plan, c
                                   const int32_t *vert_idx, int64_t vert_ld, void *ws,
                                   size_t ws_bytes, void *stream);
 
+/* saf_sparse_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, bit for bit, with its workspace taken from a
+ * static device array of 64 MiB that the library holds on every GPU it runs
+ * on until the process ends, instead of a caller's buffer.  The call itself
+ * allocates nothing and creates no stream or event: every launch goes on
+ * `stream` (the regular entry point runs the gathered rows on a side stream)
+ * and per-launch timing is skipped.  Inputs, outputs, the cached index and
+ * vert_idx are as for saf_sparse_attention.  The array needs no clearing
+ * (every kernel writes the parts it reads first), but every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other contexts, other host threads) race and must be serialised by the
+ * caller.  Errors: as saf_sparse_attention, plus SAF_EUNSUPPORTED when the
+ * plan's workspace (saf_workspace_size, less the vertical sets' share when
+ * vert_idx is given) exceeds 64 MiB. */
+saf_status_t saf_sparse_attention_noalloc(saf_ctx_t *ctx, const saf_head_plan_t *plan, const void *q,
+                                          const void *k, const void *v, void *o, saf_layout_t layout,
+                                          const int32_t *vert_idx, int64_t vert_ld, void *stream);
+
 /* Dense global attention over every key, all heads: O = softmax(Q K^T /
  * sqrt(d)) V over the N x N logits that the sparse kernels avoid (the full
  * pre-softmax attention matrix of Sec. 4.3, whose column means the query
