@@ -310,19 +310,26 @@ def main():
     per_frame = None
     if args.per_frame_k > 0:
         pctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
-        pctx.build_corr_index(dino, args.per_frame_k, mode=saf.SAF_CORR_PER_FRAME)
-        torch.cuda.synchronize()
-        pf = []
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            pctx.build_corr_index(dino, args.per_frame_k, mode=saf.SAF_CORR_PER_FRAME)
-            e1.record(stream)
+
+        def build_ms(mode):
+            pctx.build_corr_index(dino, args.per_frame_k, mode=mode)
             torch.cuda.synchronize()
-            pf.append(e0.elapsed_time(e1))
-        pf_ms = statistics.median(pf)
+            pf = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                pctx.build_corr_index(dino, args.per_frame_k, mode=mode)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                pf.append(e0.elapsed_time(e1))
+            return statistics.median(pf)
+
+        stored_ms = build_ms(saf.SAF_CORR_PER_FRAME_STORED)
+        pf_ms = build_ms(saf.SAF_CORR_PER_FRAME)
         per_frame = {"K_per_frame": args.per_frame_k, "row_length": pctx.corr_k(), "build_ms": round(pf_ms, 3),
-                     "tflops": round(2.0 * g.Np * g.Np * w.Df / (pf_ms * 1e-3) / 1e12, 2)}
+                     "recomputed_rows": len(pctx.recomputed_rows()),
+                     "tflops": round(2.0 * g.Np * g.Np * w.Df / (pf_ms * 1e-3) / 1e12, 2),
+                     "stored_cosines_build_ms": round(stored_ms, 3)}
         pctx.close()
 
     # the index taken from the first correspondence head's logits (K as the

@@ -26,7 +26,7 @@ SAF_F32, SAF_BF16 = 0, 1
 SAF_POSITION, SAF_VERTICAL, SAF_CORRESPONDENCE, SAF_SCANNING, SAF_DENSE = 0, 1, 2, 3, 4
 SAF_CORR_STRIDE = 5
 SAF_BROADCAST = 6
-SAF_CORR_TOTAL, SAF_CORR_PER_FRAME = 0, 1
+SAF_CORR_TOTAL, SAF_CORR_PER_FRAME, SAF_CORR_PER_FRAME_STORED = 0, 1, 2
 
 _STATUS_NAMES = {0: "SAF_OK", -1: "SAF_EINVAL", -2: "SAF_ENOMEM", -3: "SAF_EHIP",
                  -4: "SAF_EUNSUPPORTED", -5: "SAF_ESTATE"}
@@ -330,7 +330,8 @@ class Context:
         return out
 
     def recomputed_rows(self, stream=None):
-        """Patch numbers the last total-mode index build recomputed exactly (sorted)."""
+        """Patch numbers the last index build recomputed exactly (sorted): total
+        mode on the matrix-core engine, or the fused per-frame build."""
         cnt = C.c_int32()
         self._check(saf_corr_recomputed_rows(self._ctx, None, 0, cnt, _stream(stream)))
         n = cnt.value

@@ -386,8 +386,9 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     if (K < 1) return fail(c, SAF_EINVAL, "K %d < 1", K);
     if (Df < 1) return fail(c, SAF_EINVAL, "Df %d < 1", Df);
     if (row_stride < Df) return fail(c, SAF_EINVAL, "dino row stride %lld < Df", (long long)row_stride);
-    if (mode != SAF_CORR_TOTAL && mode != SAF_CORR_PER_FRAME) return fail(c, SAF_EINVAL, "bad mode %d", mode);
-    const bool per_frame = mode == SAF_CORR_PER_FRAME;
+    if (mode != SAF_CORR_TOTAL && mode != SAF_CORR_PER_FRAME && mode != SAF_CORR_PER_FRAME_STORED)
+        return fail(c, SAF_EINVAL, "bad mode %d", mode);
+    const bool per_frame = mode != SAF_CORR_TOTAL;
     if (Df > 4096) return fail(c, SAF_EUNSUPPORTED, "Df %d > 4096", Df);
     const int64_t q = dino_dtype == SAF_BF16 ? 8 : 4;
     if (row_stride % q || !aligned16(dino))
@@ -406,12 +407,6 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
         if (Kc > 1024) return fail(c, SAF_EUNSUPPORTED, "K %d > 1024", Kc);
     }
 
-    const int32_t cap = per_frame ? 0 : saf::corr_capacity(g, Kc);
-    const int32_t chunk_rows = per_frame ? saf::corr_frame_chunk_rows(g) : 0;
-    const size_t sb = per_frame ? saf::corr_frame_scratch_bytes(g, chunk_rows) : saf::corr_scratch_bytes(g, Kc, cap);
-    saf_status_t st = ensure_corr_scratch(c, sb);
-    if (st != SAF_OK) return st;
-    if ((st = ensure_corr_storage(c, Kc)) != SAF_OK) return st;
     saf::CorrBuild B{};
     B.g = g;
     B.dino = dino;
@@ -419,8 +414,17 @@ saf_status_t saf_build_corr_index(saf_ctx_t *c, const void *dino, int32_t dino_d
     B.Df = Df;
     B.row_stride = row_stride;
     B.K = Kk;
-    B.cap = cap;
     B.per_frame = per_frame ? 1 : 0;
+    B.frames_stored = mode == SAF_CORR_PER_FRAME_STORED ? 1 : 0;
+    const int32_t cap = per_frame ? saf::corr_frame_fused_cap(B) : saf::corr_capacity(g, Kc);
+    const int32_t chunk_rows = per_frame && cap == 0 ? saf::corr_frame_chunk_rows(g) : 0;
+    const size_t sb = !per_frame ? saf::corr_scratch_bytes(g, Kc, cap)
+                      : cap > 0  ? saf::corr_frame_fused_scratch_bytes(g, cap)
+                                 : saf::corr_frame_scratch_bytes(g, chunk_rows);
+    saf_status_t st = ensure_corr_scratch(c, sb);
+    if (st != SAF_OK) return st;
+    if ((st = ensure_corr_storage(c, Kc)) != SAF_OK) return st;
+    B.cap = cap;
     B.chunk_rows = chunk_rows;
     B.idx_out = c->corr_idx;
     B.scratch = c->corr_scratch;
@@ -450,11 +454,12 @@ saf_status_t saf_build_corr_index_qk(saf_ctx_t *c, const void *q, const void *k,
     if (g.S < 2) return fail(c, SAF_EINVAL, "correspondence index needs S >= 2");
     if (head < 0 || head >= g.H) return fail(c, SAF_EINVAL, "head %d outside [0, %d)", head, g.H);
     if (K < 1) return fail(c, SAF_EINVAL, "K %d < 1", K);
-    if (mode != SAF_CORR_TOTAL && mode != SAF_CORR_PER_FRAME) return fail(c, SAF_EINVAL, "bad mode %d", mode);
+    if (mode != SAF_CORR_TOTAL && mode != SAF_CORR_PER_FRAME && mode != SAF_CORR_PER_FRAME_STORED)
+        return fail(c, SAF_EINVAL, "bad mode %d", mode);
     saf_status_t st = check_layout(c, lay);
     if (st != SAF_OK) return st;
     if (!aligned16(q) || !aligned16(k)) return fail(c, SAF_EINVAL, "q/k must be 16-byte aligned");
-    const bool per_frame = mode == SAF_CORR_PER_FRAME;
+    const bool per_frame = mode != SAF_CORR_TOTAL;
     int32_t Kk, Kc;
     if (per_frame) {
         if (g.P > saf::kFrameMaxP) return fail(c, SAF_EUNSUPPORTED, "per-frame mode: P %d > %d", g.P, saf::kFrameMaxP);
@@ -484,6 +489,7 @@ saf_status_t saf_build_corr_index_qk(saf_ctx_t *c, const void *q, const void *k,
     B.K = Kk;
     B.cap = cap;
     B.per_frame = per_frame ? 1 : 0;
+    B.frames_stored = per_frame ? 1 : 0;  // q and k differ: no symmetric filtered pass
     B.chunk_rows = chunk_rows;
     B.idx_out = c->corr_idx;
     B.scratch = c->corr_scratch;

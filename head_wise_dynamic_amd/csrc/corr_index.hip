@@ -28,8 +28,20 @@
 // fp32 features (and flagged rows): one 1024-thread block per row computes
 //   every cosine with VALU FMAs into a scratch row and runs an exact block
 //   top-K (radix select + ordered compaction).
-// Per-frame mode (K best of every other frame): the GEMM writes fp32 row
-//   chunks of the cosine matrix, then one wave per (row, frame) selects.
+// Per-frame mode (K best of every other frame), fused (bf16, P >= 256,
+//   K <= 8): the cosine matrix is never stored either.
+//   1. bounds: every row against a 128-patch sample of every frame; the K-th
+//      largest of the 32 lane maxima (each over 4 sampled patches) of a
+//      (row, frame) is attained by K distinct patches of that frame, so it is
+//      a lower bound of the row's K-th best there;
+//   2. the symmetric square once, keeping c >= the bound of (row, frame of
+//      the column) in both directions, into per-row candidate buffers;
+//   3. per row: counting sort of the candidates by frame in LDS, then one
+//      thread per frame keeps the K best in a sorted register list;
+//   4. a row whose buffer overflowed (or a frame short of K) is recomputed
+//      exactly, as in total mode but selected per frame.
+// Per-frame mode otherwise (and on request): the GEMM writes fp32 row chunks
+//   of the cosine matrix, then one wave per (row, frame) selects.
 #include "device_util.h"
 #include "topk_block.h"
 
@@ -97,6 +109,7 @@ struct Args {
     int32_t use_list;        // STORE: tile rows are positions in s.row_list (flagged rows)
     uint32_t f_bytes;        // bytes of F (and of Fc) that rows 0..Np-1 span; 0: over 0xFFFF0000
     int32_t fallback_list_from;  // >= 0: the per-row engine takes s.row_list[from, row_count); -1: every row
+    float *pthr;             // fused per-frame mode: [S][Np] lower bound of row u's K-th best in frame f
 };
 
 // element offset of patch row u in F / Fc
@@ -163,7 +176,34 @@ constexpr int kGroupRows = 4;  // row tiles per group in the tile order
 
 constexpr int kTileElems = CT * CROW;     // one operand tile in LDS (bf16)
 constexpr int kCosThreads = 512;           // 8 waves: 4 (rows) x 2 (columns) of 64 x 128
-enum CosMode { SEED = 0, FILTER = 1, SYM = 2, STORE = 3 };
+//   PFSEED rows [row_lo,row_hi) x a sample of kFrameSample patches of every
+//          frame (sample column c: frame c / kFrameSample): each wave's 128
+//          columns are one frame's sample, and the K-th largest of its lanes'
+//          maxima (each over 4 sampled patches) is a lower bound of the row's
+//          K-th best cosine in that frame, written to A.pthr;
+//   PFSYM  SYM with those per-(row, frame) bounds as filters (per-frame mode).
+enum CosMode { SEED = 0, FILTER = 1, SYM = 2, STORE = 3, PFSEED = 4, PFSYM = 5 };
+constexpr int kFrameSample = 128;
+
+// value of lane (lane ^ j) within each group of 32 lanes (ds_swizzle in its
+// and/or/xor mode: and 0x1F, or 0, xor j)
+__device__ __forceinline__ float xor_lanes32(float x, int j) {
+    const int b = __float_as_int(x);
+    switch (j) {
+    case 1: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (1 << 10)));
+    case 2: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (2 << 10)));
+    case 4: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (4 << 10)));
+    case 8: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (8 << 10)));
+    default: return __int_as_float(__builtin_amdgcn_ds_swizzle(b, 0x1F | (16 << 10)));
+    }
+}
+
+// patch of sample column c (-1 past the last frame); P >= 2 kFrameSample
+// keeps the sampled patches of a frame distinct and evenly spread
+__device__ __forceinline__ int64_t sample_patch(const Geom &g, int64_t c) {
+    const int64_t f = c / kFrameSample, j = c % kFrameSample;
+    return f < g.S ? f * g.P + (j * g.P) / kFrameSample : -1;
+}
 
 // threshold of a row in units of acc * (inverse norm of the other side),
 // lowered by 2^-20 relative so that the filter never drops a value the exact
@@ -179,13 +219,16 @@ __device__ __forceinline__ float scaled_threshold(float th, float inv_self) {
 
 template <int MODE, int NK>
 __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
-    constexpr int kRowCap = MODE == SYM ? 24 : 48;  // survivors staged per row per tile
+    constexpr bool kSym = MODE == SYM || MODE == PFSYM;
+    constexpr int kRowCap = kSym ? 24 : 48;  // survivors staged per row per tile
     // operand tiles: As[2], Bs[2]; after the k-loop the same memory stages the
     // surviving candidates and per-lane accumulator spills
     __shared__ __attribute__((aligned(16))) uint16_t smem[4 * kTileElems];
     uint16_t (*As)[kTileElems] = (uint16_t (*)[kTileElems])smem;
     uint16_t (*Bs)[kTileElems] = (uint16_t (*)[kTileElems])(smem + 2 * kTileElems);
-    __shared__ float r_thr[CT], r_iu[CT], c_thr[CT];
+    // thresholds per row (and per column in the symmetric modes); PFSYM holds
+    // two per row, one for each frame the tile's columns (rows) span
+    __shared__ float r_thr[2 * CT], r_iu[CT], c_thr[2 * CT];
     __shared__ int32_t r_frame[CT];
     __shared__ uint32_t r_cnt[CT], c_cnt[CT];
 
@@ -197,7 +240,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     // ---- tile of this work-group
     int64_t row0, col0, row_hi, col_hi;
     bool diag = false;
-    if (MODE == SYM) {
+    if (kSym) {
         const int nt = (int)((g.Np - A.sym_lo + CT - 1) / CT);
         const int total = nt * (nt + 1) / 2;
         const int per_xcd = (total + 7) / 8;
@@ -241,30 +284,57 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         if (MODE == STORE && A.use_list) return pos < (int64_t)nlist ? (int64_t)A.s.row_list[pos] : -1;
         return pos;
     };
+    // patch of column c (-1: none)
+    auto col_operand = [&](int64_t c) -> int64_t {
+        if (MODE == PFSEED) return c < col_hi ? sample_patch(g, c) : -1;
+        return c < col_hi ? c : -1;
+    };
 
-    if (tid < CT) {
-        const int64_t u = actual_row(row0 + tid);
-        float thr = INFINITY, iu = __builtin_nanf("");  // NaN: no comparison passes
-        int32_t fr = -1;
-        if (u >= 0) {
-            iu = A.s.invn[u];
-            fr = (int32_t)(u / g.P);
-            thr = scaled_threshold(MODE == SYM ? A.s.theta_g[u] : A.s.theta[u], iu);
-        }
-        r_thr[tid] = thr;
-        r_iu[tid] = iu;
-        r_frame[tid] = fr;
-        r_cnt[tid] = 0u;
-    } else if (MODE == SYM) {
-        const int t = tid - CT;
-        const int64_t v = col0 + t;
-        c_thr[t] = v < col_hi ? scaled_threshold(A.s.theta_g[v], A.s.invn[v]) : INFINITY;
-        c_cnt[t] = 0u;
-    }
     const int32_t f_row_lo = (int32_t)(row0 / g.P);
     const int32_t f_row_hi = (int32_t)((min<int64_t>(row0 + CT, row_hi) - 1) / g.P);
     const int32_t f_col_lo = (int32_t)(col0 / g.P);
     const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, col_hi) - 1) / g.P);
+    if (tid < CT) {
+        const int64_t u = actual_row(row0 + tid);
+        float th0 = INFINITY, th1 = INFINITY, iu = __builtin_nanf("");  // NaN: no comparison passes
+        int32_t fr = -1;
+        if (u >= 0) {
+            iu = A.s.invn[u];
+            fr = (int32_t)(u / g.P);
+            if (MODE == PFSYM) {
+                // a tile's columns span at most two frames (P >= CT); the own
+                // frame is never a candidate
+                if (f_col_lo != fr) th0 = scaled_threshold(A.pthr[(int64_t)f_col_lo * g.Np + u], iu);
+                if (f_col_hi != f_col_lo && f_col_hi != fr)
+                    th1 = scaled_threshold(A.pthr[(int64_t)f_col_hi * g.Np + u], iu);
+            } else {
+                th0 = scaled_threshold(MODE == SYM ? A.s.theta_g[u] : A.s.theta[u], iu);
+            }
+        }
+        r_thr[tid] = th0;
+        if (MODE == PFSYM) r_thr[CT + tid] = th1;
+        r_iu[tid] = iu;
+        r_frame[tid] = fr;
+        r_cnt[tid] = 0u;
+    } else if (kSym) {
+        const int t = tid - CT;
+        const int64_t v = col0 + t;
+        float th0 = INFINITY, th1 = INFINITY;
+        if (v < col_hi) {
+            const float iv = A.s.invn[v];
+            if (MODE == PFSYM) {
+                const int32_t fv = (int32_t)(v / g.P);
+                if (f_row_lo != fv) th0 = scaled_threshold(A.pthr[(int64_t)f_row_lo * g.Np + v], iv);
+                if (f_row_hi != f_row_lo && f_row_hi != fv)
+                    th1 = scaled_threshold(A.pthr[(int64_t)f_row_hi * g.Np + v], iv);
+            } else {
+                th0 = scaled_threshold(A.s.theta_g[v], iv);
+            }
+        }
+        c_thr[t] = th0;
+        if (MODE == PFSYM) c_thr[CT + t] = th1;
+        c_cnt[t] = 0u;
+    }
     const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
     f32x16 acc[2][4];
@@ -308,9 +378,9 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = (tid + kCosThreads * i) >> 3, seg = (tid + kCosThreads * i) & 7;
-            const int64_t u = actual_row(row0 + row), v = col0 + row;
+            const int64_t u = actual_row(row0 + row), v = col_operand(col0 + row);
             aoff[i] = u >= 0 ? 2u * ((uint32_t)frow(A, u) + 8u * seg) : kNone;
-            boff[i] = v < col_hi ? 2u * ((uint32_t)frow(A, v) + 8u * seg) : kNone;
+            boff[i] = v >= 0 ? 2u * ((uint32_t)frow(A, v) + 8u * seg) : kNone;
         }
         u32x4 ar[4], br[4];
         auto load = [&](int st) {
@@ -344,9 +414,9 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row = (tid + kCosThreads * i) >> 3;
-            const int64_t u = actual_row(row0 + row), v = col0 + row;
+            const int64_t u = actual_row(row0 + row), v = col_operand(col0 + row);
             aoff[i] = u >= 0 ? (uint32_t)frow(A, u) : 0xFFFFFFFFu;
-            boff[i] = v < col_hi ? (uint32_t)frow(A, v) : 0xFFFFFFFFu;
+            boff[i] = v >= 0 ? (uint32_t)frow(A, v) : 0xFFFFFFFFu;
         }
         u32x4 ar[4], br[4];
         auto load = [&](int k0) {
@@ -386,10 +456,60 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     const int32_t vcol0 = (int32_t)(col0 + lc0);
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-        const int64_t v = vcol0 + 32 * bj;
-        const bool vok = v < col_hi;
+        const int64_t v = col_operand(vcol0 + 32 * bj);
+        const bool vok = v >= 0;
         iv[bj] = vok ? A.s.invn[v] : __builtin_nanf("");  // NaN never passes a comparison
         fv[bj] = vok ? (int32_t)(v / g.P) : -2;
+    }
+
+    if (MODE == PFSEED) {
+        // the wave's 128 columns are the sample of frame fs
+        const int64_t fs = col0 / kFrameSample + wc;
+        if (fs >= g.S) return;
+        // per row, the largest of the lane's 4 sampled cosines
+        float m[2][16];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+                const float iu = r_iu[lr];
+                float x = -INFINITY;
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) {
+                    const float c = acc[bi][bj][r] * (iu * iv[bj]);
+                    x = c > x ? c : x;
+                }
+                m[bi][r] = x;
+            }
+        // bitonic sort of the 32 lanes of each half-wave, descending: lane n
+        // then holds the (n+1)-th largest lane maximum of every row.  The K
+        // lanes with the largest maxima hold K distinct sampled patches at or
+        // above lane K-1's value, so it never exceeds the frame's K-th best.
+#pragma unroll
+        for (int k = 2; k <= 32; k <<= 1)
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                const bool want_max = ((n & j) == 0) == ((n & k) == 0);
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float y = xor_lanes32(m[bi][r], j);
+                        m[bi][r] = want_max ? fmaxf(m[bi][r], y) : fminf(m[bi][r], y);
+                    }
+            }
+        if (n == A.K - 1) {
+            float *dst = A.pthr + fs * g.Np + row0;
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+                    if (r_frame[lr] >= 0) dst[lr] = m[bi][r];
+                }
+        }
+        return;
     }
 
     if (MODE == STORE) {
@@ -437,8 +557,8 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     __syncthreads();  // operand tiles are no longer read: reuse them
     float2 *stage = (float2 *)smem;                              // [CT][kRowCap] forward
     float2 *cstage = stage + CT * kRowCap;                       // [CT][kRowCap] transposed
-    float *xl = (float *)(cstage + (MODE == SYM ? CT * kRowCap : 0)) + (wave * 64 + lane) * 16;
-    const bool transposed = MODE == SYM && !diag;
+    float *xl = (float *)(cstage + (kSym ? CT * kRowCap : 0)) + (wave * 64 + lane) * 16;
+    const bool transposed = kSym && !diag;
     auto push = [&](uint32_t *cnt_lds, float2 *lst, int li, int64_t grow, float2 e) {
         const uint32_t slot = atomicAdd(&cnt_lds[li], 1u);
         if (slot < (uint32_t)kRowCap) {
@@ -450,17 +570,29 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     };
     const float *thr_base = r_thr + 64 * wr + 4 * gq;
     const float *iu_base = r_iu + 64 * wr + 4 * gq;
+    // PFSYM: columns from col_split on (rows from row_split on) lie in the
+    // second frame the tile spans and use the second threshold
+    const int64_t col_split = (int64_t)(f_col_lo + 1) * g.P, row_split = (int64_t)(f_row_lo + 1) * g.P;
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
             uint32_t kf = 0, kt = 0;
-            const float cth = transposed ? c_thr[lc0 + 32 * bj] : INFINITY;
+            const float *tb = thr_base;
+            float cth = transposed ? c_thr[lc0 + 32 * bj] : INFINITY, cth1 = INFINITY;
+            if (MODE == PFSYM) {
+                if (vcol0 + 32 * bj >= col_split) tb += CT;
+                if (transposed) cth1 = c_thr[CT + lc0 + 32 * bj];
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int o = 32 * bi + 8 * (r >> 2) + (r & 3);
-                kf |= (acc[bi][bj][r] * iv[bj] >= thr_base[o]) ? (1u << r) : 0u;
-                if (transposed) kt |= (acc[bi][bj][r] * iu_base[o] >= cth) ? (1u << r) : 0u;
+                kf |= (acc[bi][bj][r] * iv[bj] >= tb[o]) ? (1u << r) : 0u;
+                if (transposed) {
+                    float ct = cth;
+                    if (MODE == PFSYM && row0 + 64 * wr + 4 * gq + o >= row_split) ct = cth1;
+                    kt |= (acc[bi][bj][r] * iu_base[o] >= ct) ? (1u << r) : 0u;
+                }
             }
             if (kf | kt) {
 #pragma unroll
@@ -804,30 +936,22 @@ template <typename T> __global__ __launch_bounds__(256) void cos_store_tiled(con
 // for the K-th key and the index cut among its ties.
 constexpr int kFrameRoundsMaxK = 8;
 
-template <int MAXE, bool CAND>
-__global__ __launch_bounds__(256) void frame_topk(const Args A) {
-    const Geom &g = A.g;
-    const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
-    const int64_t rows = A.row_hi - A.row_lo;
-    if (item >= rows * g.S) return;
-    const int64_t u = A.row_lo + item / g.S;
-    const int32_t gf = (int32_t)(item % g.S), fu = (int32_t)(u / g.P);
-    if (gf == fu) return;
-    const float *src = A.chunk + (u - A.row_lo) * g.Np + (int64_t)gf * g.P;
-    const int ne = (g.P + 63) / 64;
-    uint32_t key[MAXE];  // order_key of the cosine; 0 marks an empty slot
+// Selection of one frame's K best among its P cosines at src (one wave):
+// key[e] receives the order key of patch e * 64 + lane (0: no patch), and
+// bit e of the result is set when that patch is kept.
+template <int MAXE>
+__device__ uint64_t frame_keep(const float *src, int32_t P, uint32_t K, int lane, uint32_t (&key)[MAXE]) {
+    const int ne = (P + 63) / 64;
     // unconditional loads (a slot past the frame reads its last patch and is
     // emptied afterwards), so that all of them are in flight together
     float x[MAXE];
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) x[e] = src[min(e * 64 + lane, g.P - 1)];
+    for (int e = 0; e < MAXE; ++e) x[e] = src[min(e * 64 + lane, P - 1)];
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) {
         const int i = e * 64 + lane;
-        key[e] = (e < ne && i < g.P) ? max(order_key(x[e]), 1u) : 0u;
+        key[e] = (e < ne && i < P) ? max(order_key(x[e]), 1u) : 0u;
     }
-    const uint32_t K = (uint32_t)A.K;
     uint64_t keep = 0;  // bit e: slot e is selected
     if (K <= kFrameRoundsMaxK) {
         for (uint32_t k = 0; k < K; ++k) {
@@ -844,65 +968,48 @@ __global__ __launch_bounds__(256) void frame_topk(const Args A) {
             uint64_t w = ((uint64_t)bk << 32) | (uint32_t)(0x7FFFFFFF - (be < 0 ? 0x7FFFFFFF : be * 64 + lane));
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) {
-                const uint64_t x = __shfl_xor(w, o);
-                w = x > w ? x : w;
+                const uint64_t y = __shfl_xor(w, o);
+                w = y > w ? y : w;
             }
             const uint32_t wi = 0x7FFFFFFFu - (uint32_t)(w & 0xFFFFFFFFu);
             if ((w >> 32) != 0 && (int)(wi & 63) == lane) keep |= 1ull << (wi >> 6);
         }
-    } else {
-        auto count = [&](auto pred) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int e = 0; e < MAXE; ++e)
-                if (e < ne) c += (uint32_t)__popcll(__ballot(key[e] != 0u && pred(e)));
-            return c;
-        };
-        uint32_t thr = 0;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t cand = thr | (1u << bit);
-            if (count([&](int e) { return key[e] >= cand; }) >= K) thr = cand;
-        }
-        const uint32_t need = K - count([&](int e) { return key[e] > thr; });
-        int32_t ithr = INT32_MAX;
-        if (count([&](int e) { return key[e] == thr; }) != need) {
-            uint32_t lo = 0;  // largest index cut with fewer than need tied entries below it
-            for (int bit = 30; bit >= 0; --bit) {
-                const uint32_t cand = lo | (1u << bit);
-                if (count([&](int e) { return key[e] == thr && (uint32_t)(e * 64 + lane) < cand; }) < need)
-                    lo = cand;
-            }
-            ithr = (int32_t)lo;
-        }
+        return keep;
+    }
+    auto count = [&](auto pred) {
+        uint32_t c = 0;
 #pragma unroll
         for (int e = 0; e < MAXE; ++e)
-            if (e < ne && key[e] != 0u && (key[e] > thr || (key[e] == thr && e * 64 + lane <= ithr)))
-                keep |= 1ull << e;
+            if (e < ne) c += (uint32_t)__popcll(__ballot(key[e] != 0u && pred(e)));
+        return c;
+    };
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        if (count([&](int e) { return key[e] >= cand; }) >= K) thr = cand;
     }
-    const int32_t slot = gf - (gf > fu ? 1 : 0);
-    if (CAND) {
-        // candidates (score, patch) for an exact selection over all frames
-        float2 *cand = A.s.cand + u * A.cap + (int64_t)slot * A.K;
-        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        uint32_t pos = 0;
+    const uint32_t need = K - count([&](int e) { return key[e] > thr; });
+    int32_t ithr = INT32_MAX;
+    if (count([&](int e) { return key[e] == thr; }) != need) {
+        uint32_t lo = 0;  // largest index cut with fewer than need tied entries below it
+        for (int bit = 30; bit >= 0; --bit) {
+            const uint32_t cand = lo | (1u << bit);
+            if (count([&](int e) { return key[e] == thr && (uint32_t)(e * 64 + lane) < cand; }) < need)
+                lo = cand;
+        }
+        ithr = (int32_t)lo;
+    }
 #pragma unroll
-        for (int e = 0; e < MAXE; ++e) {
-            if (e < ne) {
-                const bool kp = (keep >> e) & 1ull;
-                const uint64_t m = __ballot(kp);
-                if (kp)
-                    cand[pos + (uint32_t)__popcll(m & below)] =
-                        make_float2(order_key_to_float(key[e]), __int_as_float(gf * g.P + e * 64 + lane));
-                pos += (uint32_t)__popcll(m);
-            }
-        }
-        if (slot == 0 && lane == 0) {
-            A.s.cnt[u] = (uint32_t)((g.S - 1) * A.K);
-            A.s.over[u] = 0u;
-        }
-        return;
-    }
-    int32_t *out = A.idx_out + u * ((int64_t)(g.S - 1) * A.K) + (int64_t)slot * A.K;
+    for (int e = 0; e < MAXE; ++e)
+        if (e < ne && key[e] != 0u && (key[e] > thr || (key[e] == thr && e * 64 + lane <= ithr)))
+            keep |= 1ull << e;
+    return keep;
+}
+
+// tokens of the kept patches of frame gf, ascending, to out[0, K)
+template <int MAXE>
+__device__ void frame_emit(const Geom &g, int32_t gf, uint64_t keep, int lane, int32_t *out) {
+    const int ne = (g.P + 63) / 64;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int32_t tok0 = gf * g.T + g.ns;
     uint32_t pos = 0;
@@ -915,6 +1022,163 @@ __global__ __launch_bounds__(256) void frame_topk(const Args A) {
             pos += (uint32_t)__popcll(m);
         }
     }
+}
+
+// Items are (row, frame) pairs of rows [row_lo, row_hi), whose cosines lie in
+// A.chunk; with A.use_list the rows are positions of s.row_list (flagged
+// rows of the fused mode) and the chunk holds them in list order.
+template <int MAXE, bool CAND>
+__global__ __launch_bounds__(256) void frame_topk(const Args A) {
+    const Geom &g = A.g;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    const int64_t rows = A.row_hi - A.row_lo;
+    if (item >= rows * g.S) return;
+    const int64_t pos = A.row_lo + item / g.S;
+    int64_t u = pos;
+    if (A.use_list) {
+        if (pos >= (int64_t)*A.s.row_count) return;
+        u = A.s.row_list[pos];
+    }
+    const int32_t gf = (int32_t)(item % g.S), fu = (int32_t)(u / g.P);
+    if (gf == fu) return;
+    const float *src = A.chunk + (pos - A.row_lo) * g.Np + (int64_t)gf * g.P;
+    uint32_t key[MAXE];  // order_key of the cosine; 0 marks an empty slot
+    const uint64_t keep = frame_keep<MAXE>(src, g.P, (uint32_t)A.K, lane, key);
+    const int32_t slot = gf - (gf > fu ? 1 : 0);
+    if (CAND) {
+        // candidates (score, patch) for an exact selection over all frames
+        const int ne = (g.P + 63) / 64;
+        float2 *cand = A.s.cand + u * A.cap + (int64_t)slot * A.K;
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        uint32_t p = 0;
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) {
+            if (e < ne) {
+                const bool kp = (keep >> e) & 1ull;
+                const uint64_t m = __ballot(kp);
+                if (kp)
+                    cand[p + (uint32_t)__popcll(m & below)] =
+                        make_float2(order_key_to_float(key[e]), __int_as_float(gf * g.P + e * 64 + lane));
+                p += (uint32_t)__popcll(m);
+            }
+        }
+        if (slot == 0 && lane == 0) {
+            A.s.cnt[u] = (uint32_t)((g.S - 1) * A.K);
+            A.s.over[u] = 0u;
+        }
+        return;
+    }
+    frame_emit<MAXE>(g, gf, keep, lane, A.idx_out + u * ((int64_t)(g.S - 1) * A.K) + (int64_t)slot * A.K);
+}
+
+// ---- fused per-frame mode: a row's candidates from the filtered symmetric
+// pass are bucketed by frame in LDS (counting sort), then one thread per
+// frame keeps the K best by (cosine desc, patch asc) in a sorted register
+// list and writes their tokens ascending.  Every frame must hold at least K
+// candidates (the filter bounds never exceed the K-th best); a row that
+// overflowed its buffer, or a frame short of K, flags the row for an exact
+// recomputation.
+constexpr int kFinThreads = 512;
+constexpr int kFinPer = 24;  // candidates per thread: capacity <= 12288
+template <int KMAX>
+__global__ __launch_bounds__(kFinThreads) void frame_finalize(const Args A) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char fin_lds[];
+    __shared__ int bad;
+    const Geom &g = A.g;
+    const int64_t u = blockIdx.x;
+    const int tid = threadIdx.x;
+    uint32_t *hist = (uint32_t *)fin_lds;                          // [S] entries per frame
+    uint32_t *base = hist + g.S;                                   // [S] bucket starts
+    float2 *ent = (float2 *)(fin_lds + align256(8 * (size_t)g.S));  // [cap] bucketed entries
+    const uint32_t n = A.s.cnt[u];
+    if (A.s.over[u] || n > (uint32_t)A.cap || n == 0u) {
+        if (tid == 0) A.s.over[u] = 1u;
+        return;
+    }
+    for (int f = tid; f < g.S; f += kFinThreads) hist[f] = 0u;
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    const float2 *cand = A.s.cand + u * A.cap;
+    float2 e[kFinPer];
+    uint32_t fp[kFinPer];  // frame << 16 | position in the frame's bucket
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) e[i] = cand[min((uint32_t)(tid + i * kFinThreads), n - 1)];
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+        if ((uint32_t)(tid + i * kFinThreads) < n) {
+            const uint32_t f = (uint32_t)__float_as_int(e[i].y) / (uint32_t)g.P;
+            fp[i] = (f << 16) | atomicAdd(&hist[f], 1u);
+        }
+    }
+    __syncthreads();
+    if (tid < 64) {  // exclusive scan of the bucket sizes, one wave
+        const int per = (g.S + 63) / 64, f0 = tid * per, f1 = min(f0 + per, g.S);
+        uint32_t sum = 0;
+        for (int f = f0; f < f1; ++f) sum += hist[f];
+        uint32_t incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o);
+            if (tid >= o) incl += y;
+        }
+        uint32_t run = incl - sum;
+        for (int f = f0; f < f1; ++f) {
+            base[f] = run;
+            run += hist[f];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+        if ((uint32_t)(tid + i * kFinThreads) < n) ent[base[fp[i] >> 16] + (fp[i] & 0xFFFFu)] = e[i];
+    __syncthreads();
+    const int32_t fu = (int32_t)(u / g.P);
+    const int K = A.K;
+    for (int f = tid; f < g.S; f += kFinThreads) {
+        if (f == fu) continue;
+        const uint32_t c = hist[f], b0 = base[f];
+        if (c < (uint32_t)K) {
+            bad = 1;
+            continue;
+        }
+        // sorted (descending) list of the KMAX best keys: cosine order key
+        // above, complemented patch below (ties go to the lower patch)
+        uint64_t L[KMAX];
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s) L[s] = 0ull;
+        for (uint32_t i = 0; i < c; ++i) {
+            const float2 x = ent[b0 + i];
+            uint64_t key = ((uint64_t)max(order_key(x.x), 1u) << 32) | (0xFFFFFFFFu - (uint32_t)__float_as_int(x.y));
+            if (key > L[KMAX - 1]) {
+#pragma unroll
+                for (int s = 0; s < KMAX; ++s) {
+                    const uint64_t hi = key > L[s] ? key : L[s];
+                    key = key > L[s] ? L[s] : key;
+                    L[s] = hi;
+                }
+            }
+        }
+        // the K best patches in ascending order (odd-even transposition sort)
+        int32_t p[KMAX];
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s) p[s] = s < K ? (int32_t)(0xFFFFFFFFu - (uint32_t)L[s]) : INT32_MAX;
+#pragma unroll
+        for (int pass = 0; pass < KMAX; ++pass)
+#pragma unroll
+            for (int s = pass & 1; s + 1 < KMAX; s += 2) {
+                const int32_t lo = min(p[s], p[s + 1]), hi = max(p[s], p[s + 1]);
+                p[s] = lo;
+                p[s + 1] = hi;
+            }
+        int32_t *out = A.idx_out + u * ((int64_t)(g.S - 1) * K) + (int64_t)(f - (f > fu ? 1 : 0)) * K;
+        const int32_t tok0 = f * g.T + g.ns - f * g.P;
+#pragma unroll
+        for (int s = 0; s < KMAX; ++s)
+            if (s < K) out[s] = tok0 + p[s];
+    }
+    __syncthreads();
+    if (tid == 0 && bad) A.s.over[u] = 1u;
 }
 
 // ---- flagged rows (overflow or a failed guess check) into a list
@@ -944,7 +1208,7 @@ __global__ __launch_bounds__(1024) void select_listed(const Args A, int64_t batc
 }
 
 // ---- exact per-row engine: one 1024-thread block per flagged row
-template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(const Args A) {
+template <typename T, bool PER_FRAME = false> __global__ __launch_bounds__(1024) void fallback_rows(const Args A) {
     __shared__ float fu[4096];
     const Geom &g = A.g;
     float *row = A.s.rowbuf + (int64_t)blockIdx.x * g.Np;
@@ -970,10 +1234,27 @@ template <typename T> __global__ __launch_bounds__(1024) void fallback_rows(cons
             row[v] = (v / g.P == fr) ? -INFINITY : acc * iu * A.s.invn[v];
         }
         __syncthreads();
-        int32_t *out = A.idx_out + u * A.K;
-        block_topk_ascending(row, g.Np, A.K, [&](int64_t pos, int64_t v) {
-            out[pos] = (int32_t)((v / g.P) * g.T + g.ns + (v % g.P));
-        });
+        if constexpr (PER_FRAME) {
+            // the K best of every other frame, one wave per frame
+            const int lane = threadIdx.x & 63;
+            for (int32_t f = (int32_t)(threadIdx.x >> 6); f < g.S; f += 16) {
+                if (f == fr) continue;
+                int32_t *out = A.idx_out + u * ((int64_t)(g.S - 1) * A.K) + (int64_t)(f - (f > fr ? 1 : 0)) * A.K;
+                const float *src = row + (int64_t)f * g.P;
+                if (g.P <= 24 * 64) {
+                    uint32_t key[24];
+                    frame_emit<24>(g, f, frame_keep<24>(src, g.P, (uint32_t)A.K, lane, key), lane, out);
+                } else {
+                    uint32_t key[64];
+                    frame_emit<64>(g, f, frame_keep<64>(src, g.P, (uint32_t)A.K, lane, key), lane, out);
+                }
+            }
+        } else {
+            int32_t *out = A.idx_out + u * A.K;
+            block_topk_ascending(row, g.Np, A.K, [&](int64_t pos, int64_t v) {
+                out[pos] = (int32_t)((v / g.P) * g.T + g.ns + (v % g.P));
+            });
+        }
         __syncthreads();
     }
 }
@@ -1031,6 +1312,32 @@ int32_t corr_frame_chunk_rows(const Geom &g) {
 
 size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows) {
     return carve_head_bytes(g.Np, 0) + align256(sizeof(float) * (size_t)chunk_rows * g.Np);
+}
+
+constexpr size_t kFrameFusedMaxBytes = (size_t)32 << 30;
+constexpr int32_t kFrameFusedMaxK = 8;
+
+size_t corr_frame_fused_scratch_bytes(const Geom &g, int32_t cap) {
+    return carve_head_bytes(g.Np, cap) + align256(sizeof(float) * (size_t)kFallbackBlocks * g.Np) +
+           align256(sizeof(float) * (size_t)g.S * g.Np);
+}
+
+static int64_t feature_span(const CorrBuild &B);
+
+int32_t corr_frame_fused_cap(const CorrBuild &B) {
+    const Geom &g = B.g;
+    if (!B.per_frame || B.frames_stored || B.dino_dtype != BF16 || (B.Df % CK) != 0) return 0;
+    if ((B.dino_cols && B.dino_cols != B.dino) || feature_span(B) >= 0xFFFFFFFFll) return 0;
+    if (g.P < CT || g.P > kFrameMaxP || B.K < 1 || B.K > kFrameFusedMaxK || g.S < 2 || g.S > 4096) return 0;
+    // candidates per (row, frame) passing a bound at the K-th largest of 32
+    // lane maxima of a 128-patch sample: about K (P+1)/129 (1 + K/64) for
+    // ranks in random order; the capacity allows 20 % more plus 512
+    const double per = (double)(g.P + 1) / (kFrameSample + 1) * B.K * (1.0 + B.K / 64.0);
+    int64_t cap = (int64_t)std::ceil((g.S - 1) * per * 1.2) + 512;
+    cap = (cap + 63) / 64 * 64;
+    if (cap > (int64_t)kFinThreads * kFinPer) return 0;
+    if (corr_frame_fused_scratch_bytes(g, (int32_t)cap) > kFrameFusedMaxBytes) return 0;
+    return (int32_t)cap;
 }
 
 size_t corr_raw_total_scratch_bytes(const Geom &g, int32_t K) {
@@ -1104,12 +1411,85 @@ static hipError_t launch_corr_frames(Args &A, const CorrBuild &B, bool cand, hip
     return hipGetLastError();
 }
 
+// Fused per-frame mode: per-(row, frame) bounds from a sampled pass, the
+// symmetric square once filtered by them, per-row frame buckets, then any
+// flagged rows exactly (a cosine row batch on the matrix cores, else the
+// per-row engine).
+static hipError_t launch_corr_frames_fused(Args &A, const CorrBuild &B, hipStream_t stream) {
+    const Geom &g = B.g;
+    const int64_t Np = g.Np;
+    A.cap = B.cap;
+    A.s = carve(B.scratch, Np, A.cap);
+    A.pthr = (float *)((char *)A.s.rowbuf + align256(sizeof(float) * (size_t)kFallbackBlocks * Np));
+    A.seed_cols = 0;
+    A.sym_lo = 0;
+    A.all_rows_fallback = 0;
+    hipLaunchKernelGGL(init_rows<uint16_t>, dim3((unsigned)((Np + 3) / 4)), dim3(256), 0, stream, A);
+    // 1. bounds: every row against kFrameSample patches of every frame
+    A.row_lo = 0;
+    A.row_hi = Np;
+    A.col_lo = 0;
+    A.col_hi = (int64_t)g.S * kFrameSample;
+    {
+        const int64_t tiles = ((Np + CT - 1) / CT) * ((A.col_hi + CT - 1) / CT);
+        if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+        launch_cos<PFSEED>(dim3((unsigned)(8 * ((tiles + 7) / 8))), stream, A);
+        if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+    }
+    // 2. the square once per unordered pair, filtered by the bounds
+    {
+        const int64_t nt = (Np + CT - 1) / CT;
+        const int64_t tiles = nt * (nt + 1) / 2;
+        A.col_lo = 0;
+        A.col_hi = Np;
+        if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+        launch_cos<PFSYM>(dim3((unsigned)(8 * ((tiles + 7) / 8))), stream, A);
+        if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+    }
+    // 3. every row: candidates bucketed by frame, the K best of each
+    const size_t lds = align256(8 * (size_t)g.S) + sizeof(float2) * (size_t)A.cap;
+    hipError_t e;
+    if (A.K <= 4) {
+        e = hipFuncSetAttribute((const void *)frame_finalize<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(frame_finalize<4>, dim3((unsigned)Np), dim3(kFinThreads), lds, stream, A);
+    } else {
+        e = hipFuncSetAttribute((const void *)frame_finalize<8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(frame_finalize<8>, dim3((unsigned)Np), dim3(kFinThreads), lds, stream, A);
+    }
+    // 4. flagged rows: kFixBatches x kFallbackBlocks of them as cosine rows on
+    // the matrix cores, selected per frame; the rest on the per-row engine
+    hipLaunchKernelGGL(list_flagged, dim3((unsigned)((Np + 255) / 256)), dim3(256), 0, stream, A);
+    Args L = A;
+    L.use_list = 1;
+    L.col_lo = 0;
+    L.col_hi = Np;
+    L.chunk = A.s.rowbuf;
+    const int64_t ct = (Np + CT - 1) / CT;
+    const unsigned fb_items = (unsigned)(((int64_t)kFallbackBlocks * g.S + kRowWaves - 1) / kRowWaves);
+    for (int b = 0; b < kFixBatches; ++b) {
+        L.row_lo = (int64_t)b * kFallbackBlocks;
+        L.row_hi = L.row_lo + kFallbackBlocks;
+        launch_cos<STORE>(dim3((unsigned)(8 * ((ct + 7) / 8))), stream, L);
+        if (g.P <= 24 * 64)
+            hipLaunchKernelGGL((frame_topk<24, false>), dim3(fb_items), dim3(256), 0, stream, L);
+        else
+            hipLaunchKernelGGL((frame_topk<64, false>), dim3(fb_items), dim3(256), 0, stream, L);
+    }
+    A.fallback_list_from = kFixBatches * kFallbackBlocks;
+    const unsigned fb = (unsigned)std::min<int64_t>(kFallbackBlocks, Np);
+    hipLaunchKernelGGL((fallback_rows<uint16_t, true>), dim3(fb), dim3(1024), 0, stream, A);
+    return hipGetLastError();
+}
+
 static bool corr_uses_engine(const CorrBuild &B) {
     return B.dino_dtype == BF16 && (B.Df % CK) == 0 && B.K <= 1024 && feature_span(B) < 0xFFFFFFFFll;
 }
 
 bool corr_build_lists_rows(const CorrBuild &B) {
-    return !B.per_frame && !B.total_by_frames && corr_uses_engine(B);
+    if (B.per_frame) return B.cap > 0;
+    return !B.total_by_frames && corr_uses_engine(B);
 }
 
 void corr_recomputed_list(void *scratch, int64_t Np, int32_t cap, int32_t **rows, uint32_t **count) {
@@ -1139,6 +1519,10 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     const int64_t Np = B.g.Np;
     if (B.per_frame) {
         if (B.g.P > kFrameMaxP) return hipErrorInvalidValue;
+        if (B.cap > 0) {
+            if (B.cap != corr_frame_fused_cap(B)) return hipErrorInvalidValue;
+            return launch_corr_frames_fused(A, B, stream);
+        }
         A.all_rows_fallback = 1;  // init_rows: norms only
         const unsigned rb = (unsigned)((Np + 3) / 4);
         if (B.dino_dtype == BF16)

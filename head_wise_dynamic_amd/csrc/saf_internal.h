@@ -127,15 +127,16 @@ struct CorrBuild {
     int32_t Df;
     int64_t row_stride;
     int32_t K;      // kept per row (total mode) or per other frame (per-frame mode), clamped
-    int32_t cap;    // candidate capacity per row (total mode)
+    int32_t cap;    // candidate capacity per row (total mode; fused per-frame mode, 0: stored cosines)
     int32_t per_frame;  // 1: the K best of every other frame, [Np, (S-1) K]
+    int32_t frames_stored;  // per-frame mode: always materialise the cosine rows (no filtered pass)
     int32_t chunk_rows; // per-frame mode: rows whose cosines are materialised at once
     int32_t raw_dot;    // 1: rank by the plain dot product f_u . f_v (no normalisation)
     const void *dino_cols;  // column operand (nullptr: the rows' own features, symmetric)
     int32_t tok_map;    // 1: patch row u lives at token (u / P) T + ns + u % P of a token layout
     int32_t total_by_frames;  // total mode as per-frame candidates + exact selection (short rows)
     int32_t *idx_out;   // [Np, K] or [Np, (S-1) K]
-    void *scratch;      // corr_scratch_bytes() / corr_frame_scratch_bytes()
+    void *scratch;      // corr_scratch_bytes() / corr_frame_scratch_bytes() / corr_frame_fused_scratch_bytes()
     // optional tracing hook: called with begin = 1 / 0 around every cosine
     // GEMM launch (the caller records events on the stream)
     void (*mark)(void *user, int begin, const char *name, hipStream_t stream);
@@ -146,11 +147,18 @@ int32_t corr_capacity(const Geom &g, int32_t K);
 constexpr int32_t kFrameMaxP = 4096;  // per-frame mode: patches per frame the selection holds
 int32_t corr_frame_chunk_rows(const Geom &g);
 size_t corr_frame_scratch_bytes(const Geom &g, int32_t chunk_rows);
+// Fused per-frame mode (a filtered symmetric pass, no stored cosines): the
+// candidate capacity per row, or 0 when B takes the stored-cosine path
+// (fp32 or non-symmetric operands, P < 256, K > 8, a long index row, or
+// scratch beyond the mode's limit).
+int32_t corr_frame_fused_cap(const CorrBuild &B);
+size_t corr_frame_fused_scratch_bytes(const Geom &g, int32_t cap);
 // total_by_frames total mode (per-frame candidates, then an exact selection)
 size_t corr_raw_total_scratch_bytes(const Geom &g, int32_t K);
 hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream);
-// Total-mode builds on the matrix-core engine list, in their scratch, the rows
-// they recomputed exactly (buffer overflow or an unconfirmed threshold guess).
+// Total-mode builds on the matrix-core engine and fused per-frame builds list,
+// in their scratch, the rows they recomputed exactly (buffer overflow, an
+// unconfirmed threshold guess, a frame short of candidates).
 bool corr_build_lists_rows(const CorrBuild &B);
 void corr_recomputed_list(void *scratch, int64_t Np, int32_t cap, int32_t **rows, uint32_t **count);
 

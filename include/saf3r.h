@@ -98,7 +98,7 @@ typedef enum {
 
 /* Correspondence top-K per query: over all other frames together, or K per
  * other frame. */
-typedef enum { SAF_CORR_TOTAL = 0, SAF_CORR_PER_FRAME = 1 } saf_corr_mode_t;
+typedef enum { SAF_CORR_TOTAL = 0, SAF_CORR_PER_FRAME = 1, SAF_CORR_PER_FRAME_STORED = 2 } saf_corr_mode_t;
 
 typedef struct {
     int32_t num_frames;          /* S >= 1 */
@@ -153,15 +153,24 @@ saf_status_t saf_workspace_size(const saf_ctx_t *ctx, const saf_head_plan_t *pla
  *   SAF_CORR_TOTAL:     the first min(K, (S-1)P) over all other frames;
  *                       Kc = that count (at most 1024).
  *   SAF_CORR_PER_FRAME: the first min(K, P) of every other frame (P <= 4096);
- *                       Kc = (S-1) min(K, P).
+ *                       Kc = (S-1) min(K, P).  With bf16 features, Df a
+ *                       multiple of 64, P >= 256 and K <= 8 the cosines are
+ *                       never stored: a pass over a 128-patch sample of
+ *                       every frame bounds each (row, frame)'s K-th best, one
+ *                       pass over the symmetric square keeps what reaches
+ *                       the bounds, and a row short of candidates is
+ *                       recomputed exactly; otherwise as the next mode.
+ *   SAF_CORR_PER_FRAME_STORED: the same index built by writing every row's
+ *                       cosines (fp32, in row chunks of about 512 MB) and
+ *                       selecting each frame's K best from them.
  * Each row of Kc global token indices is stored ascending.  The index is kept
  * in the context and reused by every later saf_sparse_attention call (the
  * cache of Sec. 4.3) until rebuilt.  The device scratch the build needs is
  * owned by the context (allocated on first use, grown when a larger build
  * needs more).
  * Errors: SAF_EINVAL (S < 2, K < 1, Df < 1, bad mode/stride/pointer),
- * SAF_EUNSUPPORTED (Df > 4096, TOTAL with Kc > 1024, PER_FRAME with
- * P > 4096), SAF_ENOMEM. */
+ * SAF_EUNSUPPORTED (Df > 4096, TOTAL with Kc > 1024, the per-frame modes
+ * with P > 4096), SAF_ENOMEM. */
 saf_status_t saf_build_corr_index(saf_ctx_t *ctx, const void *dino, int32_t dino_dtype,
                                   int32_t Df, int64_t dino_row_stride, int32_t K,
                                   int32_t mode, void *stream);
@@ -173,11 +182,13 @@ saf_status_t saf_build_corr_index(saf_ctx_t *ctx, const void *dino, int32_t dino
  * (q_i . k_j desc, token asc) -- the 1/sqrt(d) scale does not change the
  * order -- using head `head` of q and k (context dtype, layout as for
  * attention); TOTAL keeps the first min(K, (S-1)P) (at most 1024), PER_FRAME
- * the first min(K, P) of every other frame.  The result replaces the cached
+ * (or PER_FRAME_STORED, the same build here: q and k differ, so the cosine
+ * rows are always written) the first min(K, P) of every other frame.  The result replaces the cached
  * index exactly like saf_build_corr_index and serves every later
  * correspondence head.
  * Errors: SAF_EINVAL (S < 2, bad head/K/mode/layout/pointer),
- * SAF_EUNSUPPORTED (TOTAL with Kc > 1024, PER_FRAME with P > 4096), SAF_ENOMEM. */
+ * SAF_EUNSUPPORTED (TOTAL with Kc > 1024, the per-frame modes with P > 4096),
+ * SAF_ENOMEM. */
 saf_status_t saf_build_corr_index_qk(saf_ctx_t *ctx, const void *q, const void *k, saf_layout_t layout,
                                      int32_t head, int32_t K, int32_t mode, void *stream);
 
@@ -214,18 +225,20 @@ saf_status_t saf_get_corr_index(const saf_ctx_t *ctx, int32_t *dev_out, int32_t 
 
 /* Diagnostics of the last index build (saf_build_corr_index or
  * saf_build_corr_index_qk in SAF_CORR_TOTAL mode with bf16 operands, the
- * matrix-core engine): the patch numbers of the rows whose fast pass could not
- * prove its result exact (a candidate buffer overflowed, or the row's top-K
- * threshold guessed for the filtered pass was not confirmed) and which were
- * therefore recomputed exactly.  Writes min(*count, max_rows) patch numbers,
+ * matrix-core engine, or saf_build_corr_index's fused SAF_CORR_PER_FRAME
+ * build): the patch numbers of the rows whose fast pass could not prove its
+ * result exact (a candidate buffer overflowed, the row's top-K threshold
+ * guessed for the filtered pass was not confirmed, or a frame kept fewer
+ * than K candidates) and which were therefore recomputed exactly.  Writes min(*count, max_rows) patch numbers,
  * in no particular order, to host_rows (host memory; may be NULL with
  * max_rows = 0) and the number of such rows to *count.  Unlike the other
  * calls this one is synchronous: it waits for `stream`, on which the build
  * must have been enqueued.  The list is the build's own bookkeeping and does
  * not change the index (Sec. 4.3 defines only the top-K itself).
  * Errors: SAF_EINVAL (null ctx/count, max_rows < 0, host_rows NULL with
- * max_rows > 0), SAF_ESTATE (no build, or the last build kept no list: per
- * frame, block-wise, fp32 features, an imported index), SAF_EHIP. */
+ * max_rows > 0), SAF_ESTATE (no build, or the last build kept no list: the
+ * stored-cosine per-frame build, block-wise, fp32 features, an imported
+ * index), SAF_EHIP. */
 saf_status_t saf_corr_recomputed_rows(saf_ctx_t *ctx, int32_t *host_rows, int32_t max_rows,
                                       int32_t *count, void *stream);
 

@@ -9,6 +9,8 @@ GPU-built per-frame index matches the oracle element-wise (max-abs 2e-2 bf16,
 band-checked index rows and vertical sets.  Full-size (S = 100) checks are in
 test_gpu_full_size.py.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -137,3 +139,77 @@ def test_per_frame_layer_end_to_end(S, ns, P, dtype):
         err = np.max(np.abs(got[h] - ref))
         assert err <= tol(w), (h, err)
     ctx.close()
+
+
+# Geometries on the fused path (bf16, Df a multiple of 64, P >= 256, K <= 8):
+# a per-(row, frame) bound from a 128-patch sample of every frame, the
+# symmetric square once filtered by it, per-row frame buckets.
+FUSED = [
+    (2, 0, 256, 64),     # the smallest fused frame: one 256-row tile per frame
+    (4, 5, 700, 64),     # 2800 rows: 11 tiles, the last ragged, tiles across frame boundaries
+    (3, 1, 1500, 128),   # wide frames: 6 column tiles per frame, 128 channels
+]
+
+
+@pytest.mark.parametrize("S,ns,P,Df", FUSED)
+@pytest.mark.parametrize("K", [1, 3, 8])
+def test_fused_per_frame_matches_the_stored_build(S, ns, P, Df, K):
+    """The fused build selects from the same fp32 cosines as the build that
+    stores every cosine row, so the two indices agree row for row (a row that
+    differs must be a near-tie, and both pass the band rule on every row)."""
+    saf = _saf()
+    w = _workload(S, ns, P, "bf16", Df, seed=23)
+    g = w.geom
+    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+    dino = to_dev(w.dino)
+    say(f"fused per-frame index {w.name} K {K}")
+    ctx.build_corr_index(dino, K, mode=saf.SAF_CORR_PER_FRAME)
+    fused = ctx.get_corr_index().cpu().numpy()
+    n_rec = len(ctx.recomputed_rows())
+    say(f"stored per-frame index {w.name} K {K}")
+    ctx.build_corr_index(dino, K, mode=saf.SAF_CORR_PER_FRAME_STORED)
+    stored = ctx.get_corr_index().cpu().numpy()
+    ctx.close()
+    rows = np.arange(g.Np)
+    _check_rows(w, fused, rows, K)
+    same = np.all(fused == stored, axis=1)
+    if not same.all():
+        _check_rows(w, stored, rows[~same], K)
+    assert same.mean() >= 0.99, (same.mean(), n_rec)
+    # random features: the bounds leave every frame its K candidates and no
+    # buffer overflows
+    assert n_rec == 0, n_rec
+
+
+@pytest.mark.parametrize("pattern", ["identical", "zero_rows"])
+def test_fused_per_frame_recomputes_flagged_rows(pattern):
+    """Rows whose candidate buffer overflows are recomputed exactly: with
+    identical features every cosine ties, every frame keeps all P patches and
+    all 1,800 rows overflow (the first 1,024 go through cosine rows on the
+    matrix cores, the other 776 through the per-row engine); with a tenth of
+    the features zero, those rows' cosines are all 0 (the zero-norm rule) and
+    only they overflow.  Tied scores go to the lowest patches."""
+    saf = _saf()
+    S, ns, P, K = 3, 5, 600, 4
+    w = _workload(S, ns, P, "bf16", 64, seed=29)
+    g = w.geom
+    dino = w.dino.copy()
+    if pattern == "identical":
+        dino[:] = dino[0]
+        expect_rec = np.arange(g.Np)
+    else:
+        expect_rec = np.sort(np.random.default_rng(5).choice(g.Np, g.Np // 10, replace=False))
+        dino[expect_rec] = 0
+    ctx = saf.Context(g.S, g.ns, g.P, g.H, g.d, torch.bfloat16)
+    say(f"fused per-frame flagged rows ({pattern})")
+    ctx.build_corr_index(to_dev(dino), K, mode=saf.SAF_CORR_PER_FRAME)
+    gidx = ctx.get_corr_index().cpu().numpy()
+    rec = np.sort(np.asarray(ctx.recomputed_rows(), dtype=np.int64))
+    ctx.close()
+    assert np.array_equal(rec, expect_rec), (rec.size, expect_rec.size)
+    _check_rows(dataclasses.replace(w, dino=dino), gidx, np.arange(g.Np), K)
+    # all-tied rows keep the K lowest patches of every other frame
+    for u in expect_rec:
+        fu = u // g.P
+        exp = np.concatenate([f * g.T + g.ns + np.arange(K) for f in range(g.S) if f != fu])
+        assert np.array_equal(gidx[u], exp), u
