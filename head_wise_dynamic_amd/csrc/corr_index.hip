@@ -36,8 +36,8 @@
 //      a lower bound of the row's K-th best there;
 //   2. the symmetric square once, keeping c >= the bound of (row, frame of
 //      the column) in both directions, into per-row candidate buffers;
-//   3. per row: counting sort of the candidates by frame in LDS, then one
-//      thread per frame keeps the K best in a sorted register list;
+//   3. per row: counting sort of the candidates by frame in LDS, then a few
+//      lanes per frame keep the K best in sorted register lists, merged;
 //   4. a row whose buffer overflowed (or a frame short of K) is recomputed
 //      exactly, as in total mode but selected per frame.
 // Per-frame mode otherwise (and on request): the GEMM writes fp32 row chunks
@@ -1073,9 +1073,9 @@ __global__ __launch_bounds__(256) void frame_topk(const Args A) {
 }
 
 // ---- fused per-frame mode: a row's candidates from the filtered symmetric
-// pass are bucketed by frame in LDS (counting sort), then one thread per
-// frame keeps the K best by (cosine desc, patch asc) in a sorted register
-// list and writes their tokens ascending.  Every frame must hold at least K
+// pass are bucketed by frame in LDS (counting sort), then a group of lanes
+// per frame keeps the K best by (cosine desc, patch asc) and writes their
+// tokens ascending.  Every frame must hold at least K
 // candidates (the filter bounds never exceed the K-th best); a row that
 // overflowed its buffer, or a frame short of K, flags the row for an exact
 // recomputation.
@@ -1135,19 +1135,22 @@ __global__ __launch_bounds__(kFinThreads) void frame_finalize(const Args A) {
     __syncthreads();
     const int32_t fu = (int32_t)(u / g.P);
     const int K = A.K;
-    for (int f = tid; f < g.S; f += kFinThreads) {
-        if (f == fu) continue;
-        const uint32_t c = hist[f], b0 = base[f];
-        if (c < (uint32_t)K) {
-            bad = 1;
-            continue;
-        }
-        // sorted (descending) list of the KMAX best keys: cosine order key
-        // above, complemented patch below (ties go to the lower patch)
+    // G lanes per frame (8 when the frames fit the block that way): lane gl
+    // of a group keeps the KMAX best of the bucket entries gl, gl + G, ... in a
+    // sorted register list of keys (cosine order key above, complemented patch
+    // below, so ties go to the lower patch); the group's lists are then merged
+    // by a butterfly of bitonic merges
+    const int G = g.S * 8 <= kFinThreads ? 8 : g.S * 4 <= kFinThreads ? 4 : g.S * 2 <= kFinThreads ? 2 : 1;
+    const int gl = tid & (G - 1);
+    for (int fb = 0; fb < g.S; fb += kFinThreads / G) {
+        const int f = fb + tid / G;
+        const bool active = f < g.S && f != fu;
+        const uint32_t c = active ? hist[f] : 0u, b0 = active ? base[f] : 0u;
+        if (active && c < (uint32_t)K) bad = 1;
         uint64_t L[KMAX];
 #pragma unroll
         for (int s = 0; s < KMAX; ++s) L[s] = 0ull;
-        for (uint32_t i = 0; i < c; ++i) {
+        for (uint32_t i = gl; i < c; i += G) {
             const float2 x = ent[b0 + i];
             uint64_t key = ((uint64_t)max(order_key(x.x), 1u) << 32) | (0xFFFFFFFFu - (uint32_t)__float_as_int(x.y));
             if (key > L[KMAX - 1]) {
@@ -1159,6 +1162,29 @@ __global__ __launch_bounds__(kFinThreads) void frame_finalize(const Args A) {
                 }
             }
         }
+        for (int o = 1; o < G; o <<= 1) {
+            // the KMAX best of two descending lists: the elementwise max of one
+            // and the other reversed is bitonic; a half-cleaner cascade sorts it
+            uint64_t M[KMAX];
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s) {
+                const uint64_t r = __shfl_xor(L[KMAX - 1 - s], o);
+                M[s] = L[s] > r ? L[s] : r;
+            }
+#pragma unroll
+            for (int j = KMAX / 2; j > 0; j >>= 1)
+#pragma unroll
+                for (int s = 0; s < KMAX; ++s)
+                    if ((s & j) == 0) {
+                        const uint64_t hi = M[s] > M[s + j] ? M[s] : M[s + j];
+                        const uint64_t lo = M[s] > M[s + j] ? M[s + j] : M[s];
+                        M[s] = hi;
+                        M[s + j] = lo;
+                    }
+#pragma unroll
+            for (int s = 0; s < KMAX; ++s) L[s] = M[s];
+        }
+        if (!active || gl != 0 || c < (uint32_t)K) continue;
         // the K best patches in ascending order (odd-even transposition sort)
         int32_t p[KMAX];
 #pragma unroll
