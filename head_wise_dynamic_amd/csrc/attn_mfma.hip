@@ -102,6 +102,7 @@ __device__ __forceinline__ RowMap make_rowmap(const HeadWork &w, const Geom &g, 
 }
 
 constexpr int kAttnThreads = 256;  // 4 waves x 64 query rows
+constexpr int kSpecTable = 4096;   // special tokens an LDS table holds (ns S <= this)
 
 // DENSE = true is the dense flash-attention kernel: every head attends to all
 // N keys, so key tiles are contiguous token ranges [kt, kt + 64): no key-set
@@ -111,6 +112,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KROW];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * VROWS];
     __shared__ float kbias[2][KT];
+    // token of the m-th special token (m < ns S) for position and scanning
+    // heads; -1 for a scanning head's special already on its stride
+    __shared__ int32_t spec_tok[kSpecTable];
 
     const Geom &g = L.g;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -141,6 +145,32 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const int64_t kbeg = (int64_t)split * per;
     const int64_t kend = min<int64_t>(count, kbeg + per);
     const int64_t first_masked = DENSE ? INT64_MAX : key_first_masked(w, g);
+
+    // Key enumeration without 64-bit divisions (N < 2^31): position and
+    // scanning sets are the special tokens (from an LDS table built once per
+    // work-group) and affine token ranges; vertical sets come from their
+    // list; broadcast sets keep the general enumeration.
+    const int32_t nsS = g.ns * g.S;
+    const bool table = !DENSE && (w.role == POSITION || w.role == SCANNING) && nsS <= kSpecTable;
+    if (table) {
+        for (int i = tid; i < nsS; i += kAttnThreads) {
+            const int32_t tok = (i / g.ns) * g.T + i % g.ns;
+            spec_tok[i] = (w.role == SCANNING && tok % w.budget == 0) ? -1 : tok;
+        }
+        __syncthreads();
+    }
+    const int32_t anchor_base = w.anchor * g.T + g.ns, own_base = rm.qsel * g.T + g.ns;
+    const int32_t nst = w.role == SCANNING ? (int32_t)((g.N + w.budget - 1) / w.budget) : 0;
+    auto token_of = [&](int64_t m64) -> int64_t {
+        if (DENSE) return m64;
+        if (!table) return key_token(w, g, m64, rm.qsel);
+        const int32_t m = (int32_t)m64;
+        if (w.role == POSITION) {
+            if (m < nsS) return spec_tok[m];
+            return m < nsS + g.P ? anchor_base + (m - nsS) : own_base + (m - nsS - g.P);
+        }
+        return m < nst ? m * w.budget : spec_tok[m - nst];  // scanning
+    };
 
     // ---- this wave's 64 query rows as two 32-row B operands (4 k-steps each)
     bool qvalid[2];
@@ -187,7 +217,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int64_t m = kt + 2 * lp + i;
-                tk[i] = (m < kend) ? (DENSE ? m : key_token(w, g, m, rm.qsel)) : -1;
+                tk[i] = (m < kend) ? token_of(m) : -1;
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
