@@ -31,30 +31,54 @@ METRIC = "ms per 16-head sparse global-attn layer at S=100 frames; HBM GB/s & MF
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 
-# HBM counters of the cosine GEMM launches of one step (rocprofv3 --pmc
-# FETCH_SIZE, then WRITE_SIZE, in separate runs; KiB per dispatch averaged per
-# kernel and summed over the step's 1 seed + 6 filtered + 1 symmetric launches).
-# Each counter is scaled by what it reads for a plain 1 GiB device copy in the
-# same run (FETCH_SIZE 524309.0 KiB, WRITE_SIZE 1048576 KiB).  The figures hold
-# for the kernel source with this digest only; after any change the traffic is
-# reported as null until the counters are taken again.
-COSINE_GEMM_COUNTERS = {
-    "config": 3,  # the workload the counters were taken on (S = 100)
-    "source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-    "sha256": "5a060c0484a7166e92b37ad27a562527a3a78e2b18db6c5dfa9bf32154ccdbc5",
-    "fetch_kib_per_step": 771903.62 + 6 * 321064.45 + 34938508.72,
-    "write_kib_per_step": 2901375.22 + 6 * 68530.72 + 1570484.69,
-    "fetch_scale": 1048576.0 / 524303.62,
-    "write_scale": 1048576.0 / 1048576.0,
+# Counter readings of the step's kernel groups on the S = 100 workload
+# (rocprofv3 --pmc, one pass per group of counters; per step: the index
+# build's cosine GEMM is 1 seed + 6 filtered + 1 symmetric launch, the
+# fused per-frame build's GEMM 1 sampled + 1 filtered symmetric launch, the
+# others one launch).  executed_tflop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+# FLOP; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x
+# 1024 SIMDs), the share of SIMD cycles the matrix cores were busy while the
+# kernel ran; fetch/write = FETCH_SIZE / WRITE_SIZE in KiB, scaled by what
+# the counters read for a plain device copy in the same run (WRITE_SIZE reads
+# the copied KiB exactly, FETCH_SIZE half of them).  A group's figures hold
+# for the kernel source with the recorded digest only; after any change they
+# are reported as null until the counters are taken again.
+COUNTERS = {
+    "config": 3,
+    "fetch_scale": 1.99993,
+    "write_scale": 1.0,
+    "groups": {
+        "cosine_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
+                        "sha256": "ce88fb77825dc81cef7516ce964830c331cbb8bd2d8d1cce6f8e41aa354fc794",
+                        "executed_tflop": 20.8678, "mfma_busy": 0.3678,
+                        "fetch_kib": 37551181.2, "write_kib": 4909855.2},
+        "per_frame_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
+                           "sha256": "ce88fb77825dc81cef7516ce964830c331cbb8bd2d8d1cce6f8e41aa354fc794",
+                           "executed_tflop": 22.8345, "mfma_busy": 0.3047,
+                           "fetch_kib": 40225328.4, "write_kib": 6035663.8},
+        "shared_attention": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
+                             "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
+                             "executed_tflop": 2.7005, "mfma_busy": 0.3737,
+                             "fetch_kib": 797394.8, "write_kib": 230452.6},
+        "dense": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
+                  "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
+                  "executed_tflop": 77.3724, "mfma_busy": 0.4164,
+                  "fetch_kib": 7579133.3, "write_kib": 274800.0},
+        "gather_attention": {"source": "head_wise_dynamic_amd/csrc/attn_valu.hip",
+                             "sha256": "7a6a099b4bbf2c81cc87a60c3c943b77e257a2c71554576e95376ff81701d681",
+                             "executed_tflop": 0.0, "mfma_busy": None,
+                             "fetch_kib": 12614063.1, "write_kib": 51337.5},
+    },
 }
 
 
-def counters_traffic_gb(rec, config):
-    """HBM bytes (GB) per step from the recorded counters, or None for another
-    workload or when the kernel source no longer matches the one they were
-    taken on."""
+def counters_for(group, config):
+    """The recorded counter figures of a kernel group, with its HBM traffic in
+    GB, or None for another workload or when the kernel source no longer
+    matches the one they were taken on."""
     import hashlib
-    if config != rec["config"]:
+    rec = COUNTERS["groups"].get(group)
+    if rec is None or config != COUNTERS["config"]:
         return None
     try:
         with open(os.path.join(ROOT, rec["source"]), "rb") as f:
@@ -62,8 +86,10 @@ def counters_traffic_gb(rec, config):
                 return None
     except OSError:
         return None
-    kib = rec["fetch_kib_per_step"] * rec["fetch_scale"] + rec["write_kib_per_step"] * rec["write_scale"]
-    return kib * 1024 / 1e9
+    out = dict(rec)
+    out["traffic_gb"] = (rec["fetch_kib"] * COUNTERS["fetch_scale"] + rec["write_kib"] * COUNTERS["write_scale"]) \
+        * 1024 / 1e9
+    return out
 
 
 def parse():
@@ -476,18 +502,53 @@ def main():
                                    peak=PEAK_BF16_TFLOPS, unit="TFLOP/s", ms=t,
                                    launches=launch_counts.get("cosine_gemm", 0))
     dom = max(cand, key=lambda n: cand[n]["ms"])
+
+    def counter_view(name, ms):
+        """Counter-based figures of a kernel group at the live time ms: FLOP
+        the matrix cores executed (and that rate against the peak), their
+        busy share, and the calibrated HBM bytes (and that rate)."""
+        c = counters_for(name, args.config)
+        if c is None:
+            return None
+        v = {"mfma_busy": c["mfma_busy"], "traffic_gb": round(c["traffic_gb"], 3),
+             "traffic_gbs": round(c["traffic_gb"] / (ms * 1e-3), 1),
+             "traffic_frac": round(c["traffic_gb"] / (ms * 1e-3) / PEAK_HBM_GBS, 4)}
+        if c["executed_tflop"]:
+            v["executed_tflop"] = c["executed_tflop"]
+            v["executed_tflops"] = round(c["executed_tflop"] / (ms * 1e-3), 2)
+            v["executed_frac"] = round(c["executed_tflop"] / (ms * 1e-3) / PEAK_BF16_TFLOPS, 4)
+        return v
+
     r = cand[dom]
-    traffic = counters_traffic_gb(COSINE_GEMM_COUNTERS, args.config) if dom == "cosine_gemm" else None
+    cv = counter_view(dom, r["ms"])
     roofline = {"kernel": dom, "bound": r["bound"], "achieved": round(r["achieved"], 2), "peak": r["peak"],
                 "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4),
-                "traffic": round(traffic, 2) if traffic is not None else None,
-                "traffic_unit": "GB of HBM traffic per step (all launches of the kernel)",
+                "achieved_is": "algorithmic work (every pair of the cosine matrix once per direction) / live time",
+                "traffic": cv["traffic_gb"] if cv else None,
+                "traffic_unit": "GB of HBM traffic per step (all launches of the kernel), from counters",
+                "counters": cv,
                 "kernel_ms_per_step": round(r["ms"], 4), "launches_per_step": r.get("launches", 1)}
     others = {n: {"achieved": round(c["achieved"], 2), "unit": c["unit"], "peak": c["peak"],
-                  "frac": round(c["achieved"] / c["peak"], 4), "kernel_ms": round(c["ms"], 4)}
+                  "frac": round(c["achieved"] / c["peak"], 4), "kernel_ms": round(c["ms"], 4),
+                  "counters": counter_view(n, c["ms"])}
               for n, c in cand.items() if n != dom}
+    if dense_ms:
+        others["dense"] = {"achieved": round(4.0 * d * g.H * g.N * g.N / (dense_ms * 1e-3) / 1e12, 2),
+                           "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
+                           "frac": round(4.0 * d * g.H * g.N * g.N / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "kernel_ms": round(dense_ms, 4), "counters": counter_view("dense", dense_ms)}
     corr_flops = 2.0 * g.Np * g.Np * w.Df
     corr_ms = breakdown.get("corr_index")
+
+    def per_frame_counters(pf):
+        """The fused per-frame build's two GEMM launches (sampled bounds,
+        filtered square): executed FLOP against the whole build's time."""
+        c = counters_for("per_frame_gemm", args.config) if pf["K_per_frame"] == 4 else None
+        if c is None:
+            return None
+        return {"gemm_executed_tflop": c["executed_tflop"], "gemm_mfma_busy": c["mfma_busy"],
+                "gemm_traffic_gb": round(c["traffic_gb"], 3),
+                "executed_frac_of_build": round(c["executed_tflop"] / (pf["build_ms"] * 1e-3) / PEAK_BF16_TFLOPS, 4)}
 
     # ---- CPU oracle on a bounded sample, extrapolated to the full step
     cpu = None
@@ -523,7 +584,7 @@ def main():
         "dense_tflops": round(4.0 * d * g.H * g.N * g.N / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "speedup_attn_vs_dense": round(dense_ms / attn_ms, 2) if dense_ms else None,
         "speedup_step_vs_dense": round(dense_ms / ms_per_step, 2) if dense_ms else None,
-        "per_frame_index": per_frame,
+        "per_frame_index": dict(per_frame, counters=per_frame_counters(per_frame)) if per_frame else None,
         "block_index": block,
         "corr_stride_layer": corr_stride,
         "broadcast_layer": broadcast,
