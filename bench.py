@@ -65,7 +65,7 @@ COUNTERS = {
                   "executed_tflop": 77.3724, "mfma_busy": 0.4164,
                   "fetch_kib": 7579133.3, "write_kib": 274800.0},
         "gather_attention": {"source": "head_wise_dynamic_amd/csrc/attn_valu.hip",
-                             "sha256": "7a6a099b4bbf2c81cc87a60c3c943b77e257a2c71554576e95376ff81701d681",
+                             "sha256": "16a750096b436f0759d7ee9a55fec5dda2cc0ad23bc2f3d374188a4cf7c5eb41",
                              "executed_tflop": 0.0, "mfma_busy": None,
                              "fetch_kib": 12614063.1, "write_kib": 51337.5},
     },

@@ -2,12 +2,15 @@
 //
 // This is the gather-bound path of the correspondence heads (SAF3R Sec. 4.1,
 // "DINO Top-K Kernel"): every query reads its own cached index row and pulls
-// the selected K and V rows by token index.  A wave serves one query row for
-// every head of the launch, one head after the other; each head's pass reads
-// the row's index entries again (they are the same for every correspondence
-// head of the layer, so only the first pass finds them outside the caches).
-// With fp32 inputs the same kernel runs every role (the matrix-core path is
-// bf16-only).
+// the selected K and V rows by token index.  Two kernels:
+//   gather_attn_kernel (bf16 correspondence rows): a wave serves one patch
+//   row for a group of up to three heads, reading each chunk's index
+//   entries once for the group and the K and V rows of all its heads
+//   together;
+//   valu_attn_kernel (fp32 inputs, where it runs every role: the matrix-core
+//   path is bf16-only): a wave serves one query row for every head of the
+//   launch, one head after the other, each head's pass reading the row's
+//   index entries again (only the first pass finds them outside the caches).
 //
 // Lane layout: a key row is read as 16-byte pieces, LPR lanes per row
 // (8 for bf16, 16 for fp32) and RPP = 64 / LPR rows per load instruction.

@@ -45,7 +45,9 @@ def test_index_builds_report_enomem(ctx):
     kc = C.c_int32()
     _enomem(ctx, saf.saf_build_corr_index(ctx, FAKE, 1, 64, 64, 8, 0, None), "index scratch")
     assert saf.saf_get_corr_index(ctx, None, kc, None) == saf.SAF_ESTATE
+    # per-frame: the fused build (bf16, P = 256, K = 8) and the stored-row build
     _enomem(ctx, saf.saf_build_corr_index(ctx, FAKE, 1, 64, 64, 8, 1, None), "index scratch")
+    _enomem(ctx, saf.saf_build_corr_index(ctx, FAKE, 1, 64, 64, 8, 2, None), "index scratch")
     _enomem(ctx, saf.saf_build_corr_index_blocks(ctx, FAKE, 1, 64, 64, 4, 8, 0, None), "index scratch")
     _enomem(ctx, saf.saf_build_corr_index_qk(ctx, FAKE, FAKE, LAY, 0, 8, 0, None), "index scratch")
     _enomem(ctx, saf.saf_set_corr_index(ctx, FAKE, 8, None), "correspondence index")
