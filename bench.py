@@ -10,7 +10,9 @@ Prints one JSON line.  Besides the contract fields it carries:
   breakdown    per launch group, ms per step (HIP events on the stream)
   attn_only_ms the layer with the index cached (what every later layer costs)
   dense_ms     the in-house dense flash attention at the same shape
-  roofline     the dominant kernel against the MI355X peak
+  roofline     the dominant kernel against the MI355X peak, with counter figures
+  sequence_lengths  the step, the cached-index layer and the dense kernel at
+               S = 32 and S = 500 (latency against sequence length)
   cpu_baseline the CPU oracle, timed on a bounded row sample, extrapolated
 """
 from __future__ import annotations
@@ -111,6 +113,8 @@ def parse():
                          "radius on the patch grid (-1: skip)")
     ap.add_argument("--no-qk-index", action="store_true",
                     help="skip timing the index built from the first correspondence head's logits")
+    ap.add_argument("--no-seq-lengths", action="store_true",
+                    help="skip the S = 32 and S = 500 steps (latency against sequence length)")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip timing the 24-layer stack (index built once, the stack's per-layer plans)")
     ap.add_argument("--stack-inputs", type=int, default=3,
@@ -476,6 +480,56 @@ def main():
         del full
         pctx.close()
 
+    # latency against sequence length (SAF3R Sec. 5.2, Fig. 6): the same step
+    # (index build + layer) on the S = 32 and S = 500 workloads, the layer
+    # with the index cached, and the dense kernel once; S = 100 is this line.
+    # Each workload is generated, run in a context of its own and released;
+    # not part of the step.
+    seq = None
+    if not args.no_seq_lengths and args.config == 3:
+        seq = {f"S={g.S}": {"N": g.N, "step_ms": round(ms_per_step, 3), "attn_only_ms": round(attn_ms, 3),
+                            "dense_ms": round(dense_ms, 3) if dense_ms else None}}
+        for cid in (2, 5):
+            t_gen = time.time()
+            wl = make_inputs(cid)
+            gl = wl.geom
+            ql, kl, vl, dl = dev(wl.q), dev(wl.k), dev(wl.v), dev(wl.dino)
+            print(f"[bench] generated {wl.name} N={gl.N} in {time.time() - t_gen:.1f}s", file=sys.stderr,
+                  flush=True)
+            ol = torch.empty_like(ql)
+            cl = saf.Context(gl.S, gl.ns, gl.P, gl.H, gl.d, torch.bfloat16)
+
+            def timed_l(fn, reps):
+                fn()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    fn()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                return statistics.median(ts)
+
+            def step_l():
+                cl.build_corr_index(dl, wl.corr_K)
+                cl.sparse_attention(wl.plan, ql, kl, vl, o=ol)
+
+            st_ms = timed_l(step_l, 3)
+            ix_ms = timed_l(lambda: cl.build_corr_index(dl, wl.corr_K), 3)
+            at_ms = timed_l(lambda: cl.sparse_attention(wl.plan, ql, kl, vl, o=ol), 3)
+            dn_ms = None
+            if not args.no_dense:
+                dn_ms = timed_l(lambda: cl.dense_attention(ql, kl, vl, o=ol), 1)
+            seq[f"S={gl.S}"] = {"N": gl.N, "step_ms": round(st_ms, 3), "index_ms": round(ix_ms, 3),
+                                "attn_only_ms": round(at_ms, 3), "dense_ms": round(dn_ms, 3) if dn_ms else None,
+                                "speedup_attn_vs_dense": round(dn_ms / at_ms, 2) if dn_ms else None}
+            print(f"[bench] {wl.name}: step {st_ms:.2f} ms, layer {at_ms:.2f} ms", file=sys.stderr, flush=True)
+            cl.close()
+            del wl, ql, kl, vl, dl, ol
+            torch.cuda.empty_cache()
+
     # ---- roofline of the dominant kernel (largest single-kernel share)
     pairs = key_counts(w)
     shared_pairs = sum(p for kind, p in pairs if kind == "shared")
@@ -585,6 +639,7 @@ def main():
         "speedup_attn_vs_dense": round(dense_ms / attn_ms, 2) if dense_ms else None,
         "speedup_step_vs_dense": round(dense_ms / ms_per_step, 2) if dense_ms else None,
         "per_frame_index": dict(per_frame, counters=per_frame_counters(per_frame)) if per_frame else None,
+        "sequence_lengths": seq,
         "block_index": block,
         "corr_stride_layer": corr_stride,
         "broadcast_layer": broadcast,
