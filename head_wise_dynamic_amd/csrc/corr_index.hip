@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     // thresholds per row (and per column in the symmetric modes); PFSYM holds
     // two per row, one for each frame the tile's columns (rows) span
     __shared__ float r_thr[2 * CT], r_iu[CT], c_thr[2 * CT];
+    __shared__ float c_iv[CT];  // inverse norms of the tile's columns (NaN past the end)
     __shared__ int32_t r_frame[CT];
     __shared__ uint32_t r_cnt[CT], c_cnt[CT];
 
@@ -294,47 +295,72 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     const int32_t f_row_hi = (int32_t)((min<int64_t>(row0 + CT, row_hi) - 1) / g.P);
     const int32_t f_col_lo = (int32_t)(col0 / g.P);
     const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, col_hi) - 1) / g.P);
-    if (tid < CT) {
-        const int64_t u = actual_row(row0 + tid);
-        float th0 = INFINITY, th1 = INFINITY, iu = __builtin_nanf("");  // NaN: no comparison passes
-        int32_t fr = -1;
-        if (u >= 0) {
-            iu = A.s.invn[u];
-            fr = (int32_t)(u / g.P);
+    // Per-tile set-up: rows' inverse norms, thresholds and frames, and the
+    // columns' (thresholds in the symmetric modes).  It runs after the first
+    // operand stage's loads are issued, and every load here is unconditional
+    // from a valid index (selected afterwards): a load under a per-lane
+    // condition is waited for on its own, which serialised these loads.
+    auto prologue = [&]() {
+        if (tid < CT) {
+            const int64_t u = actual_row(row0 + tid);
+            const int64_t uc = u >= 0 ? u : 0;
+            const float iu_l = A.s.invn[uc];
+            float t0 = 0.f, t1 = 0.f;
             if (MODE == PFSYM) {
-                // a tile's columns span at most two frames (P >= CT); the own
-                // frame is never a candidate
-                if (f_col_lo != fr) th0 = scaled_threshold(A.pthr[(int64_t)f_col_lo * g.Np + u], iu);
-                if (f_col_hi != f_col_lo && f_col_hi != fr)
-                    th1 = scaled_threshold(A.pthr[(int64_t)f_col_hi * g.Np + u], iu);
+                t0 = A.pthr[(int64_t)f_col_lo * g.Np + uc];
+                t1 = A.pthr[(int64_t)f_col_hi * g.Np + uc];
             } else {
-                th0 = scaled_threshold(MODE == SYM ? A.s.theta_g[u] : A.s.theta[u], iu);
+                t0 = MODE == SYM ? A.s.theta_g[uc] : A.s.theta[uc];
+            }
+            float th0 = INFINITY, th1 = INFINITY, iu = __builtin_nanf("");  // NaN: no comparison passes
+            int32_t fr = -1;
+            if (u >= 0) {
+                iu = iu_l;
+                fr = (int32_t)(u / g.P);
+                if (MODE == PFSYM) {
+                    // a tile's columns span at most two frames (P >= CT); the
+                    // own frame is never a candidate
+                    if (f_col_lo != fr) th0 = scaled_threshold(t0, iu);
+                    if (f_col_hi != f_col_lo && f_col_hi != fr) th1 = scaled_threshold(t1, iu);
+                } else {
+                    th0 = scaled_threshold(t0, iu);
+                }
+            }
+            r_thr[tid] = th0;
+            if (MODE == PFSYM) r_thr[CT + tid] = th1;
+            r_iu[tid] = iu;
+            r_frame[tid] = fr;
+            r_cnt[tid] = 0u;
+        } else {
+            const int t = tid - CT;
+            const int64_t v = col_operand(col0 + t);
+            const int64_t vc = v >= 0 ? v : 0;
+            const float iv_l = A.s.invn[vc];
+            float t0 = 0.f, t1 = 0.f;
+            if (MODE == PFSYM) {
+                t0 = A.pthr[(int64_t)f_row_lo * g.Np + vc];
+                t1 = A.pthr[(int64_t)f_row_hi * g.Np + vc];
+            } else if (kSym) {
+                t0 = A.s.theta_g[vc];
+            }
+            c_iv[t] = v >= 0 ? iv_l : __builtin_nanf("");
+            if (kSym) {
+                float th0 = INFINITY, th1 = INFINITY;
+                if (v >= 0) {
+                    if (MODE == PFSYM) {
+                        const int32_t fv = (int32_t)(v / g.P);
+                        if (f_row_lo != fv) th0 = scaled_threshold(t0, iv_l);
+                        if (f_row_hi != f_row_lo && f_row_hi != fv) th1 = scaled_threshold(t1, iv_l);
+                    } else {
+                        th0 = scaled_threshold(t0, iv_l);
+                    }
+                }
+                c_thr[t] = th0;
+                if (MODE == PFSYM) c_thr[CT + t] = th1;
+                c_cnt[t] = 0u;
             }
         }
-        r_thr[tid] = th0;
-        if (MODE == PFSYM) r_thr[CT + tid] = th1;
-        r_iu[tid] = iu;
-        r_frame[tid] = fr;
-        r_cnt[tid] = 0u;
-    } else if (kSym) {
-        const int t = tid - CT;
-        const int64_t v = col0 + t;
-        float th0 = INFINITY, th1 = INFINITY;
-        if (v < col_hi) {
-            const float iv = A.s.invn[v];
-            if (MODE == PFSYM) {
-                const int32_t fv = (int32_t)(v / g.P);
-                if (f_row_lo != fv) th0 = scaled_threshold(A.pthr[(int64_t)f_row_lo * g.Np + v], iv);
-                if (f_row_hi != f_row_lo && f_row_hi != fv)
-                    th1 = scaled_threshold(A.pthr[(int64_t)f_row_hi * g.Np + v], iv);
-            } else {
-                th0 = scaled_threshold(A.s.theta_g[v], iv);
-            }
-        }
-        c_thr[t] = th0;
-        if (MODE == PFSYM) c_thr[CT + t] = th1;
-        c_cnt[t] = 0u;
-    }
+    };
     const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
     f32x16 acc[2][4];
@@ -399,6 +425,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             }
         };
         load(0);
+        prologue();
         store(0);
         __syncthreads();
 #pragma unroll
@@ -437,6 +464,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         };
         const int nk = A.Df / CK;
         load(0);
+        prologue();
         store(0);
         __syncthreads();
         for (int t = 0; t < nk; ++t) {
@@ -457,9 +485,8 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
         const int64_t v = col_operand(vcol0 + 32 * bj);
-        const bool vok = v >= 0;
-        iv[bj] = vok ? A.s.invn[v] : __builtin_nanf("");  // NaN never passes a comparison
-        fv[bj] = vok ? (int32_t)(v / g.P) : -2;
+        iv[bj] = c_iv[lc0 + 32 * bj];  // NaN never passes a comparison
+        fv[bj] = v >= 0 ? (int32_t)(v / g.P) : -2;
     }
 
     if (MODE == PFSEED) {
