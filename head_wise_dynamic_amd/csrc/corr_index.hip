@@ -1407,7 +1407,8 @@ static int64_t feature_span(const CorrBuild &B) {
 }
 
 // cos_phase launch with the stage count fixed at compile time for the usual
-// feature widths (ViT-S/B/L: 384, 768, 1024 channels)
+// feature widths (ViT-S/B/L: 384, 768, 1024 channels) and for 64 (an
+// attention head's q and k, the index taken from a head's logits)
 template <int MODE> static void launch_cos(dim3 grid, hipStream_t stream, const Args &A) {
     const bool fixed = A.f_bytes != 0;  // byte offsets fit 32 bits
     if (fixed && A.Df == 1024)
@@ -1416,6 +1417,8 @@ template <int MODE> static void launch_cos(dim3 grid, hipStream_t stream, const 
         hipLaunchKernelGGL((cos_phase<MODE, 12>), grid, dim3(kCosThreads), 0, stream, A);
     else if (fixed && A.Df == 384)
         hipLaunchKernelGGL((cos_phase<MODE, 6>), grid, dim3(kCosThreads), 0, stream, A);
+    else if (fixed && A.Df == 64)
+        hipLaunchKernelGGL((cos_phase<MODE, 1>), grid, dim3(kCosThreads), 0, stream, A);
     else
         hipLaunchKernelGGL((cos_phase<MODE, 0>), grid, dim3(kCosThreads), 0, stream, A);
 }

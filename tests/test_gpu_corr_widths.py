@@ -1,8 +1,8 @@
 """Correspondence index at the usual feature widths, HIP path vs the oracle.
 
 The matrix-core cosine kernel has a variant with the channel loop fixed at
-compile time for 384, 768 and 1024 channels (ViT-S/B/L features) and a
-run-time loop for other multiples of 64; every variant must give the
+compile time for 64 (an attention head's q and k), 384, 768 and 1024
+channels (ViT-S/B/L features) and a run-time loop for other multiples of 64; every variant must give the
 oracle's top-K (band rule, 1e-5).  The geometry (12 frames of 200 patches)
 puts the symmetric square over patches [400, 2400): 2000 rows, a ragged last
 tile of 208.  Per-frame mode runs the same kernel in its store mode.
@@ -33,7 +33,7 @@ def _workload(Df, K, seed):
                                 corr_K=K, name=f"widths_Df{Df}")
 
 
-@pytest.mark.parametrize("Df", [192, 384, 768, 1024])
+@pytest.mark.parametrize("Df", [64, 192, 384, 768, 1024])
 def test_total_index_at_width(Df):
     saf = _saf()
     K = 24
