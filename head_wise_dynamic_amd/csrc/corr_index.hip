@@ -112,10 +112,18 @@ struct Args {
     float *pthr;             // fused per-frame mode: [S][Np] lower bound of row u's K-th best in frame f
 };
 
+// frame of patch number u: a 32-bit division (patch numbers are below
+// N < 2^31, checked when the context is created; a 64-bit division takes
+// several times the instructions)
+__device__ __forceinline__ int32_t patch_frame(const Geom &g, int64_t u) {
+    return (int32_t)((uint32_t)u / (uint32_t)g.P);
+}
+
 // element offset of patch row u in F / Fc
 __device__ __forceinline__ int64_t frow(const Args &A, int64_t u) {
-    const int64_t r = A.tok_map ? (u / A.g.P) * A.g.T + A.g.ns + u % A.g.P : u;
-    return r * A.stride;
+    if (!A.tok_map) return u * A.stride;
+    const int32_t f = patch_frame(A.g, u);
+    return ((int64_t)f * A.g.T + A.g.ns + (u - (int64_t)f * A.g.P)) * A.stride;
 }
 
 template <typename T> __device__ inline float ldf(const T *p, int64_t i);
@@ -291,10 +299,10 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         return c < col_hi ? c : -1;
     };
 
-    const int32_t f_row_lo = (int32_t)(row0 / g.P);
-    const int32_t f_row_hi = (int32_t)((min<int64_t>(row0 + CT, row_hi) - 1) / g.P);
-    const int32_t f_col_lo = (int32_t)(col0 / g.P);
-    const int32_t f_col_hi = (int32_t)((min<int64_t>(col0 + CT, col_hi) - 1) / g.P);
+    const int32_t f_row_lo = patch_frame(g, row0);
+    const int32_t f_row_hi = patch_frame(g, min<int64_t>(row0 + CT, row_hi) - 1);
+    const int32_t f_col_lo = patch_frame(g, col0);
+    const int32_t f_col_hi = patch_frame(g, min<int64_t>(col0 + CT, col_hi) - 1);
     // Per-tile set-up: rows' inverse norms, thresholds and frames, and the
     // columns' (thresholds in the symmetric modes).  It runs after the first
     // operand stage's loads are issued, and every load here is unconditional
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             int32_t fr = -1;
             if (u >= 0) {
                 iu = iu_l;
-                fr = (int32_t)(u / g.P);
+                fr = patch_frame(g, u);
                 if (MODE == PFSYM) {
                     // a tile's columns span at most two frames (P >= CT); the
                     // own frame is never a candidate
@@ -348,7 +356,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                 float th0 = INFINITY, th1 = INFINITY;
                 if (v >= 0) {
                     if (MODE == PFSYM) {
-                        const int32_t fv = (int32_t)(v / g.P);
+                        const int32_t fv = patch_frame(g, v);
                         if (f_row_lo != fv) th0 = scaled_threshold(t0, iv_l);
                         if (f_row_hi != f_row_lo && f_row_hi != fv) th1 = scaled_threshold(t1, iv_l);
                     } else {
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
     for (int bj = 0; bj < 4; ++bj) {
         const int64_t v = col_operand(vcol0 + 32 * bj);
         iv[bj] = c_iv[lc0 + 32 * bj];  // NaN never passes a comparison
-        fv[bj] = v >= 0 ? (int32_t)(v / g.P) : -2;
+        fv[bj] = v >= 0 ? patch_frame(g, v) : -2;
     }
 
     if (MODE == PFSEED) {
