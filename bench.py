@@ -51,25 +51,25 @@ COUNTERS = {
     "write_scale": 1.0,
     "groups": {
         "cosine_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-                        "sha256": "ce88fb77825dc81cef7516ce964830c331cbb8bd2d8d1cce6f8e41aa354fc794",
-                        "executed_tflop": 20.8678, "mfma_busy": 0.3678,
-                        "fetch_kib": 37551181.2, "write_kib": 4909855.2},
+            "sha256": "01301ea87d605744e1ce40d4ad0d6aa1fc564cde4995bbd13d5040e8616ce16c",
+            "executed_tflop": 20.8678, "mfma_busy": 0.3768,
+            "fetch_kib": 37548277.4, "write_kib": 4890096.0},
         "per_frame_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-                           "sha256": "ce88fb77825dc81cef7516ce964830c331cbb8bd2d8d1cce6f8e41aa354fc794",
-                           "executed_tflop": 22.8345, "mfma_busy": 0.3047,
-                           "fetch_kib": 40225328.4, "write_kib": 6035663.8},
+            "sha256": "01301ea87d605744e1ce40d4ad0d6aa1fc564cde4995bbd13d5040e8616ce16c",
+            "executed_tflop": 22.8345, "mfma_busy": 0.3078,
+            "fetch_kib": 40159323.4, "write_kib": 6034824.1},
         "shared_attention": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
-                             "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
-                             "executed_tflop": 2.7005, "mfma_busy": 0.3737,
-                             "fetch_kib": 797394.8, "write_kib": 230452.6},
+            "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
+            "executed_tflop": 2.7005, "mfma_busy": 0.3761,
+            "fetch_kib": 797284.7, "write_kib": 230452.4},
         "dense": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
-                  "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
-                  "executed_tflop": 77.3724, "mfma_busy": 0.4164,
-                  "fetch_kib": 7579133.3, "write_kib": 274800.0},
+            "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
+            "executed_tflop": 77.3724, "mfma_busy": 0.4213,
+            "fetch_kib": 7661559.9, "write_kib": 274800.0},
         "gather_attention": {"source": "head_wise_dynamic_amd/csrc/attn_valu.hip",
-                             "sha256": "16a750096b436f0759d7ee9a55fec5dda2cc0ad23bc2f3d374188a4cf7c5eb41",
-                             "executed_tflop": 0.0, "mfma_busy": None,
-                             "fetch_kib": 12614063.1, "write_kib": 51337.5},
+            "sha256": "16a750096b436f0759d7ee9a55fec5dda2cc0ad23bc2f3d374188a4cf7c5eb41",
+            "executed_tflop": 0.0, "mfma_busy": None,
+            "fetch_kib": 12613602.3, "write_kib": 51337.5},
     },
 }
 
