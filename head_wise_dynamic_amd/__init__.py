@@ -67,6 +67,7 @@ _PROTOS = {
     "saf_head_nmse": (C.c_int, [_VP, _VP, _VP, saf_layout_t, _VP, _VP]),
     "saf_head_nmse_accumulate": (C.c_int, [_VP, _VP, _VP, saf_layout_t, C.c_double, _VP, _I64, _VP]),
     "saf_head_pairs": (C.c_int, [_VP, C.POINTER(saf_head_plan_t), _I32, C.POINTER(C.c_int64)]),
+    "saf_head_cost": (C.c_int, [_VP, C.POINTER(saf_head_plan_t), _I32, C.POINTER(C.c_double)]),
     "saf_profile_select": (C.c_int32, [C.POINTER(C.c_double), C.POINTER(C.c_double), _I32]),
     "saf_baseline_stride": (C.c_int32, [C.c_double]),
     "saf_set_corr_index": (C.c_int, [_VP, _VP, _I32, _VP]),
@@ -142,6 +143,10 @@ def saf_head_nmse_accumulate(ctx, o_full, o_sparse, layout, weight, dev_err, err
 
 def saf_head_pairs(ctx, head, corr_kc, pairs) -> int:
     return lib().saf_head_pairs(ctx, head, corr_kc, pairs)
+
+
+def saf_head_cost(ctx, head, corr_kc, flops) -> int:
+    return lib().saf_head_cost(ctx, head, corr_kc, flops)
 
 
 def saf_profile_select(errors, costs, n) -> int:
@@ -413,6 +418,13 @@ class Context:
         h = saf_head_plan_t(role, budget, anchor, 0)
         self._check(saf_head_pairs(self._ctx, C.byref(h), corr_kc, C.byref(n)))
         return n.value
+
+    def head_cost(self, role: int, budget: int = 0, anchor: int = 0, corr_kc: int = 0) -> float:
+        """Eq. 2's cost of one head under (role, budget, anchor): FLOPs."""
+        f = C.c_double()
+        h = saf_head_plan_t(role, budget, anchor, 0)
+        self._check(saf_head_cost(self._ctx, C.byref(h), corr_kc, C.byref(f)))
+        return f.value
 
     def dense_attention(self, q, k, v, o=None, stream=None) -> torch.Tensor:
         if o is None:

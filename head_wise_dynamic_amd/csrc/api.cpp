@@ -1220,6 +1220,16 @@ saf_status_t saf_head_pairs(const saf_ctx_t *cc, const saf_head_plan_t *head, in
     }
 }
 
+saf_status_t saf_head_cost(const saf_ctx_t *cc, const saf_head_plan_t *head, int32_t corr_kc, double *flops) {
+    if (!cc) return SAF_EINVAL;
+    if (!flops) return fail(const_cast<saf_ctx_t *>(cc), SAF_EINVAL, "null pointer");
+    int64_t pairs = 0;
+    const saf_status_t st = saf_head_pairs(cc, head, corr_kc, &pairs);
+    if (st != SAF_OK) return st;
+    *flops = 4.0 * (double)cc->g.d * (double)pairs;
+    return SAF_OK;
+}
+
 int32_t saf_profile_select(const double *errors, const double *costs, int32_t n) {
     if (!errors || !costs || n < 1) return -1;
     int32_t best = 0;

@@ -33,8 +33,7 @@ def baseline(sigma: float) -> Config:
 
 def config_flops(ctx: Context, cfg: Config) -> float:
     role, budget, anchor = cfg
-    pairs = ctx.head_pairs(role, budget, anchor, corr_kc=budget if role == SAF_CORRESPONDENCE else 0)
-    return 4.0 * ctx.d * pairs
+    return ctx.head_cost(role, budget, anchor, corr_kc=budget if role == SAF_CORRESPONDENCE else 0)
 
 
 def select(errors: Sequence[float], costs: Sequence[float]) -> int:

@@ -355,6 +355,12 @@ saf_status_t saf_head_nmse_accumulate(saf_ctx_t *ctx, const void *o_full, const 
 saf_status_t saf_head_pairs(const saf_ctx_t *ctx, const saf_head_plan_t *head, int32_t corr_kc,
                             int64_t *pairs);
 
+/* Eq. 2's cost Omega(c) of one head under *head (Sec. 4.2): its floating-point
+ * work, 4 head_dim per query-key pair (2 head_dim for q.k, 2 head_dim for
+ * p.v) over the pairs saf_head_pairs counts, written to *flops.  Host only.
+ * Errors: as saf_head_pairs, and SAF_EINVAL for a null flops. */
+saf_status_t saf_head_cost(const saf_ctx_t *ctx, const saf_head_plan_t *head, int32_t corr_kc, double *flops);
+
 /* Eq. 2 by progressive substitution: entry 0 is the baseline; walking
  * entries 1 .. n-1 in order, an entry replaces the current choice when its
  * error is strictly lower and its cost does not exceed the baseline's.

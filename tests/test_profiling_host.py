@@ -1,6 +1,6 @@
 """Host logic of the offline head profiler (C ABI, no GPU needed) against
-the oracle: pair counts per configuration, the baseline stride and the
-selection rule of Eq. 2."""
+the oracle: pair counts and Eq. 2's cost per configuration, the baseline
+stride and the selection rule of Eq. 2."""
 import ctypes as C
 
 import numpy as np
@@ -34,6 +34,10 @@ def test_head_pairs_match_oracle(S, ns, P):
             h = saf.saf_head_plan_t(role, budget, anchor, 0)
             assert saf.saf_head_pairs(c, C.byref(h), budget, C.byref(n)) == saf.SAF_OK
             assert n.value == profiling.head_pairs(geom, (role, budget, anchor)), (role, budget, anchor)
+            # Eq. 2's cost: the oracle's FLOP count of the configuration
+            f = C.c_double()
+            assert saf.saf_head_cost(c, C.byref(h), budget, C.byref(f)) == saf.SAF_OK
+            assert f.value == float(profiling.head_flops(geom, (role, budget, anchor))), (role, budget, anchor)
         n = C.c_int64()
         bad = saf.saf_head_plan_t(saf.SAF_POSITION, 0, S, 0)
         assert saf.saf_head_pairs(c, C.byref(bad), 0, C.byref(n)) == saf.SAF_EINVAL
@@ -45,6 +49,10 @@ def test_head_pairs_match_oracle(S, ns, P):
             assert saf.saf_head_pairs(c, C.byref(b3), 0, C.byref(n)) == saf.SAF_EINVAL
         corr = saf.saf_head_plan_t(saf.SAF_CORRESPONDENCE, 0, 0, 0)
         assert saf.saf_head_pairs(c, C.byref(corr), 0, C.byref(n)) == saf.SAF_ESTATE    # no cached index
+        f = C.c_double()
+        assert saf.saf_head_cost(c, C.byref(corr), 0, C.byref(f)) == saf.SAF_ESTATE
+        assert saf.saf_head_cost(c, C.byref(bad), 0, C.byref(f)) == saf.SAF_EINVAL
+        assert saf.lib().saf_head_cost(c, C.byref(corr), 8, None) == saf.SAF_EINVAL
     finally:
         saf.saf_destroy(c)
 
