@@ -11,7 +11,11 @@
 // to a per-row candidate buffer (staged in LDS, one global atomic per row
 // per tile).  After each phase a compaction wave per row raises theta_u to a
 // lower bound of the K-th best of its buffer and drops what lies below.
-//   1. seed: columns of frames 0 and 1, every candidate kept;
+//   1. seed: columns of frames 0 and 1.  When 4 K + 128 <= P, only each
+//      lane's largest cosine over its 4 seed columns of other frames is
+//      kept, and a row's K-th largest such value (reached by K distinct
+//      patches) becomes its first theta_u; the first filtered phase then
+//      covers [0, 4P).  Otherwise every seed candidate is kept;
 //   2. doubling phases [2P, 4P), [4P, 8P), ... up to W, for every row;
 //   3. rows below W continue doubling over [W, Np);
 //   4. the square [W, Np)^2 once per unordered pair (cosine is symmetric: a
@@ -109,6 +113,7 @@ struct Args {
     int32_t use_list;        // STORE: tile rows are positions in s.row_list (flagged rows)
     uint32_t f_bytes;        // bytes of F (and of Fc) that rows 0..Np-1 span; 0: over 0xFFFF0000
     int32_t fallback_list_from;  // >= 0: the per-row engine takes s.row_list[from, row_count); -1: every row
+    int32_t lm_per_row;      // TBOUND: lane maxima stored per row (64 per column tile)
     float *pthr;             // fused per-frame mode: [S][Np] lower bound of row u's K-th best in frame f
 };
 
@@ -194,7 +199,12 @@ constexpr int kCosThreads = 512;           // 8 waves: 4 (rows) x 2 (columns) of
 //          maxima (each over 4 sampled patches) is a lower bound of the row's
 //          K-th best cosine in that frame, written to A.pthr;
 //   PFSYM  SYM with those per-(row, frame) bounds as filters (per-frame mode).
-enum CosMode { SEED = 0, FILTER = 1, SYM = 2, STORE = 3, PFSEED = 4, PFSYM = 5 };
+//   TBOUND rows [row_lo,row_hi) x the seed columns: per row, each lane's
+//          largest cosine over its 4 columns of other frames, stored to the
+//          row's candidate buffer as plain floats (bound_rows then takes
+//          the row's K-th largest: a lower bound of its K-th best, reached
+//          by K distinct patches).
+enum CosMode { SEED = 0, FILTER = 1, SYM = 2, STORE = 3, PFSEED = 4, PFSYM = 5, TBOUND = 6 };
 constexpr int kFrameSample = 128;
 
 // value of lane (lane ^ j) within each group of 32 lanes (ds_swizzle in its
@@ -384,26 +394,26 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         const bool overlap = !(f_row_hi < f_col_lo || f_col_hi < f_row_lo);
 
         f32x16 acc[2][4];
-    #pragma unroll
+#pragma unroll
         for (int bi = 0; bi < 2; ++bi)
-    #pragma unroll
+#pragma unroll
             for (int bj = 0; bj < 4; ++bj)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) acc[bi][bj][r] = 0.f;
         auto mma = [&](int buf) {
-    #pragma unroll
+#pragma unroll
             for (int kk = 0; kk < CK / 16; ++kk) {
                 __builtin_amdgcn_iglp_opt(0);  // interleave LDS reads with the MFMA chain
                 bf16x8 a[2], b[4];
-    #pragma unroll
+#pragma unroll
                 for (int bi = 0; bi < 2; ++bi)
                     a[bi] = *(const bf16x8 *)(&As[buf][(64 * wr + 32 * bi + n) * CROW + 16 * kk + 8 * gq]);
-    #pragma unroll
+#pragma unroll
                 for (int bj = 0; bj < 4; ++bj)
                     b[bj] = *(const bf16x8 *)(&Bs[buf][(128 * wc + 32 * bj + n) * CROW + 16 * kk + 8 * gq]);
-    #pragma unroll
+#pragma unroll
                 for (int bi = 0; bi < 2; ++bi)
-    #pragma unroll
+#pragma unroll
                     for (int bj = 0; bj < 4; ++bj)
                         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi], b[bj], acc[bi][bj], 0, 0, 0);
             }
@@ -421,7 +431,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             // <= 0xFFFF0000 every stage offset added stays past it (no wrap)
             const uint32_t kNone = A.f_bytes;
             uint32_t aoff[4], boff[4];
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = (tid + kCosThreads * i) >> 3, seg = (tid + kCosThreads * i) & 7;
                 const int64_t u = actual_row(row0 + row), v = col_operand(col0 + row);
@@ -430,14 +440,14 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             }
             u32x4 ar[4], br[4];
             auto load = [&](int st) {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     ar[i] = __builtin_amdgcn_raw_buffer_load_b128(rf, aoff[i] + 2 * CK * st, 0, 0);
                     br[i] = __builtin_amdgcn_raw_buffer_load_b128(rc, boff[i] + 2 * CK * st, 0, 0);
                 }
             };
             auto store = [&](int buf) {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
                     *(u32x4 *)(&As[buf][row * CROW + 8 * seg]) = ar[i];
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             prologue();
             store(0);
             __syncthreads();
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < NK; ++t) {
                 if (t + 1 < NK) load(t + 1);
                 mma(t & 1);
@@ -458,7 +468,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         } else {
             // element offsets of the rows this thread loads (0xFFFFFFFF: none)
             uint32_t aoff[4], boff[4];
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = (tid + kCosThreads * i) >> 3;
                 const int64_t u = actual_row(row0 + row), v = col_operand(col0 + row);
@@ -467,7 +477,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             }
             u32x4 ar[4], br[4];
             auto load = [&](int k0) {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int seg = (tid + kCosThreads * i) & 7;
                     ar[i] = aoff[i] != 0xFFFFFFFFu ? *(const u32x4 *)(F + aoff[i] + k0 + 8 * seg) : u32x4{0u, 0u, 0u, 0u};
@@ -475,7 +485,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                 }
             };
             auto store = [&](int buf) {
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = tid + kCosThreads * i, row = c >> 3, seg = c & 7;
                     *(u32x4 *)(&As[buf][row * CROW + 8 * seg]) = ar[i];
@@ -502,7 +512,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         int32_t fv[4];
         const int32_t lc0 = 128 * wc + n;                   // local column of block bj: lc0 + 32 bj
         const int32_t vcol0 = (int32_t)(col0 + lc0);
-    #pragma unroll
+#pragma unroll
         for (int bj = 0; bj < 4; ++bj) {
             const int64_t v = col_operand(vcol0 + 32 * bj);
             iv[bj] = c_iv[lc0 + 32 * bj];  // NaN never passes a comparison
@@ -515,14 +525,14 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             if (fs >= g.S) return;
             // per row, the largest of the lane's 4 sampled cosines
             float m[2][16];
-    #pragma unroll
+#pragma unroll
             for (int bi = 0; bi < 2; ++bi)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
                     const float iu = r_iu[lr];
                     float x = -INFINITY;
-    #pragma unroll
+#pragma unroll
                     for (int bj = 0; bj < 4; ++bj) {
                         const float c = acc[bi][bj][r] * (iu * iv[bj]);
                         x = c > x ? c : x;
@@ -533,14 +543,14 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             // then holds the (n+1)-th largest lane maximum of every row.  The K
             // lanes with the largest maxima hold K distinct sampled patches at or
             // above lane K-1's value, so it never exceeds the frame's K-th best.
-    #pragma unroll
+#pragma unroll
             for (int k = 2; k <= 32; k <<= 1)
-    #pragma unroll
+#pragma unroll
                 for (int j = k >> 1; j > 0; j >>= 1) {
                     const bool want_max = ((n & j) == 0) == ((n & k) == 0);
-    #pragma unroll
+#pragma unroll
                     for (int bi = 0; bi < 2; ++bi)
-    #pragma unroll
+#pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const float y = xor_lanes32(m[bi][r], j);
                             m[bi][r] = want_max ? fmaxf(m[bi][r], y) : fminf(m[bi][r], y);
@@ -548,9 +558,9 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                 }
             if (n == A.K - 1) {
                 float *dst = A.pthr + fs * g.Np + row0;
-    #pragma unroll
+#pragma unroll
                 for (int bi = 0; bi < 2; ++bi)
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
                         if (r_frame[lr] >= 0) dst[lr] = m[bi][r];
@@ -559,16 +569,41 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             return;
         }
 
-        if (MODE == STORE) {
-    #pragma unroll
+        if (MODE == TBOUND) {
+            // per row, the lane's largest cosine over its columns of other
+            // frames (own frame and columns past the seed excluded); one slot
+            // per (column tile, wave column half, lane)
+            float *lm = (float *)A.s.cand;
+            const int64_t slot = (col0 - A.col_lo) / CT * 64 + 32 * wc + n;
+#pragma unroll
             for (int bi = 0; bi < 2; ++bi)
-    #pragma unroll
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
+                    const int32_t fr = r_frame[lr];
+                    if (fr < 0) continue;
+                    const float iu = r_iu[lr];
+                    float x = -INFINITY;
+#pragma unroll
+                    for (int bj = 0; bj < 4; ++bj) {
+                        const float c = acc[bi][bj][r] * (iu * iv[bj]);
+                        if (fv[bj] >= 0 && fv[bj] != fr && c > x) x = c;
+                    }
+                    lm[(row0 + lr) * 2 * (int64_t)A.cap + slot] = x;
+                }
+            return;
+        }
+
+        if (MODE == STORE) {
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
                     if (r_frame[lr] < 0) continue;
                     const float iu = r_iu[lr];
                     float *crow = A.chunk + (row0 + lr - A.row_lo) * g.Np;
-    #pragma unroll
+#pragma unroll
                     for (int bj = 0; bj < 4; ++bj)
                         if (fv[bj] >= 0) crow[vcol0 + 32 * bj] = acc[bi][bj][r] * (iu * iv[bj]);
                 }
@@ -576,14 +611,14 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         }
 
         if (MODE == SEED) {
-    #pragma unroll
+#pragma unroll
             for (int bi = 0; bi < 2; ++bi)
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int lr = 64 * wr + 32 * bi + 8 * (r >> 2) + 4 * gq + (r & 3);
                     const int32_t fr = r_frame[lr];
                     const float iu = r_iu[lr];
-    #pragma unroll
+#pragma unroll
                     for (int bj = 0; bj < 4; ++bj) {
                         const int32_t v = vcol0 + 32 * bj;
                         if (fr >= 0 && fv[bj] >= 0 && fr != fv[bj]) {
@@ -620,9 +655,9 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
         // PFSYM: columns from col_split on (rows from row_split on) lie in the
         // second frame the tile spans and use the second threshold
         const int64_t col_split = (int64_t)(f_col_lo + 1) * g.P, row_split = (int64_t)(f_row_lo + 1) * g.P;
-    #pragma unroll
+#pragma unroll
         for (int bi = 0; bi < 2; ++bi) {
-    #pragma unroll
+#pragma unroll
             for (int bj = 0; bj < 4; ++bj) {
                 uint32_t kf = 0, kt = 0;
                 const float *tb = thr_base;
@@ -631,7 +666,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                     if (vcol0 + 32 * bj >= col_split) tb += CT;
                     if (transposed) cth1 = c_thr[CT + lc0 + 32 * bj];
                 }
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int o = 32 * bi + 8 * (r >> 2) + (r & 3);
                     kf |= (acc[bi][bj][r] * iv[bj] >= tb[o]) ? (1u << r) : 0u;
@@ -642,7 +677,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                     }
                 }
                 if (kf | kt) {
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) xl[r] = acc[bi][bj][r];
                     const int lc = lc0 + 32 * bj;
                     const int32_t v = vcol0 + 32 * bj;
@@ -680,6 +715,31 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
             }
         }
     }
+}
+
+// ---- bound seed: each row's K-th largest stored lane maximum (TBOUND) as
+// its first threshold; a row with fewer than K of them gets none (-inf)
+template <int MAXE> __global__ __launch_bounds__(256) void bound_rows(const Args A) {
+    const int64_t u = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (u >= A.g.Np) return;
+    const float *lm = (const float *)A.s.cand + u * 2 * (int64_t)A.cap;
+    const int n = A.lm_per_row;
+    uint32_t key[MAXE];  // order key; 0: no value
+    float x[MAXE];
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) x[e] = lm[min(e * 64 + lane, n - 1)];  // unconditional, masked below
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) key[e] = (e * 64 + lane < n && x[e] > -INFINITY) ? order_key(x[e]) : 0u;
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < MAXE; ++e) c += (uint32_t)__popcll(__ballot(key[e] >= cand));
+        if (c >= (uint32_t)A.K) thr = cand;
+    }
+    if (lane == 0) A.s.theta[u] = thr ? order_key_to_float(thr) : -INFINITY;
 }
 
 // ---- per-row selection inside one wave.
@@ -1645,7 +1705,15 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             hipLaunchKernelGGL(fallback_rows<float>, dim3(fb), dim3(1024), 0, stream, A);
         return hipGetLastError();
     }
-    A.seed_cols = std::min<int64_t>(Np, 2 * (int64_t)B.g.P);
+    const int64_t seed_cols = std::min<int64_t>(Np, 2 * (int64_t)B.g.P);
+    // Bound seed: instead of storing every cosine of the seed frames (then
+    // compacting them), their lane maxima give each row a lower bound of its
+    // K-th best, and the first filtered phase starts at column 0.  Needs K
+    // lane maxima of other frames in every row (4 K + 128 <= P) and the lane
+    // maxima within the candidate buffer's row.
+    const bool bound_seed = gemm && seed_cols == 2 * (int64_t)B.g.P && B.g.P <= 4096 &&
+                            4 * (int64_t)B.K + 128 <= B.g.P;
+    A.seed_cols = bound_seed ? 0 : seed_cols;
     // the symmetric square needs one operand for rows and columns
     A.sym_lo = (A.Fc == A.F) ? corr_sym_start(B.g) : Np;
     const unsigned rb = (unsigned)((Np + 3) / 4);
@@ -1681,10 +1749,31 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             compact();
             A.guess_k = 0;
         };
-        // 1. seed: frames 0 and 1 for every row, every candidate kept
-        rect(SEED, 0, Np, 0, A.seed_cols);
+        int64_t lo0 = seed_cols;
+        if (bound_seed) {
+            // 1. bounds from the seed frames' lane maxima, then the first
+            // filtered phase over [0, 2 seed)
+            A.row_lo = 0;
+            A.row_hi = Np;
+            A.col_lo = 0;
+            A.col_hi = seed_cols;
+            A.lm_per_row = (int32_t)((seed_cols + CT - 1) / CT * 64);
+            const int64_t tiles = ((Np + CT - 1) / CT) * ((seed_cols + CT - 1) / CT);
+            if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+            launch_cos<TBOUND>(dim3((unsigned)(8 * ((tiles + 7) / 8))), stream, A);
+            if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+            if (A.lm_per_row <= 16 * 64)
+                hipLaunchKernelGGL(bound_rows<16>, dim3(cb), dim3(256), 0, stream, A);
+            else
+                hipLaunchKernelGGL(bound_rows<32>, dim3(cb), dim3(256), 0, stream, A);
+            lo0 = std::min<int64_t>(2 * seed_cols, W);
+            rect(FILTER, 0, Np, 0, lo0);
+        } else {
+            // 1. seed: frames 0 and 1 for every row, every candidate kept
+            rect(SEED, 0, Np, 0, seed_cols);
+        }
         // 2. doubling filtered phases for every row up to W
-        for (int64_t lo = A.seed_cols; lo < W; lo = std::min<int64_t>(2 * lo, W))
+        for (int64_t lo = lo0; lo < W; lo = std::min<int64_t>(2 * lo, W))
             rect(FILTER, 0, Np, lo, std::min<int64_t>(2 * lo, W));
         if (W < Np) {
             // 3. rows below W keep doubling over the remaining columns
