@@ -35,7 +35,7 @@ PEAK_BF16_TFLOPS = 2500.0
 
 # Counter readings of the step's kernel groups on the S = 100 workload
 # (rocprofv3 --pmc, one pass per group of counters; per step: the index
-# build's cosine GEMM is 1 seed + 6 filtered + 1 symmetric launch, the
+# build's cosine GEMM is 1 seed-bound + 6 filtered + 1 symmetric launch, the
 # fused per-frame build's GEMM 1 sampled + 1 filtered symmetric launch, the
 # others one launch).  executed_tflop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
 # FLOP; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x
@@ -51,25 +51,25 @@ COUNTERS = {
     "write_scale": 1.0,
     "groups": {
         "cosine_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-            "sha256": "01301ea87d605744e1ce40d4ad0d6aa1fc564cde4995bbd13d5040e8616ce16c",
-            "executed_tflop": 20.8678, "mfma_busy": 0.3768,
-            "fetch_kib": 37548277.4, "write_kib": 4890096.0},
+            "sha256": "9651fbf40147952751588b19938949e3e634235524386ed34dc4e28e4f5f786d",
+            "executed_tflop": 21.6576, "mfma_busy": 0.3766,
+            "fetch_kib": 37934459.2, "write_kib": 2814449.6},
         "per_frame_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-            "sha256": "01301ea87d605744e1ce40d4ad0d6aa1fc564cde4995bbd13d5040e8616ce16c",
-            "executed_tflop": 22.8345, "mfma_busy": 0.3078,
-            "fetch_kib": 40159323.4, "write_kib": 6034824.1},
+            "sha256": "9651fbf40147952751588b19938949e3e634235524386ed34dc4e28e4f5f786d",
+            "executed_tflop": 22.8345, "mfma_busy": 0.3079,
+            "fetch_kib": 40148678.5, "write_kib": 6040009.3},
         "shared_attention": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
             "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
-            "executed_tflop": 2.7005, "mfma_busy": 0.3761,
-            "fetch_kib": 797284.7, "write_kib": 230452.4},
+            "executed_tflop": 2.7005, "mfma_busy": 0.3749,
+            "fetch_kib": 797283.6, "write_kib": 230452.7},
         "dense": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
             "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4213,
-            "fetch_kib": 7661559.9, "write_kib": 274800.0},
+            "executed_tflop": 77.3724, "mfma_busy": 0.4243,
+            "fetch_kib": 7259348.5, "write_kib": 274801.5},
         "gather_attention": {"source": "head_wise_dynamic_amd/csrc/attn_valu.hip",
             "sha256": "16a750096b436f0759d7ee9a55fec5dda2cc0ad23bc2f3d374188a4cf7c5eb41",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12613602.3, "write_kib": 51337.5},
+            "fetch_kib": 12612891.9, "write_kib": 51337.5},
     },
 }
 
