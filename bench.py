@@ -10,7 +10,9 @@ Prints one JSON line.  Besides the contract fields it carries:
   breakdown    per launch group, ms per step (HIP events on the stream)
   attn_only_ms the layer with the index cached (what every later layer costs)
   dense_ms     the in-house dense flash attention at the same shape
-  roofline     the dominant kernel against the MI355X peak, with counter figures
+  roofline     the dominant kernel against the MI355X peak, with counter figures;
+               roofline_other.*.alone: the gather and the shared-key kernels each
+               timed on their own heads
   sequence_lengths  the step, the cached-index layer and the dense kernel at
                S = 32 and S = 500 (latency against sequence length)
   cpu_baseline the CPU oracle, timed on a bounded row sample, extrapolated
@@ -115,6 +117,8 @@ def parse():
                     help="skip timing the index built from the first correspondence head's logits")
     ap.add_argument("--no-seq-lengths", action="store_true",
                     help="skip the S = 32 and S = 500 steps (latency against sequence length)")
+    ap.add_argument("--no-alone", action="store_true",
+                    help="skip timing the gather and the shared-key kernels each on their own heads")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip timing the 24-layer stack (index built once, the stack's per-layer plans)")
     ap.add_argument("--stack-inputs", type=int, default=3,
@@ -249,6 +253,40 @@ def main():
         torch.cuda.synchronize()
         attn.append(e0.elapsed_time(e1))
     attn_ms = statistics.median(attn)
+
+    # each kernel group on its own heads (contexts of their own, the same
+    # per-head data): the gathered heads alone, and the other heads alone, so
+    # the in-layer rates (the two kernels share the chip) can be read against
+    # the rates each reaches by itself
+    alone = None
+    if not args.no_alone:
+        corr_h = [h for h, r in enumerate(w.plan) if r[0] == 2]
+        other_h = [h for h, r in enumerate(w.plan) if r[0] != 2]
+
+        def group_alone(heads, name):
+            sub = saf.Context(g.S, g.ns, g.P, len(heads), g.d, torch.bfloat16)
+            qs, ks, vs = (t[heads].contiguous() for t in (q, k, v))
+            os_ = torch.empty_like(qs)
+            plan = [w.plan[h] for h in heads]
+            if any(r[0] == 2 for r in plan):
+                sub.set_corr_index(ctx.get_corr_index())
+            sub.sparse_attention(plan, qs, ks, vs, o=os_)
+            torch.cuda.synchronize()
+            sub.set_kernel_timing(True)
+            sub.read_kernel_timing()
+            ts = []
+            for _ in range(args.reps):
+                sub.sparse_attention(plan, qs, ks, vs, o=os_)
+                torch.cuda.synchronize()
+                ts.append(sum(ms for n, ms in sub.read_kernel_timing() if n == name))
+            sub.set_kernel_timing(False)
+            sub.close()
+            del qs, ks, vs, os_
+            return statistics.median(ts)
+
+        alone = {"gather_attention_ms": round(group_alone(corr_h, "gather_attention"), 4),
+                 "shared_attention_ms": round(group_alone(other_h, "shared_attention"), 4),
+                 "heads": {"gather": corr_h, "shared": other_h}}
 
     # cold caches: 1 GiB scrub before each rep
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -586,6 +624,18 @@ def main():
                   "frac": round(c["achieved"] / c["peak"], 4), "kernel_ms": round(c["ms"], 4),
                   "counters": counter_view(n, c["ms"])}
               for n, c in cand.items() if n != dom}
+    if alone:
+        # the same algorithmic work per kernel, at its time on its own heads
+        alone["gather_attention_gbs"] = round(gather_bytes / (alone["gather_attention_ms"] * 1e-3) / 1e9, 1)
+        alone["gather_attention_frac"] = round(alone["gather_attention_gbs"] / PEAK_HBM_GBS, 4)
+        # without the correspondence heads, whose dense special rows also run
+        # on the matrix cores in the layer
+        other_flops = 4.0 * d * (shared_pairs - n_corr * g.ns * g.S * g.N)
+        alone["shared_attention_tflops"] = round(other_flops / (alone["shared_attention_ms"] * 1e-3) / 1e12, 2)
+        alone["shared_attention_frac"] = round(alone["shared_attention_tflops"] / PEAK_BF16_TFLOPS, 4)
+        for n in ("gather_attention", "shared_attention"):
+            if n in others:
+                others[n]["alone"] = {k: v for k, v in alone.items() if k.startswith(n)}
     if dense_ms:
         others["dense"] = {"achieved": round(4.0 * d * g.H * g.N * g.N / (dense_ms * 1e-3) / 1e12, 2),
                            "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
