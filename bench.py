@@ -52,26 +52,26 @@ COUNTERS = {
     "fetch_scale": 1.99993,
     "write_scale": 1.0,
     "groups": {
-        "cosine_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-            "sha256": "9651fbf40147952751588b19938949e3e634235524386ed34dc4e28e4f5f786d",
-            "executed_tflop": 21.6576, "mfma_busy": 0.3766,
-            "fetch_kib": 37934459.2, "write_kib": 2814449.6},
-        "per_frame_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_index.hip",
-            "sha256": "9651fbf40147952751588b19938949e3e634235524386ed34dc4e28e4f5f786d",
-            "executed_tflop": 22.8345, "mfma_busy": 0.3079,
-            "fetch_kib": 40148678.5, "write_kib": 6040009.3},
+        "cosine_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_cos.hip",
+            "sha256": "2f37e5a815de8a4f9f353fbd242332c42a8168e8d2f8bc2c294a3b946987c28a",
+            "executed_tflop": 21.6576, "mfma_busy": 0.4245,
+            "fetch_kib": 38066372.8, "write_kib": 2791346.4},
+        "per_frame_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_cos.hip",
+            "sha256": "2f37e5a815de8a4f9f353fbd242332c42a8168e8d2f8bc2c294a3b946987c28a",
+            "executed_tflop": 22.8345, "mfma_busy": 0.3509,
+            "fetch_kib": 40193445.3, "write_kib": 6030291.7},
         "shared_attention": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
             "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
             "executed_tflop": 2.7005, "mfma_busy": 0.3749,
-            "fetch_kib": 797283.6, "write_kib": 230452.7},
+            "fetch_kib": 797284.7, "write_kib": 230452.2},
         "dense": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
             "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4243,
-            "fetch_kib": 7259348.5, "write_kib": 274801.5},
+            "executed_tflop": 77.3724, "mfma_busy": 0.4259,
+            "fetch_kib": 7669986.7, "write_kib": 274800.0},
         "gather_attention": {"source": "head_wise_dynamic_amd/csrc/attn_valu.hip",
             "sha256": "16a750096b436f0759d7ee9a55fec5dda2cc0ad23bc2f3d374188a4cf7c5eb41",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12612891.9, "write_kib": 51337.5},
+            "fetch_kib": 12619705.5, "write_kib": 51337.5},
     },
 }
 

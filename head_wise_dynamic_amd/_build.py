@@ -19,7 +19,12 @@ OUT = os.path.join(PKG, "libsaf3r.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("SAF_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "attn_mfma.hip", "attn_valu.hip", "vertical.hip", "corr_index.hip", "corr_block.hip", "nmse.hip", "noalloc.cpp"]
+# (source, object, extra flags): the cosine GEMM is compiled once per phase
+# mode (its instantiations dominate the build time), all units in parallel
+SOURCES = [(s, os.path.splitext(s)[0], []) for s in
+           ["api.cpp", "attn_mfma.hip", "attn_valu.hip", "vertical.hip", "corr_index.hip", "corr_block.hip",
+            "nmse.hip", "noalloc.cpp"]]
+SOURCES += [("corr_cos.hip", f"corr_cos_m{m}", [f"-DSAF_COS_MODE={m}"]) for m in range(7)]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
@@ -42,13 +47,14 @@ def _deps(path: str, seen=None) -> set:
     return seen
 
 
-def _compile(src: str, force: bool = True) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(unit, force: bool = True) -> str:
+    src, name, extra = unit
+    obj = os.path.join(BUILD, name + ".o")
     if not force and os.path.exists(obj):
         newest = max([os.path.getmtime(f) for f in _deps(os.path.join(CSRC, src))] + [os.path.getmtime(__file__)])
         if os.path.getmtime(obj) > newest:
             return obj
-    cmd = ["hipcc"] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ["hipcc"] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,8 +67,10 @@ def build(verbose: bool = False, force: bool = True) -> str:
     """Compile every source and link.  force=False reuses an object that is
     newer than its source, every header and this script."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda src: _compile(src, force), SOURCES))
+    # the slowest units first, so that they start at once
+    units = sorted(SOURCES, key=lambda u: u[0] not in ("corr_cos.hip", "corr_index.hip", "attn_mfma.hip"))
+    with ThreadPoolExecutor(max_workers=min(os.cpu_count() or 8, 16, len(units))) as ex:
+        objs = list(ex.map(lambda u: _compile(u, force), units))
     tmp = OUT + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
