@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -918,6 +919,21 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
         items.push_back(it);
     }
     std::stable_sort(items.begin(), items.end(), [](const Item &a, const Item &b) { return a.cost > b.cost; });
+    // While the side stream's gather runs, the first (longest) matrix-core
+    // blocks run at one work-group per compute unit: two take all of a
+    // SIMD's registers, and the gather's waves would wait for them to
+    // finish.  About as many blocks as finish while the gather runs: its
+    // K/V row bytes and the blocks' logit FLOP at the rates the two kernels
+    // reach side by side on MI355X (S = 100: ~5 TB/s and ~0.45 PFLOP/s).
+    constexpr double kShareGatherBytesPerMs = 5.0e9, kShareMfmaFlopPerMs = 0.45e12;
+    double share_ms = 0.0;
+    if (forked) {
+        double gather_bytes = 0.0;
+        for (int h = 0; h < g.H; ++h)
+            if (plan[h].role == SAF_CORRESPONDENCE || plan[h].role == SAF_CORR_STRIDE)
+                gather_bytes += (double)g.Np * c->corr_k * 4.0 * g.d;  // a K and a V bf16 row per key
+        share_ms = gather_bytes / kShareGatherBytesPerMs;
+    }
     saf::MfmaLaunch M{};
     M.g = g;
     M.q = q;
@@ -941,9 +957,22 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
         }
         if (blocks >= ((int64_t)1 << 31)) return fail(c, SAF_EINVAL, "launch too large");
         M.total_blocks = (int32_t)blocks;
+        int64_t shared_blocks = 0;  // blocks [0, shared_blocks) share the CUs with the gather
+        for (size_t i = i0; i < std::min(items.size(), i0 + saf::kMaxWork) && share_ms > 0.0; ++i) {
+            const int64_t nb = items[i].tiles * items[i].w.nsplit;
+            const double ms_per_block = 4.0 * g.d * QT * items[i].cost / kShareMfmaFlopPerMs;
+            const int64_t take = std::min<int64_t>(nb, (int64_t)std::ceil(share_ms / ms_per_block));
+            shared_blocks += take;
+            share_ms = take < nb ? 0.0 : share_ms - (double)take * ms_per_block;
+        }
         {
             Timed tm(c, s, "shared_attention");
-            e = saf::launch_mfma_attention(M, s);
+            M.block_base = 0;
+            e = saf::launch_mfma_attention(M, (int32_t)shared_blocks, true, s);
+            if (e == hipSuccess) {
+                M.block_base = (int32_t)shared_blocks;
+                e = saf::launch_mfma_attention(M, (int32_t)(blocks - shared_blocks), false, s);
+            }
         }
         if (e != hipSuccess) return hip_fail(c, e, "matrix-core attention kernel");
         {
@@ -1053,10 +1082,11 @@ saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, con
             M.work[M.nwork++] = w;
         }
         M.total_blocks = (int32_t)blocks;
+        M.block_base = 0;
         hipError_t e;
         {
             Timed tm(c, s, "dense_attention");
-            e = saf::launch_mfma_attention(M, s);
+            e = saf::launch_mfma_attention(M, M.total_blocks, false, s);
         }
         if (e != hipSuccess) return hip_fail(c, e, "dense attention kernel");
     }

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const int kx = 4 * ((n >> 2) & 1);  // K rows are read as swap_bits23(n): bit 3 of the row = bit 2 of n
 
     // ---- locate this work-group's head, query tile and key split
-    const int b = blockIdx.x;
+    const int b = blockIdx.x + L.block_base;
     int wi = 0;
     for (int i = 1; i < L.nwork; ++i)
         if (L.work[i].block0 <= b) wi = i;
@@ -445,17 +445,41 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const MfmaLaunch L) 
 
 }  // namespace
 
-hipError_t launch_mfma_attention(const MfmaLaunch &L, hipStream_t stream) {
-    if (L.total_blocks <= 0) return hipSuccess;
+// Dynamic LDS that holds the key-set kernel to one work-group per compute
+// unit: more than half of the CU's LDS per work-group (0: not possible).
+// A failed query leaves no error behind: the launch then runs unshared.
+static int share_cu_lds() {
+    int dev = 0, lds_cu = 0;
+    hipFuncAttributes fa{};
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipFuncGetAttributes(&fa, (const void *)mfma_attn_kernel<false>) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int dyn = lds_cu / 2 + 256 - (int)fa.sharedSizeBytes;
+    if (dyn <= 0 || (int)fa.sharedSizeBytes + dyn > lds_cu) return 0;
+    if (hipFuncSetAttribute((const void *)mfma_attn_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            dyn) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return dyn;
+}
+
+hipError_t launch_mfma_attention(const MfmaLaunch &L, int32_t nblocks, bool share_cu, hipStream_t stream) {
+    if (nblocks <= 0) return hipSuccess;
     // every piece of work a dense head over all rows: the contiguous-key kernel
     bool dense = true;
     for (int i = 0; i < L.nwork; ++i)
         dense = dense && L.work[i].role == DENSE && L.work[i].rows == ROWS_ALL && L.work[i].nsplit == 1 &&
                 !L.work[i].rec_out;
-    if (dense)
-        hipLaunchKernelGGL(mfma_attn_kernel<true>, dim3(L.total_blocks), dim3(kAttnThreads), 0, stream, L);
-    else
-        hipLaunchKernelGGL(mfma_attn_kernel<false>, dim3(L.total_blocks), dim3(kAttnThreads), 0, stream, L);
+    if (dense) {
+        hipLaunchKernelGGL(mfma_attn_kernel<true>, dim3(nblocks), dim3(kAttnThreads), 0, stream, L);
+    } else {
+        const int dyn = share_cu ? share_cu_lds() : 0;
+        hipLaunchKernelGGL(mfma_attn_kernel<false>, dim3(nblocks), dim3(kAttnThreads), (unsigned)dyn, stream, L);
+    }
     return hipGetLastError();
 }
 

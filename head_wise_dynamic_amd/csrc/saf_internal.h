@@ -68,6 +68,7 @@ struct MfmaLaunch {
     int64_t head_stride, token_stride;
     int32_t nwork;
     int32_t total_blocks;
+    int32_t block_base;  // a launch runs blocks [block_base, block_base + grid) of the work list
     HeadWork work[kMaxWork];
 };
 
@@ -88,7 +89,10 @@ struct ValuLaunch {
 
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launch.
-hipError_t launch_mfma_attention(const MfmaLaunch &L, hipStream_t stream);
+// Blocks [L.block_base, L.block_base + nblocks).  share_cu: at most one
+// work-group per compute unit (a larger LDS allocation), so that a kernel on
+// another stream finds registers beside it on every SIMD.
+hipError_t launch_mfma_attention(const MfmaLaunch &L, int32_t nblocks, bool share_cu, hipStream_t stream);
 hipError_t launch_split_combine(const MfmaLaunch &L, hipStream_t stream);
 hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t stream);
 // CORR_STRIDE heads (bf16): merge, for every patch row, the stride set's
