@@ -54,24 +54,24 @@ COUNTERS = {
     "groups": {
         "cosine_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_cos.hip",
             "sha256": "2f37e5a815de8a4f9f353fbd242332c42a8168e8d2f8bc2c294a3b946987c28a",
-            "executed_tflop": 21.6576, "mfma_busy": 0.4245,
-            "fetch_kib": 38066372.8, "write_kib": 2791346.4},
+            "executed_tflop": 21.6576, "mfma_busy": 0.4149,
+            "fetch_kib": 37899226.5, "write_kib": 2824386.7},
         "per_frame_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_cos.hip",
             "sha256": "2f37e5a815de8a4f9f353fbd242332c42a8168e8d2f8bc2c294a3b946987c28a",
-            "executed_tflop": 22.8345, "mfma_busy": 0.3509,
-            "fetch_kib": 40193445.3, "write_kib": 6030291.7},
+            "executed_tflop": 22.8345, "mfma_busy": 0.347,
+            "fetch_kib": 40156949.8, "write_kib": 6026023.3},
         "shared_attention": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
-            "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
-            "executed_tflop": 2.7005, "mfma_busy": 0.3749,
-            "fetch_kib": 797284.7, "write_kib": 230452.2},
+            "sha256": "fb77e72815cb0f6979f71554a63106efd0cd727f8421fd78c63a4a2d613a72cd",
+            "executed_tflop": 2.7005, "mfma_busy": 0.248,
+            "fetch_kib": 809020.4, "write_kib": 230493.8},
         "dense": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
-            "sha256": "36e8a292d6f50a6caf7e2589b48f65388998687cba43ba6a928e51fc2e5ced93",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4259,
-            "fetch_kib": 7669986.7, "write_kib": 274800.0},
+            "sha256": "fb77e72815cb0f6979f71554a63106efd0cd727f8421fd78c63a4a2d613a72cd",
+            "executed_tflop": 77.3724, "mfma_busy": 0.4179,
+            "fetch_kib": 6822118.2, "write_kib": 274800.0},
         "gather_attention": {"source": "head_wise_dynamic_amd/csrc/attn_valu.hip",
             "sha256": "16a750096b436f0759d7ee9a55fec5dda2cc0ad23bc2f3d374188a4cf7c5eb41",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12619705.5, "write_kib": 51337.5},
+            "fetch_kib": 12609934.7, "write_kib": 51337.5},
     },
 }
 
