@@ -37,9 +37,9 @@ PEAK_BF16_TFLOPS = 2500.0
 
 # Counter readings of the step's kernel groups on the S = 100 workload
 # (rocprofv3 --pmc, one pass per group of counters; per step: the index
-# build's cosine GEMM is 1 seed-bound + 6 filtered + 1 symmetric launch, the
-# fused per-frame build's GEMM 1 sampled + 1 filtered symmetric launch, the
-# others one launch).  executed_tflop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+# build's cosine GEMM is 1 seed-bound + 1 symmetric launch, the fused
+# per-frame build's GEMM 1 sampled + 1 filtered symmetric launch, the
+# shared-key attention two launches, the others one).  executed_tflop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
 # FLOP; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x
 # 1024 SIMDs), the share of SIMD cycles the matrix cores were busy while the
 # kernel ran; fetch/write = FETCH_SIZE / WRITE_SIZE in KiB, scaled by what

@@ -67,7 +67,9 @@ struct Args {
     int64_t seed_cols;       // columns of the seed phase (whole frames)
     int64_t sym_lo;          // start of the symmetric square [sym_lo, Np)^2
     float *chunk;            // STORE mode: cosines of rows [row_lo, row_hi) x all columns
-    int32_t guess_k;         // compaction: also set theta_g from the guess_k-th best (0: no)
+    int32_t guess_k;         // compaction: also set theta_g from the guess_k-th best (0: no); bound_rows:
+                             // theta_g from the guess_k-th largest lane maximum (0: no)
+    int32_t guess_k_seed;    // bound_rows: that rank for rows of the two seed frames (one frame fewer seen)
     int32_t raw_dot;         // scores are plain dot products (unit "norms")
     const void *Fc;          // column operand (== F for the symmetric cosine)
     int32_t tok_map;         // row u of F / Fc is token (u / P) T + ns + u % P (patches of a token layout)

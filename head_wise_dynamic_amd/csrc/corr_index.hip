@@ -11,6 +11,13 @@
 // to a per-row candidate buffer (staged in LDS, one global atomic per row
 // per tile).  After each phase a compaction wave per row raises theta_u to a
 // lower bound of the K-th best of its buffer and drops what lies below.
+// Direct square (4 K + 128 <= P, one operand for rows and columns, and the
+// two seed frames holding on average at least 5 of a row's K best:
+// 2 K >= 5 (S - 1)): the seed phase's lane maxima (as in 1. below) give
+// every row a guess theta_g_u of its K-th best, their r-th largest with r
+// the guess rank over the seed columns of other frames; the whole square
+// [0, Np)^2 is then filtered by it once per unordered pair, compacted, and
+// finalized with the guess check of 4./5.  Otherwise:
 //   1. seed: columns of frames 0 and 1.  When 4 K + 128 <= P, only each
 //      lane's largest cosine over its 4 seed columns of other frames is
 //      kept, and a row's K-th largest such value (reached by K distinct
@@ -88,7 +95,9 @@ template <typename T> __global__ __launch_bounds__(256) void init_rows(const Arg
 }
 
 // ---- bound seed: each row's K-th largest stored lane maximum (TBOUND) as
-// its first threshold; a row with fewer than K of them gets none (-inf)
+// its first threshold; a row with fewer than K of them gets none (-inf).
+// With a guess rank (A.guess_k), also theta_g from the guess_k-th largest:
+// the direct square's filter, checked when the row is finalized.
 template <int MAXE> __global__ __launch_bounds__(256) void bound_rows(const Args A) {
     const int64_t u = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -101,15 +110,25 @@ template <int MAXE> __global__ __launch_bounds__(256) void bound_rows(const Args
     for (int e = 0; e < MAXE; ++e) x[e] = lm[min(e * 64 + lane, n - 1)];  // unconditional, masked below
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) key[e] = (e * 64 + lane < n && x[e] > -INFINITY) ? order_key(x[e]) : 0u;
-    uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        uint32_t c = 0;
+    // largest order key reached by at least `rank` stored values (0: fewer values)
+    auto kth_key = [&](uint32_t rank) {
+        uint32_t thr = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            uint32_t c = 0;
 #pragma unroll
-        for (int e = 0; e < MAXE; ++e) c += (uint32_t)__popcll(__ballot(key[e] >= cand));
-        if (c >= (uint32_t)A.K) thr = cand;
-    }
+            for (int e = 0; e < MAXE; ++e) c += (uint32_t)__popcll(__ballot(key[e] >= cand));
+            if (c >= rank) thr = cand;
+        }
+        return thr;
+    };
+    const uint32_t thr = kth_key((uint32_t)A.K);
     if (lane == 0) A.s.theta[u] = thr ? order_key_to_float(thr) : -INFINITY;
+    if (A.guess_k) {
+        const uint32_t rank = (uint32_t)(u < 2 * (int64_t)A.g.P ? A.guess_k_seed : A.guess_k);
+        const uint32_t gthr = kth_key(rank);
+        if (lane == 0) A.s.theta_g[u] = gthr ? order_key_to_float(gthr) : -INFINITY;
+    }
 }
 
 // ---- per-row selection inside one wave.
@@ -1064,8 +1083,15 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     const bool bound_seed = gemm && seed_cols == 2 * (int64_t)B.g.P && B.g.P <= 4096 &&
                             4 * (int64_t)B.K + 128 <= B.g.P;
     A.seed_cols = bound_seed ? 0 : seed_cols;
+    // Direct square (bound seed, one operand for rows and columns): every
+    // row's guess of its K-th best comes from the seed frames' lane maxima,
+    // and the whole square [0, Np)^2 is filtered by it once per unordered pair
+    // (no filtered column phases, no compaction between them).  The seed
+    // frames hold on average K 2P / ((S-1) P) of a row's K best; below 5 the
+    // guess fails too often (each failure is a recomputed row).
+    const bool direct = bound_seed && A.Fc == A.F && (int64_t)B.K * seed_cols >= 5ll * (B.g.S - 1) * B.g.P;
     // the symmetric square needs one operand for rows and columns
-    A.sym_lo = (A.Fc == A.F) ? corr_sym_start(B.g) : Np;
+    A.sym_lo = direct ? 0 : (A.Fc == A.F) ? corr_sym_start(B.g) : Np;
     const unsigned rb = (unsigned)((Np + 3) / 4);
     if (B.dino_dtype == BF16)
         hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
@@ -1100,7 +1126,38 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             A.guess_k = 0;
         };
         int64_t lo0 = seed_cols;
-        if (bound_seed) {
+        if (direct) {
+            // 1. the seed frames' lane maxima: a lower bound (theta) and a
+            // guess (theta_g) of every row's K-th best; the guess rank is
+            // corr_guess_rank's over the seed columns of other frames
+            A.row_lo = 0;
+            A.row_hi = Np;
+            A.col_lo = 0;
+            A.col_hi = seed_cols;
+            A.lm_per_row = (int32_t)((seed_cols + CT - 1) / CT * 64);
+            const int64_t tiles = ((Np + CT - 1) / CT) * ((seed_cols + CT - 1) / CT);
+            if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+            launch_cos<TBOUND>(dim3((unsigned)(8 * ((tiles + 7) / 8))), stream, A);
+            if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+            A.guess_k = corr_guess_rank(B.g, B.K, seed_cols);
+            A.guess_k_seed = corr_guess_rank(B.g, B.K, seed_cols - B.g.P);
+            if (A.lm_per_row <= 16 * 64)
+                hipLaunchKernelGGL(bound_rows<16>, dim3(cb), dim3(256), 0, stream, A);
+            else
+                hipLaunchKernelGGL(bound_rows<32>, dim3(cb), dim3(256), 0, stream, A);
+            A.guess_k = A.guess_k_seed = 0;
+            // 2. the square [0, Np)^2 once per unordered pair
+            const int64_t nt = (Np + CT - 1) / CT;
+            const int64_t sq = nt * (nt + 1) / 2;
+            A.row_lo = 0;
+            A.row_hi = Np;
+            A.col_lo = 0;
+            A.col_hi = Np;
+            if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+            launch_cos<SYM>(dim3((unsigned)(8 * ((sq + 7) / 8))), stream, A);
+            if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+            compact();
+        } else if (bound_seed) {
             // 1. bounds from the seed frames' lane maxima, then the first
             // filtered phase over [0, 2 seed)
             A.row_lo = 0;
@@ -1123,9 +1180,9 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             rect(SEED, 0, Np, 0, seed_cols);
         }
         // 2. doubling filtered phases for every row up to W
-        for (int64_t lo = lo0; lo < W; lo = std::min<int64_t>(2 * lo, W))
+        for (int64_t lo = lo0; !direct && lo < W; lo = std::min<int64_t>(2 * lo, W))
             rect(FILTER, 0, Np, lo, std::min<int64_t>(2 * lo, W));
-        if (W < Np) {
+        if (!direct && W < Np) {
             // 3. rows below W keep doubling over the remaining columns
             for (int64_t lo = W; lo < Np; lo = std::min<int64_t>(2 * lo, Np))
                 rect(FILTER, 0, W, lo, std::min<int64_t>(2 * lo, Np));
