@@ -52,43 +52,49 @@ COUNTERS = {
     "fetch_scale": 1.99993,
     "write_scale": 1.0,
     "groups": {
-        "cosine_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_cos.hip",
-            "sha256": "2f37e5a815de8a4f9f353fbd242332c42a8168e8d2f8bc2c294a3b946987c28a",
-            "executed_tflop": 21.6576, "mfma_busy": 0.4149,
-            "fetch_kib": 37899226.5, "write_kib": 2824386.7},
-        "per_frame_gemm": {"source": "head_wise_dynamic_amd/csrc/corr_cos.hip",
-            "sha256": "2f37e5a815de8a4f9f353fbd242332c42a8168e8d2f8bc2c294a3b946987c28a",
-            "executed_tflop": 22.8345, "mfma_busy": 0.347,
-            "fetch_kib": 40156949.8, "write_kib": 6026023.3},
-        "shared_attention": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
-            "sha256": "fb77e72815cb0f6979f71554a63106efd0cd727f8421fd78c63a4a2d613a72cd",
-            "executed_tflop": 2.7005, "mfma_busy": 0.248,
-            "fetch_kib": 809020.4, "write_kib": 230493.8},
-        "dense": {"source": "head_wise_dynamic_amd/csrc/attn_mfma.hip",
-            "sha256": "fb77e72815cb0f6979f71554a63106efd0cd727f8421fd78c63a4a2d613a72cd",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4179,
-            "fetch_kib": 6822118.2, "write_kib": 274800.0},
-        "gather_attention": {"source": "head_wise_dynamic_amd/csrc/attn_valu.hip",
-            "sha256": "16a750096b436f0759d7ee9a55fec5dda2cc0ad23bc2f3d374188a4cf7c5eb41",
+        "cosine_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
+            "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
+            "executed_tflop": 20.034, "mfma_busy": 0.4355,
+            "fetch_kib": 38577781.0, "write_kib": 2037077.0},
+        "per_frame_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
+            "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
+            "executed_tflop": 22.8345, "mfma_busy": 0.3471,
+            "fetch_kib": 40230639.7, "write_kib": 6027339.8},
+        "shared_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
+            "sha256": "b0d13da183fa6e0033f35f3c2e0d652437d2e3d7e876fe12f56a21dc64315ef6",
+            "executed_tflop": 2.7005, "mfma_busy": 0.2485,
+            "fetch_kib": 810963.9, "write_kib": 230489.9},
+        "dense": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
+            "sha256": "b0d13da183fa6e0033f35f3c2e0d652437d2e3d7e876fe12f56a21dc64315ef6",
+            "executed_tflop": 77.3724, "mfma_busy": 0.4242,
+            "fetch_kib": 6821681.2, "write_kib": 274800.0},
+        "gather_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_valu.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
+            "sha256": "9bc2aace1a211723f2327c911c196c838e58a00bf2b0b14c673b37e487e38323",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12609934.7, "write_kib": 51337.5},
+            "fetch_kib": 12610208.6, "write_kib": 51337.5},
     },
 }
 
 
 def counters_for(group, config):
     """The recorded counter figures of a kernel group, with its HBM traffic in
-    GB, or None for another workload or when the kernel source no longer
-    matches the one they were taken on."""
+    GB, or None for another workload or when the sources no longer match the
+    ones they were taken on (the kernel's file, or a list of files: the
+    kernel and the code that schedules its launches; the digest is over
+    their bytes in order)."""
     import hashlib
     rec = COUNTERS["groups"].get(group)
     if rec is None or config != COUNTERS["config"]:
         return None
+    srcs = rec["source"] if isinstance(rec["source"], list) else [rec["source"]]
+    h = hashlib.sha256()
     try:
-        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-                return None
+        for src in srcs:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
     except OSError:
+        return None
+    if h.hexdigest() != rec["sha256"]:
         return None
     out = dict(rec)
     out["traffic_gb"] = (rec["fetch_kib"] * COUNTERS["fetch_scale"] + rec["write_kib"] * COUNTERS["write_scale"]) \
