@@ -49,3 +49,25 @@ def test_recorded_groups_cover_the_step_kernels():
     # its algorithmic 2 (S P)^2 Df = 38.4 TFLOP at S = 100
     assert 0 < g["cosine_gemm"]["executed_tflop"] < 38.4
     assert 0 < g["shared_attention"]["mfma_busy"] < 1 and 0 < g["dense"]["mfma_busy"] < 1
+
+
+def test_counters_keyed_on_every_listed_source(tmp_path):
+    """A group recorded over two files (the kernel and the code that
+    schedules its launches) loses its figures when either file changes."""
+    b = _bench()
+    a, s = tmp_path / "kernel.hip", tmp_path / "schedule.cpp"
+    a.write_bytes(b"// kernel\n")
+    s.write_bytes(b"// schedule\n")
+    rec = dict(b.COUNTERS["groups"]["cosine_gemm"])
+    rec["source"] = [str(a), str(s)]
+    rec["sha256"] = hashlib.sha256(a.read_bytes() + s.read_bytes()).hexdigest()
+    b.COUNTERS["groups"]["probe2"] = rec
+    cfg = b.COUNTERS["config"]
+    assert b.counters_for("probe2", cfg) is not None
+    s.write_bytes(b"// another schedule\n")
+    assert b.counters_for("probe2", cfg) is None
+    s.write_bytes(b"// schedule\n")
+    assert b.counters_for("probe2", cfg) is not None
+    a.write_bytes(b"// another kernel\n")
+    assert b.counters_for("probe2", cfg) is None
+
