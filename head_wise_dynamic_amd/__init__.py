@@ -430,7 +430,10 @@ class Context:
         if o is None:
             o = torch.empty_like(q)
         lay = self._tensors(q, ("k", k), ("v", v), ("o", o))
+        need = self.workspace_size(None)
+        ws = self.workspace(need, q.device) if need else None
         self._check(saf_dense_attention(self._ctx, C.c_void_p(q.data_ptr()), C.c_void_p(k.data_ptr()),
-                                        C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), lay, None, 0,
-                                        _stream(stream)))
+                                        C.c_void_p(v.data_ptr()), C.c_void_p(o.data_ptr()), lay,
+                                        C.c_void_p(ws.data_ptr()) if ws is not None else None,
+                                        ws.numel() if ws is not None else 0, _stream(stream)))
         return o

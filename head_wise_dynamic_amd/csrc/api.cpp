@@ -171,8 +171,14 @@ struct PlanInfo {
     int64_t vert_ws = 0;      // bytes for in-call vertical index builds
     int64_t split_ws = 0;     // bytes for dense-row split partials
     int64_t union_ws = 0;     // bytes for the records of correspondence + stride heads
+    int64_t norm_ws = 0;      // bytes for the key-norm maxima of the matrix-core launches
     int corr_splits = 1;
 };
+
+// key-norm maxima of one matrix-core launch group (bf16 contexts)
+int64_t norm_bytes(const saf::Geom &g) {
+    return g.dtype == saf::BF16 ? (int64_t)align256(sizeof(float) * saf::kMaxWork * saf::kNormParts) : 0;
+}
 
 int corr_special_splits(const saf::Geom &g) {
     const int64_t s = (g.N + kSplitKeys - 1) / kSplitKeys;
@@ -247,6 +253,7 @@ saf_status_t check_plan(saf_ctx_t *c, const saf_head_plan_t *plan, PlanInfo *pi)
         if (pi->corr_splits > 1) pi->split_ws = (int64_t)ndense_specials * split_part_bytes(g, pi->corr_splits);
         pi->union_ws = (int64_t)pi->nunion * union_rec_bytes(g);
     }
+    pi->norm_ws = norm_bytes(g);
     return SAF_OK;
 }
 
@@ -268,7 +275,9 @@ saf_status_t saf_create(const saf_geometry_t *geom, saf_ctx_t **out) {
     if (G.head_dim != 64) return fail(nullptr, SAF_EUNSUPPORTED, "geometry: head_dim must be 64");
     const int64_t T = (int64_t)G.specials_per_frame + G.patches_per_frame;
     const int64_t N = T * G.num_frames;
-    if (N >= (int64_t)1 << 31) return fail(nullptr, SAF_EINVAL, "geometry: N must be < 2^31");
+    // key-set sizes (at most N + ns S) stay below 2^31; a larger N would not
+    // fit one GPU's memory anyway (Q alone: H x 2^30 x 64 x 2 bytes)
+    if (N >= (int64_t)1 << 30) return fail(nullptr, SAF_EINVAL, "geometry: N must be < 2^30");
     saf_ctx_t *c = new (std::nothrow) saf_ctx_t();
     if (!c) return fail(nullptr, SAF_ENOMEM, "out of host memory");
     c->g.S = G.num_frames;
@@ -313,11 +322,15 @@ saf_status_t saf_workspace_size(const saf_ctx_t *cc, const saf_head_plan_t *plan
     if (!c) return SAF_EINVAL;
     if (!bytes) return fail(c, SAF_EINVAL, "null bytes pointer");
     *bytes = 0;
-    if (!plan) return SAF_OK;  // dense attention needs none
+    if (!plan) {  // dense attention: the key-norm maxima (bf16)
+        const int64_t nb = norm_bytes(c->g);
+        *bytes = nb ? (size_t)nb + 256 : 0;
+        return SAF_OK;
+    }
     PlanInfo pi;
     const saf_status_t st = check_plan(c, plan, &pi);
     if (st != SAF_OK) return st;
-    *bytes = (size_t)(pi.vert_ws + pi.split_ws + pi.union_ws) + 256;
+    *bytes = (size_t)(pi.vert_ws + pi.split_ws + pi.union_ws + pi.norm_ws) + 256;
     return SAF_OK;
 }
 
@@ -671,7 +684,7 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
                 return fail(c, SAF_ESTATE, "head %d budget %d differs from the index's K %d (row length %d)", h,
                             plan[h].budget, c->corr_build_k, c->corr_k);
     }
-    size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws);
+    size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws + pi.norm_ws);
     if (need > 0) need += 256;  // room to align the start to 256 bytes
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(c, SAF_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -942,6 +955,10 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
     M.o = o;
     M.head_stride = lay.head_stride;
     M.token_stride = lay.token_stride;
+    // key-norm maxima: one buffer, reused by the launch groups in stream order
+    float *knorm = (float *)wp;
+    wp += pi.norm_ws;
+    M.knorm = knorm;
     for (size_t i0 = 0; i0 < items.size(); i0 += saf::kMaxWork) {
         M.nwork = 0;
         int64_t blocks = 0;
@@ -965,6 +982,11 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
             shared_blocks += take;
             share_ms = take < nb ? 0.0 : share_ms - (double)take * ms_per_block;
         }
+        {
+            Timed tm(c, s, "key_norms");
+            e = saf::launch_key_norms(M, knorm, s);
+        }
+        if (e != hipSuccess) return hip_fail(c, e, "key norm kernel");
         {
             Timed tm(c, s, "shared_attention");
             M.block_base = 0;
@@ -1024,13 +1046,16 @@ saf_status_t saf_sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, con
 
 saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, const void *v, void *o,
                                  saf_layout_t lay, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (!c) return SAF_EINVAL;
     const saf::Geom &g = c->g;
     saf_status_t st;
     if ((st = check_tensors(c, q, k, v, o)) != SAF_OK) return st;
     if ((st = check_layout(c, lay)) != SAF_OK) return st;
+    const int64_t nb = norm_bytes(g);
+    const size_t need = nb ? (size_t)nb + 256 : 0;
+    if (need > 0 && (!ws || ws_bytes < need)) return fail(c, SAF_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (ws && !aligned16(ws)) return fail(c, SAF_EINVAL, "workspace must be 16-byte aligned");
+    float *knorm = nb ? (float *)(((uintptr_t)ws + 255) & ~(uintptr_t)255) : nullptr;
     hipStream_t s = as_stream(stream);
     if (g.dtype == saf::F32) {
         saf::ValuLaunch L{};
@@ -1067,6 +1092,7 @@ saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, con
     M.o = o;
     M.head_stride = lay.head_stride;
     M.token_stride = lay.token_stride;
+    M.knorm = knorm;
     const int64_t all_tiles = (g.N + QT - 1) / QT;
     for (int h0 = 0; h0 < g.H; h0 += saf::kMaxWork) {
         M.nwork = 0;
@@ -1086,7 +1112,8 @@ saf_status_t saf_dense_attention(saf_ctx_t *c, const void *q, const void *k, con
         hipError_t e;
         {
             Timed tm(c, s, "dense_attention");
-            e = saf::launch_mfma_attention(M, M.total_blocks, false, s);
+            e = saf::launch_key_norms(M, knorm, s);
+            if (e == hipSuccess) e = saf::launch_mfma_attention(M, M.total_blocks, false, s);
         }
         if (e != hipSuccess) return hip_fail(c, e, "dense attention kernel");
     }
@@ -1136,7 +1163,7 @@ saf_status_t saf_layer_internal(saf_ctx_t *c, const saf_head_plan_t *plan, const
     PlanInfo pi;
     saf_status_t st = check_plan(c, plan, &pi);
     if (st != SAF_OK) return st;
-    *ws_need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws) + 256;
+    *ws_need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws + pi.norm_ws) + 256;
     if (*ws_need > ws_cap)
         return fail(c, SAF_EUNSUPPORTED, "this plan needs %zu bytes of workspace; the static scratch holds %zu",
                     *ws_need, ws_cap);

@@ -22,6 +22,17 @@
 // that enter P.V (v_dot2c_f32_bf16), so the output is an exact convex
 // combination of the V rows under those weights.
 // exp is computed as exp2 with log2(e)/sqrt(d) folded into one FMA.
+//
+// Softmax shift.  Softmax is unchanged by subtracting any per-query constant
+// from the logits; the running maximum is only one choice.  With the head's
+// largest key norm known (key_norm_kernel), every logit of query q is at most
+// B_q = |q| max_j |k_j| (Cauchy-Schwarz; scaled to log2 units).  A wave whose
+// queries all have B_q <= kShiftBoundMax subtracts the fixed shift
+// m_q = max(B_q - kShiftHeadroom, 0): every weight is at most 2^kShiftHeadroom,
+// and the largest weight (its logit is >= -B_q) is at least
+// 2^-(2 kShiftBoundMax - kShiftHeadroom) = 2^-80, far above the smallest
+// normal float, so no per-tile maximum, cross-lane exchange or rescale of O
+// is needed.  Other waves keep the online running maximum.
 #include "device_util.h"
 
 namespace saf {
@@ -51,6 +62,13 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
                                            acc, false);
 }
 constexpr int PSTRIDE = kRecStride;  // split partial record: m, l, o[64]
+constexpr float kShiftBoundMax = 56.f;  // log2 units
+constexpr float kShiftHeadroom = 32.f;
+
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
 
 __device__ __forceinline__ int kswz(int row) { return 4 * ((row >> 3) & 1); }
 
@@ -140,11 +158,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const uint16_t *K = (const uint16_t *)L.k + hoff;
     const uint16_t *V = (const uint16_t *)L.v + hoff;
 
-    const int64_t count = DENSE ? g.N : key_count(w, g, rm.qsel);
-    const int64_t per = ((count + w.nsplit - 1) / w.nsplit + KT - 1) / KT * KT;
-    const int64_t kbeg = (int64_t)split * per;
-    const int64_t kend = min<int64_t>(count, kbeg + per);
-    const int64_t first_masked = DENSE ? INT64_MAX : key_first_masked(w, g);
+    // key slots in 32 bits: a key set holds at most N + ns S < 2^31 slots
+    const int32_t count = (int32_t)(DENSE ? g.N : key_count(w, g, rm.qsel));
+    const int32_t per = ((count + w.nsplit - 1) / w.nsplit + KT - 1) / KT * KT;
+    const int32_t kbeg = split * per;
+    const int32_t kend = min(count, kbeg + per);
+    const int32_t first_masked = DENSE ? INT32_MAX : (int32_t)min<int64_t>(key_first_masked(w, g), INT32_MAX);
 
     // Key enumeration without 64-bit divisions (N < 2^31): position and
     // scanning sets are the special tokens (from an LDS table built once per
@@ -174,23 +193,54 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
 
     // ---- this wave's 64 query rows as two 32-row B operands (4 k-steps each)
     bool qvalid[2];
-    int64_t qtok[2];
+    int32_t qtok[2];  // N < 2^30
     bf16x8 qreg[2][4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const int qr = wave * 64 + 32 * qb + n;
         qvalid[qb] = qr < rm.valid;
-        qtok[qb] = qvalid[qb] ? tile_row(rm, g, qr) : 0;
+        qtok[qb] = qvalid[qb] ? (int32_t)tile_row(rm, g, qr) : 0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             u32x4 raw = {0u, 0u, 0u, 0u};
-            if (qvalid[qb]) raw = *(const u32x4 *)(Q + qtok[qb] * ts + 16 * c + 8 * gq);
+            if (qvalid[qb]) raw = *(const u32x4 *)(Q + (int64_t)qtok[qb] * ts + 16 * c + 8 * gq);
             qreg[qb][c] = __builtin_bit_cast(bf16x8, raw);
         }
     }
 
     const float sc = kLog2e * 0.125f;  // log2(e) / sqrt(64)
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    // fixed softmax shift from the Cauchy-Schwarz bound (see the top of the
+    // file); lanes n and n + 32 hold the two channel halves of a query
+    bool fixed = false;
+    if (L.knorm) {
+        float k2 = L.knorm[wi * kNormParts + lane];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, off));
+        float bmax = 0.f, bq[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float q2 = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const u32x4 u = __builtin_bit_cast(u32x4, qreg[qb][c]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(u[e] << 16), hi = __uint_as_float(u[e] & 0xFFFF0000u);
+                    q2 = fmaf(lo, lo, fmaf(hi, hi, q2));
+                }
+            }
+            q2 += __shfl_xor(q2, 32);
+            bq[qb] = sqrtf(q2 * k2) * sc;
+            bmax = fmaxf(bmax, bq[qb]);
+        }
+        fixed = !__any(!(bmax <= kShiftBoundMax));  // a NaN bound takes the running maximum
+        if (fixed) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) m_run[qb] = fmaxf(bq[qb] - kShiftHeadroom, 0.f);
+        }
+    }
     f32x16 oacc[2][2];  // [query block][channel block]
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
@@ -204,7 +254,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     constexpr int kUnits = (KT / 2) * 8 / kAttnThreads;
     u32x4 kreg[kUnits][2], vreg[kUnits][2];
     bool kval[kUnits][2];
-    auto load_tile = [&](int64_t kt) {
+    auto load_tile = [&](int32_t kt) {
 #pragma unroll
         for (int j = 0; j < kUnits; ++j) {
             const int unit = tid + kAttnThreads * j, lp = unit >> 3, lseg = unit & 7;
@@ -213,11 +263,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
             // reads token 0 and is zeroed when the tile is stored.  Guarded
             // loads would make the compiler wait for them before the current
             // tile's first MFMA, which defeats the prefetch.
-            int64_t tk[2];
+            int32_t tk[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int64_t m = kt + 2 * lp + i;
-                tk[i] = (m < kend) ? token_of(m) : -1;
+                const int32_t m = kt + 2 * lp + i;
+                tk[i] = (m < kend) ? (int32_t)token_of(m) : -1;
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -261,7 +311,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         }
     };
 
-    const int64_t ntiles = (kend - kbeg + KT - 1) / KT;
+    const int32_t ntiles = (kend - kbeg + KT - 1) / KT;
     if (ntiles > 0) {
         load_tile(kbeg);
         store_tile(0, kbeg + KT <= kend);
@@ -273,9 +323,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt at their maxima
     __syncthreads();
 
-    for (int64_t t = 0; t < ntiles; ++t) {
-        const int buf = (int)(t & 1);
-        const int64_t kt = kbeg + t * KT;
+    auto tile_loop = [&](auto fixed_tag) {
+    constexpr bool FIXED = decltype(fixed_tag)::value;
+    for (int32_t t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        const int32_t kt = kbeg + t * KT;
         if (t + 1 < ntiles) load_tile(kt + KT);
 
         // S^T = K Q^T: two 32-key blocks x two 32-query blocks; each K
@@ -304,11 +356,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
                     for (int qb = 0; qb < 2; ++qb) s[bb][qb][r] += bias;
                 }
         }
-        // online softmax per query block (log2 domain).  The running max is
-        // only raised when a logit exceeds it by more than 8 (weights stay
-        // <= 2^8), so the O rescale is skipped on most tiles.
+        // softmax weights per query block (log2 domain).  Fixed shift: the
+        // bound-derived m_q.  Otherwise an online running max, only raised
+        // when a logit exceeds it by more than 8 (weights stay <= 2^8), so
+        // the O rescale is skipped on most tiles.
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+            if (FIXED) {
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[bb][qb][r] = fast_exp2(fmaf(s[bb][qb][r], sc, -m_run[qb]));
+                continue;
+            }
             float mx = s[0][qb][0];
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb)
@@ -368,6 +428,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         if (t + 1 < ntiles) store_tile(buf ^ 1, kt + 2 * KT <= kend);
         __syncthreads();
     }
+    };
+    if (fixed)
+        tile_loop(BoolTag<true>{});
+    else
+        tile_loop(BoolTag<false>{});
 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -376,7 +441,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         const int qr = wave * 64 + 32 * qb + n;
         if (w.nsplit == 1 && !w.rec_out) {
             const float inv = 1.f / l_tot;
-            uint16_t *O = (uint16_t *)L.o + hoff + qtok[qb] * ts;
+            uint16_t *O = (uint16_t *)L.o + hoff + (int64_t)qtok[qb] * ts;
 #pragma unroll
             for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -403,6 +468,41 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
                 }
         }
     }
+}
+
+// parts[wi * kNormParts + p]: largest |k|^2 over token range p of work wi's
+// head.  8 lanes per key row (16 bytes each), 32 rows per pass of a block,
+// four passes' loads in flight (rows past the range re-read its last row).
+__global__ __launch_bounds__(256) void key_norm_kernel(const MfmaLaunch L, float *parts) {
+    __shared__ float red[4];
+    const int wi = blockIdx.y, p = blockIdx.x, tid = threadIdx.x, seg = tid & 7;
+    const int64_t N = L.g.N, per = (N + kNormParts - 1) / kNormParts;
+    const int64_t r0 = (int64_t)p * per, r1 = min<int64_t>(N, r0 + per);
+    const uint16_t *K = (const uint16_t *)L.k + (int64_t)L.work[wi].head * L.head_stride + 8 * seg;
+    float mx = 0.f;
+    for (int64_t r = r0 + (tid >> 3); r < r1; r += 4 * 32) {
+        u32x4 raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = *(const u32x4 *)(K + min<int64_t>(r + 32 * i, r1 - 1) * L.token_stride);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float q2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = __uint_as_float(raw[i][e] << 16), hi = __uint_as_float(raw[i][e] & 0xFFFF0000u);
+                q2 = fmaf(lo, lo, fmaf(hi, hi, q2));
+            }
+            q2 += __shfl_xor(q2, 1);
+            q2 += __shfl_xor(q2, 2);
+            q2 += __shfl_xor(q2, 4);
+            mx = fmaxf(mx, q2);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 8; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    if (tid == 0) parts[wi * kNormParts + p] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // Combine key splits: one wave per query row, lane = channel.
@@ -480,6 +580,12 @@ hipError_t launch_mfma_attention(const MfmaLaunch &L, int32_t nblocks, bool shar
         const int dyn = share_cu ? share_cu_lds() : 0;
         hipLaunchKernelGGL(mfma_attn_kernel<false>, dim3(nblocks), dim3(kAttnThreads), (unsigned)dyn, stream, L);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_key_norms(const MfmaLaunch &L, float *parts, hipStream_t stream) {
+    if (L.nwork <= 0) return hipSuccess;
+    hipLaunchKernelGGL(key_norm_kernel, dim3(kNormParts, L.nwork), dim3(256), 0, stream, L, parts);
     return hipGetLastError();
 }
 

@@ -61,11 +61,19 @@ constexpr int kRecStride = 66;
 constexpr int kMaxWork = 24;
 constexpr int kQueryTile = 256;  // query rows per work-group of the matrix-core kernel
 
+// Partial maxima of |k|^2 per piece of work of a matrix-core launch (each
+// over a contiguous range of the head's tokens); the attention kernel
+// reduces them to the head's largest key norm in its prologue.
+constexpr int kNormParts = 64;
+
 struct MfmaLaunch {
     Geom g;
     const void *q, *k, *v;
     void *o;
     int64_t head_stride, token_stride;
+    // [kMaxWork][kNormParts] squared-norm maxima (launch_key_norms), or null:
+    // then every wave keeps a running maximum of its logits
+    const float *knorm;
     int32_t nwork;
     int32_t total_blocks;
     int32_t block_base;  // a launch runs blocks [block_base, block_base + grid) of the work list
@@ -93,6 +101,9 @@ struct ValuLaunch {
 // work-group per compute unit (a larger LDS allocation), so that a kernel on
 // another stream finds registers beside it on every SIMD.
 hipError_t launch_mfma_attention(const MfmaLaunch &L, int32_t nblocks, bool share_cu, hipStream_t stream);
+// parts[wi * kNormParts + p] = largest |k|^2 over the p-th token range of
+// work wi's head (bf16 K; parts holds kMaxWork * kNormParts floats)
+hipError_t launch_key_norms(const MfmaLaunch &L, float *parts, hipStream_t stream);
 hipError_t launch_split_combine(const MfmaLaunch &L, hipStream_t stream);
 hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t stream);
 // CORR_STRIDE heads (bf16): merge, for every patch row, the stride set's

@@ -129,7 +129,8 @@ typedef struct {
 typedef struct saf_ctx saf_ctx_t;
 
 /* Create a context for one geometry.  Touches no device.  *out receives the
- * context; NULL on failure.  Errors: SAF_EINVAL (bad geometry),
+ * context; NULL on failure.  Errors: SAF_EINVAL (bad geometry, or N = S (ns +
+ * P) >= 2^30),
  * SAF_EUNSUPPORTED (head_dim != 64), SAF_ENOMEM. */
 saf_status_t saf_create(const saf_geometry_t *geometry, saf_ctx_t **out);
 
@@ -289,9 +290,11 @@ saf_status_t saf_sparse_attention_noalloc(saf_ctx_t *ctx, const saf_head_plan_t 
  * pre-softmax attention matrix of Sec. 4.3, whose column means the query
  * probe reproduces; the "Full" row of Sec. 5.3, Table 6).  This is the
  * speedup baseline and the reference output of the profiling error of
- * Eq. 1 (Sec. 4.2).  Layout and dtype as for saf_sparse_attention; ws may be
- * NULL (no workspace).  Errors: SAF_EINVAL (null or misaligned pointer, bad
- * layout), SAF_EHIP. */
+ * Eq. 1 (Sec. 4.2).  Layout and dtype as for saf_sparse_attention; ws: at
+ * least saf_workspace_size(ctx, NULL) bytes, 16-byte aligned (bf16: the
+ * heads' largest key norms, which bound every logit and give the softmax a
+ * fixed shift; fp32 needs none and ws may be NULL).  Errors: SAF_EINVAL (null
+ * or misaligned pointer, bad layout, workspace too small), SAF_EHIP. */
 saf_status_t saf_dense_attention(saf_ctx_t *ctx, const void *q, const void *k, const void *v,
                                  void *o, saf_layout_t layout, void *ws, size_t ws_bytes,
                                  void *stream);

@@ -197,8 +197,12 @@ def test_context_wrapper_raises_on_error():
         saf.Context(4, 5, 256, d=32)
     assert ei.value.status == saf.SAF_EUNSUPPORTED
     ctx = saf.Context(4, 5, 256, dtype=__import__("torch").float32)
-    assert ctx.workspace_size(None) == 0
+    assert ctx.workspace_size(None) == 0  # fp32 dense: the row kernel needs none
     assert ctx.workspace_size(GOOD) > 0
+    ctx.close()
+    # bf16 dense: room for the key-norm maxima of one launch group
+    ctx = saf.Context(4, 5, 256, dtype=__import__("torch").bfloat16)
+    assert ctx.workspace_size(None) >= 24 * 64 * 4
     with pytest.raises(saf.SafError):
         ctx.workspace_size([(9, 0, 0, 0)] * 16)
     ctx.close()
