@@ -65,9 +65,9 @@ constexpr int PSTRIDE = kRecStride;  // split partial record: m, l, o[64]
 constexpr float kShiftBoundMax = 56.f;  // log2 units
 constexpr float kShiftHeadroom = 32.f;
 
-template <bool B>
-struct BoolTag {
-    static constexpr bool value = B;
+template <int M>
+struct IntTag {
+    static constexpr int value = M;
 };
 
 __device__ __forceinline__ int kswz(int row) { return 4 * ((row >> 3) & 1); }
@@ -215,7 +215,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     // file); lanes n and n + 32 hold the two channel halves of a query
     bool fixed = false;
     if (L.knorm) {
-        float k2 = L.knorm[wi * kNormParts + lane];
+        static_assert(kNormParts % 64 == 0, "whole partials per lane");
+        float k2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < kNormParts / 64; ++i) k2 = fmaxf(k2, L.knorm[wi * kNormParts + 64 * i + lane]);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, off));
         float bmax = 0.f, bq[2];
@@ -323,18 +326,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt at their maxima
     __syncthreads();
 
-    auto tile_loop = [&](auto fixed_tag) {
-    constexpr bool FIXED = decltype(fixed_tag)::value;
-    for (int32_t t = 0; t < ntiles; ++t) {
+    // One key tile.  MODE 0: fixed shift, every slot a key (pipelined);
+    // 1: fixed shift, masked slots; 2: running maximum.
+    auto tile_step = [&](int32_t t, auto mode_tag) {
+        constexpr int MODE = decltype(mode_tag)::value;
+        constexpr bool FIXED = MODE != 2;
         const int buf = t & 1;
         const int32_t kt = kbeg + t * KT;
         if (t + 1 < ntiles) load_tile(kt + KT);
 
-        // S^T = K Q^T: two 32-key blocks x two 32-query blocks; each K
-        // fragment feeds both query blocks
+        // S^T = K Q^T for one 32-key block (bb) and both 32-query blocks;
+        // each K fragment feeds both query blocks
         f32x16 s[2][2];
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
+        auto s_block = [&](int bb) {
             const uint16_t *krow = &Ks[buf][(32 * bb + swap_bits23(n)) * KROW];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -344,58 +348,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
                     s[bb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][c], c ? s[bb][qb] : f32x16{}, 0,
                                                                         0, 0);
             }
-        }
-        // masked slots: ragged tail, or specials already on the scanning stride
-        if (kt + KT > kend || kt + KT > first_masked) {
+        };
+        // weights of one key block with the fixed shift
+        auto weights = [&](int bb) {
 #pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
+            for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float bias = kbias[buf][32 * bb + 16 * (r >> 3) + 8 * gq + (r & 7)];
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) s[bb][qb][r] += bias;
-                }
-        }
-        // softmax weights per query block (log2 domain).  Fixed shift: the
-        // bound-derived m_q.  Otherwise an online running max, only raised
-        // when a logit exceeds it by more than 8 (weights stay <= 2^8), so
-        // the O rescale is skipped on most tiles.
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            if (FIXED) {
-#pragma unroll
-                for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[bb][qb][r] = fast_exp2(fmaf(s[bb][qb][r], sc, -m_run[qb]));
-                continue;
-            }
-            float mx = s[0][qb][0];
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][qb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
-            if (__any(mx > m_run[qb] + 8.f)) {
-                const float m_new = fmaxf(m_run[qb], mx);
-                const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
-                l_run[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < 2; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-                m_run[qb] = m_new;
-            }
-            const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[bb][qb][r] = fast_exp2(fmaf(s[bb][qb][r], sc, -m_use));
-        }
-
-        // O^T += V^T P^T, four k-steps of 16 keys; each V^T fragment feeds
+                for (int r = 0; r < 16; ++r) s[bb][qb][r] = fast_exp2(fmaf(s[bb][qb][r], sc, -m_run[qb]));
+        };
+        // O^T += V^T P^T for the 16 keys 16 e ..; each V^T fragment feeds
         // both query blocks
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        auto pv = [&](int e) {
             const int bb = e >> 1, h8 = (e & 1) * 8;
             bf16x8 pb[2];
 #pragma unroll
@@ -423,16 +386,106 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
                 for (int qb = 0; qb < 2; ++qb)
                     oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
             }
+        };
+        if (MODE == 0) {
+            // Fixed shift, every slot a key: the weights of one key block need
+            // only that block's logits, so each wave issues the matrix-core
+            // work of one block beside the vector work of the other:
+            //   S(keys 0-31) | S(keys 32-63) + weights(0-31)
+            //   | P.V(0-31) + weights(32-63) | P.V(32-63)
+            s_block(0);
+            __builtin_amdgcn_sched_barrier(0);
+            s_block(1);
+            weights(0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);  // the block's K fragments
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            pv(0);
+            pv(1);
+            weights(1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);  // V^T fragments of keys 0-31
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 2);  // packed weights of keys 0-15
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+                __builtin_amdgcn_sched_group_barrier(0x002, 11, 2);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            pv(2);
+            pv(3);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 3);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 3);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 3);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            s_block(0);
+            s_block(1);
+            // masked slots: ragged tail, or specials already on the scanning stride
+            if (kt + KT > kend || kt + KT > first_masked) {
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float bias = kbias[buf][32 * bb + 16 * (r >> 3) + 8 * gq + (r & 7)];
+#pragma unroll
+                        for (int qb = 0; qb < 2; ++qb) s[bb][qb][r] += bias;
+                    }
+            }
+            if (FIXED) {
+                weights(0);
+                weights(1);
+            } else {
+                // online running max per query block (log2 domain), only
+                // raised when a logit exceeds it by more than 8 (weights stay
+                // <= 2^8), so the O rescale is skipped on most tiles
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    float mx = s[0][qb][0];
+#pragma unroll
+                    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][qb][r]);
+                    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sc;
+                    if (__any(mx > m_run[qb] + 8.f)) {
+                        const float m_new = fmaxf(m_run[qb], mx);
+                        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[qb] - m_new);
+                        l_run[qb] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < 2; ++db)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+                        m_run[qb] = m_new;
+                    }
+                    const float m_use = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+#pragma unroll
+                    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) s[bb][qb][r] = fast_exp2(fmaf(s[bb][qb][r], sc, -m_use));
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pv(e);
         }
 
         if (t + 1 < ntiles) store_tile(buf ^ 1, kt + 2 * KT <= kend);
         __syncthreads();
-    }
     };
-    if (fixed)
-        tile_loop(BoolTag<true>{});
-    else
-        tile_loop(BoolTag<false>{});
+    if (fixed) {
+        // tiles [0, t_full) hold no masked slot
+        const int32_t t_full = max(0, min(ntiles, (min(kend, first_masked) - kbeg) / KT));
+        for (int32_t t = 0; t < t_full; ++t) tile_step(t, IntTag<0>{});
+        for (int32_t t = t_full; t < ntiles; ++t) tile_step(t, IntTag<1>{});
+    } else {
+        for (int32_t t = 0; t < ntiles; ++t) tile_step(t, IntTag<2>{});
+    }
 
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {

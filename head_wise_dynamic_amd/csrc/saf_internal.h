@@ -64,7 +64,7 @@ constexpr int kQueryTile = 256;  // query rows per work-group of the matrix-core
 // Partial maxima of |k|^2 per piece of work of a matrix-core launch (each
 // over a contiguous range of the head's tokens); the attention kernel
 // reduces them to the head's largest key norm in its prologue.
-constexpr int kNormParts = 64;
+constexpr int kNormParts = 256;
 
 struct MfmaLaunch {
     Geom g;
