@@ -54,24 +54,24 @@ COUNTERS = {
     "groups": {
         "cosine_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
-            "executed_tflop": 20.034, "mfma_busy": 0.4355,
-            "fetch_kib": 38577781.0, "write_kib": 2037077.0},
+            "executed_tflop": 20.034, "mfma_busy": 0.4397,
+            "fetch_kib": 38539649.2, "write_kib": 2036257.8},
         "per_frame_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
-            "executed_tflop": 22.8345, "mfma_busy": 0.3471,
-            "fetch_kib": 40230639.7, "write_kib": 6027339.8},
+            "executed_tflop": 22.8345, "mfma_busy": 0.3512,
+            "fetch_kib": 40237933.9, "write_kib": 6027210.3},
         "shared_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "b0d13da183fa6e0033f35f3c2e0d652437d2e3d7e876fe12f56a21dc64315ef6",
-            "executed_tflop": 2.7005, "mfma_busy": 0.2485,
-            "fetch_kib": 810963.9, "write_kib": 230489.9},
+            "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
+            "executed_tflop": 2.7005, "mfma_busy": 0.2954,
+            "fetch_kib": 809953.3, "write_kib": 230490.6},
         "dense": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "b0d13da183fa6e0033f35f3c2e0d652437d2e3d7e876fe12f56a21dc64315ef6",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4242,
-            "fetch_kib": 6821681.2, "write_kib": 274800.0},
+            "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
+            "executed_tflop": 77.3724, "mfma_busy": 0.4971,
+            "fetch_kib": 28643557.2, "write_kib": 274800.0},
         "gather_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_valu.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "9bc2aace1a211723f2327c911c196c838e58a00bf2b0b14c673b37e487e38323",
+            "sha256": "081001d50c59b24c5e443f0a8e1374ff6a26976e921801fb5234983fe01c9db3",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12610208.6, "write_kib": 51337.5},
+            "fetch_kib": 12613045.7, "write_kib": 51337.5},
     },
 }
 
