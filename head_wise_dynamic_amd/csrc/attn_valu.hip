@@ -298,9 +298,13 @@ __device__ __forceinline__ float max_groups(float x) {
 // afterwards), so a chunk costs one memory round trip for all NH heads.  The
 // softmax of each head runs online over the chunks; lanes of one 8-lane
 // group hold one key row, 16 bytes each.
+constexpr int kIdxRun = 256;  // index entries staged in LDS per wave at a time
+
 template <int NH, int NP>
-__device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u, int64_t tok, int lane) {
+__device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u, int64_t tok, int lane,
+                             int32_t *sidx) {
     constexpr int RPP = 8, CH = NP * RPP;
+    static_assert(kIdxRun % CH == 0 && kIdxRun % 64 == 0, "chunks within one staged run");
     const int sub = lane & 7, grp = lane >> 3;
     const int64_t ts = L.token_stride;
     const float sc = kLog2e * 0.125f;
@@ -320,15 +324,27 @@ __device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u,
         skip[h] = hw[h].rec_out ? hw[h].budget : 0;
     }
     const int32_t *idx = L.corr_idx + u * L.corr_k;
-    const int64_t count = L.corr_k;
-    for (int64_t c0 = 0; c0 < count; c0 += CH) {
+    const int32_t count = L.corr_k;
+    for (int32_t c0 = 0; c0 < count; c0 += CH) {
+        // the row's index entries reach LDS kIdxRun at a time, read by the
+        // whole wave at once (coalesced), so that each chunk waits for one
+        // memory round trip (its K and V rows), not two; a wave reads back
+        // only what it wrote itself (in order: no barrier)
+        const int32_t run0 = c0 / kIdxRun * kIdxRun;
+        if (c0 == run0) {
+            int32_t e[kIdxRun / 64];
+#pragma unroll
+            for (int j = 0; j < kIdxRun / 64; ++j) e[j] = idx[min(run0 + lane + 64 * j, count - 1)];
+#pragma unroll
+            for (int j = 0; j < kIdxRun / 64; ++j) sidx[lane + 64 * j] = e[j];
+        }
         int32_t t[NP];
         bool in[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int64_t mi = c0 + p * RPP + grp;
+            const int32_t mi = c0 + p * RPP + grp;
             in[p] = mi < count;
-            t[p] = idx[in[p] ? mi : count - 1];
+            t[p] = sidx[(in[p] ? mi : count - 1) - run0];
         }
         u32x4 kr[NH][NP], vr[NH][NP];
 #pragma unroll
@@ -413,14 +429,16 @@ __global__ __launch_bounds__(256) void gather_attn_kernel(const ValuLaunch L) {
     const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (u >= g.Np) return;
     const int64_t tok = (u / g.P) * g.T + g.ns + (u % g.P);
+    __shared__ int32_t sidx[4][kIdxRun];
+    int32_t *my = sidx[threadIdx.x >> 6];
     for (int i0 = 0; i0 < L.nwork; i0 += kGatherGroup) {
         const int nh = min(kGatherGroup, L.nwork - i0);
         if (nh == 3)
-            gather_group<3, kGatherNP>(L, L.work + i0, u, tok, lane);
+            gather_group<3, kGatherNP>(L, L.work + i0, u, tok, lane, my);
         else if (nh == 2)
-            gather_group<2, kGatherNP>(L, L.work + i0, u, tok, lane);
+            gather_group<2, kGatherNP>(L, L.work + i0, u, tok, lane, my);
         else
-            gather_group<1, kGatherNP>(L, L.work + i0, u, tok, lane);
+            gather_group<1, kGatherNP>(L, L.work + i0, u, tok, lane, my);
     }
 }
 
