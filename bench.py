@@ -39,7 +39,9 @@ PEAK_BF16_TFLOPS = 2500.0
 # (rocprofv3 --pmc, one pass per group of counters; per step: the index
 # build's cosine GEMM is 1 seed-bound + 1 symmetric launch, the fused
 # per-frame build's GEMM 1 sampled + 1 filtered symmetric launch, the
-# shared-key attention two launches, the others one).  executed_tflop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+# shared-key attention its launch(es) of one layer, the others one;
+# shared_attention_alone: the 13 shared-key heads on their own, no gather
+# beside them, full occupancy).  executed_tflop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
 # FLOP; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x
 # 1024 SIMDs), the share of SIMD cycles the matrix cores were busy while the
 # kernel ran; fetch/write = FETCH_SIZE / WRITE_SIZE in KiB, scaled by what
@@ -54,24 +56,28 @@ COUNTERS = {
     "groups": {
         "cosine_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
-            "executed_tflop": 20.034, "mfma_busy": 0.4397,
-            "fetch_kib": 38539649.2, "write_kib": 2036257.8},
+            "executed_tflop": 20.034, "mfma_busy": 0.4359,
+            "fetch_kib": 38541080.9, "write_kib": 2031553.4},
         "per_frame_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
-            "executed_tflop": 22.8345, "mfma_busy": 0.3512,
-            "fetch_kib": 40237933.9, "write_kib": 6027210.3},
+            "executed_tflop": 22.8345, "mfma_busy": 0.3484,
+            "fetch_kib": 40171927.8, "write_kib": 6030272.9},
         "shared_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
             "executed_tflop": 2.7005, "mfma_busy": 0.2954,
-            "fetch_kib": 809953.3, "write_kib": 230490.6},
+            "fetch_kib": 811802.1, "write_kib": 230481.0},
+        "shared_attention_alone": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
+            "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
+            "executed_tflop": 2.6465, "mfma_busy": 0.4334,
+            "fetch_kib": 698971.8, "write_kib": 223275.6},
         "dense": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4971,
-            "fetch_kib": 28643557.2, "write_kib": 274800.0},
+            "executed_tflop": 77.3724, "mfma_busy": 0.4951,
+            "fetch_kib": 30115731.9, "write_kib": 274800.0},
         "gather_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_valu.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "081001d50c59b24c5e443f0a8e1374ff6a26976e921801fb5234983fe01c9db3",
+            "sha256": "934ddfc41ecf959febe656a481bb345e324c89a228d216aef9e64da292b75669",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12613045.7, "write_kib": 51337.5},
+            "fetch_kib": 12599155.5, "write_kib": 51337.5},
     },
 }
 
@@ -642,6 +648,10 @@ def main():
         for n in ("gather_attention", "shared_attention"):
             if n in others:
                 others[n]["alone"] = {k: v for k, v in alone.items() if k.startswith(n)}
+        if "shared_attention" in others:
+            # full occupancy, no gather beside it
+            others["shared_attention"]["alone"]["counters"] = counter_view("shared_attention_alone",
+                                                                            alone["shared_attention_ms"])
     if dense_ms:
         others["dense"] = {"achieved": round(4.0 * d * g.H * g.N * g.N / (dense_ms * 1e-3) / 1e12, 2),
                            "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS,
