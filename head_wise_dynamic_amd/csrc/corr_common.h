@@ -70,6 +70,7 @@ struct Args {
     int32_t guess_k;         // compaction: also set theta_g from the guess_k-th best (0: no); bound_rows:
                              // theta_g from the guess_k-th largest lane maximum (0: no)
     int32_t guess_k_seed;    // bound_rows: that rank for rows of the two seed frames (one frame fewer seen)
+    int32_t filter_guess;    // FILTER: keep scores >= theta_g (the direct pass of two operands), not theta
     int32_t raw_dot;         // scores are plain dot products (unit "norms")
     const void *Fc;          // column operand (== F for the symmetric cosine)
     int32_t tok_map;         // row u of F / Fc is token (u / P) T + ns + u % P (patches of a token layout)

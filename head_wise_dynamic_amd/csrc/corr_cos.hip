@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kCosThreads, 1) void cos_phase(const Args A) {
                     t0 = A.pthr[(int64_t)f_col_lo * g.Np + uc];
                     t1 = A.pthr[(int64_t)f_col_hi * g.Np + uc];
                 } else {
-                    t0 = MODE == SYM ? A.s.theta_g[uc] : A.s.theta[uc];
+                    t0 = (MODE == SYM || (MODE == FILTER && A.filter_guess)) ? A.s.theta_g[uc] : A.s.theta[uc];
                 }
                 float th0 = INFINITY, th1 = INFINITY, iu = __builtin_nanf("");  // NaN: no comparison passes
                 int32_t fr = -1;

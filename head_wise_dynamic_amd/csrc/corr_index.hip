@@ -17,7 +17,9 @@
 // every row a guess theta_g_u of its K-th best, their r-th largest with r
 // the guess rank over the seed columns of other frames; the whole square
 // [0, Np)^2 is then filtered by it once per unordered pair, compacted, and
-// finalized with the guess check of 4./5.  Otherwise:
+// finalized with the guess check of 4./5.  With two operands (a head's
+// logits q_u . k_v: no symmetry), the same guess filters one pass over every
+// (row, column) pair instead.  Otherwise:
 //   1. seed: columns of frames 0 and 1.  When 4 K + 128 <= P, only each
 //      lane's largest cosine over its 4 seed columns of other frames is
 //      kept, and a row's K-th largest such value (reached by K distinct
@@ -1089,9 +1091,13 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
     // (no filtered column phases, no compaction between them).  The seed
     // frames hold on average K 2P / ((S-1) P) of a row's K best; below 5 the
     // guess fails too often (each failure is a recomputed row).
-    const bool direct = bound_seed && A.Fc == A.F && (int64_t)B.K * seed_cols >= 5ll * (B.g.S - 1) * B.g.P;
-    // the symmetric square needs one operand for rows and columns
-    A.sym_lo = direct ? 0 : (A.Fc == A.F) ? corr_sym_start(B.g) : Np;
+    const bool guess_ok = bound_seed && (int64_t)B.K * seed_cols >= 5ll * (B.g.S - 1) * B.g.P;
+    const bool direct = guess_ok && A.Fc == A.F;
+    // two operands: one filtered pass over [0, Np) x [0, Np) with the guess
+    const bool direct_rect = guess_ok && A.Fc != A.F;
+    // the symmetric square needs one operand for rows and columns; with a
+    // direct pass every row's guess is checked when it is finalized
+    A.sym_lo = (direct || direct_rect) ? 0 : (A.Fc == A.F) ? corr_sym_start(B.g) : Np;
     const unsigned rb = (unsigned)((Np + 3) / 4);
     if (B.dino_dtype == BF16)
         hipLaunchKernelGGL(init_rows<uint16_t>, dim3(rb), dim3(256), 0, stream, A);
@@ -1126,7 +1132,36 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
             A.guess_k = 0;
         };
         int64_t lo0 = seed_cols;
-        if (direct) {
+        auto bound_and_guess = [&]() {
+            // the seed frames' lane maxima: a lower bound (theta) and a guess
+            // (theta_g) of every row's K-th best; the guess rank is
+            // corr_guess_rank's over the seed columns of other frames
+            A.row_lo = 0;
+            A.row_hi = Np;
+            A.col_lo = 0;
+            A.col_hi = seed_cols;
+            A.lm_per_row = (int32_t)((seed_cols + CT - 1) / CT * 64);
+            const int64_t tiles = ((Np + CT - 1) / CT) * ((seed_cols + CT - 1) / CT);
+            if (B.mark) B.mark(B.mark_user, 1, "cosine_gemm", stream);
+            launch_cos<TBOUND>(dim3((unsigned)(8 * ((tiles + 7) / 8))), stream, A);
+            if (B.mark) B.mark(B.mark_user, 0, "cosine_gemm", stream);
+            A.guess_k = corr_guess_rank(B.g, B.K, seed_cols);
+            A.guess_k_seed = corr_guess_rank(B.g, B.K, seed_cols - B.g.P);
+            if (A.lm_per_row <= 16 * 64)
+                hipLaunchKernelGGL(bound_rows<16>, dim3(cb), dim3(256), 0, stream, A);
+            else
+                hipLaunchKernelGGL(bound_rows<32>, dim3(cb), dim3(256), 0, stream, A);
+            A.guess_k = A.guess_k_seed = 0;
+        };
+        if (direct_rect) {
+            // 1. bound and guess from the seed frames; 2. every pair once,
+            // filtered by the guess; then compaction, finalize and its check
+            bound_and_guess();
+            A.filter_guess = 1;
+            rect(FILTER, 0, Np, 0, Np);
+            A.filter_guess = 0;
+            lo0 = Np;
+        } else if (direct) {
             // 1. the seed frames' lane maxima: a lower bound (theta) and a
             // guess (theta_g) of every row's K-th best; the guess rank is
             // corr_guess_rank's over the seed columns of other frames
@@ -1182,7 +1217,7 @@ hipError_t launch_corr_build(const CorrBuild &B, hipStream_t stream) {
         // 2. doubling filtered phases for every row up to W
         for (int64_t lo = lo0; !direct && lo < W; lo = std::min<int64_t>(2 * lo, W))
             rect(FILTER, 0, Np, lo, std::min<int64_t>(2 * lo, W));
-        if (!direct && W < Np) {
+        if (!direct && !direct_rect && W < Np) {
             // 3. rows below W keep doubling over the remaining columns
             for (int64_t lo = W; lo < Np; lo = std::min<int64_t>(2 * lo, Np))
                 rect(FILTER, 0, W, lo, std::min<int64_t>(2 * lo, Np));
