@@ -55,29 +55,29 @@ COUNTERS = {
     "write_scale": 1.0,
     "groups": {
         "cosine_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
-            "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
-            "executed_tflop": 20.034, "mfma_busy": 0.4359,
-            "fetch_kib": 38541080.9, "write_kib": 2031553.4},
+            "sha256": "bddb6f37cfe3da0e81df60bc8b8afe971104fa7b5dd0fcbca6c6f787b96d5421",
+            "executed_tflop": 20.034, "mfma_busy": 0.4387,
+            "fetch_kib": 38525553.1, "write_kib": 2033150.0},
         "per_frame_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
-            "sha256": "0c6590fe014f48efd063dd90c39a63567a9d06bbbf0388ee9cb1fb77b9cae8f9",
-            "executed_tflop": 22.8345, "mfma_busy": 0.3484,
-            "fetch_kib": 40171927.8, "write_kib": 6030272.9},
+            "sha256": "bddb6f37cfe3da0e81df60bc8b8afe971104fa7b5dd0fcbca6c6f787b96d5421",
+            "executed_tflop": 22.8345, "mfma_busy": 0.349,
+            "fetch_kib": 40186736.2, "write_kib": 6027702.6},
         "shared_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
-            "executed_tflop": 2.7005, "mfma_busy": 0.2954,
-            "fetch_kib": 811802.1, "write_kib": 230481.0},
+            "executed_tflop": 2.7005, "mfma_busy": 0.2965,
+            "fetch_kib": 811392.9, "write_kib": 230480.8},
         "shared_attention_alone": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
-            "executed_tflop": 2.6465, "mfma_busy": 0.4334,
-            "fetch_kib": 698971.8, "write_kib": 223275.6},
+            "executed_tflop": 2.6465, "mfma_busy": 0.4383,
+            "fetch_kib": 698840.3, "write_kib": 223277.2},
         "dense": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4951,
-            "fetch_kib": 30115731.9, "write_kib": 274800.0},
+            "executed_tflop": 77.3724, "mfma_busy": 0.4919,
+            "fetch_kib": 26327779.8, "write_kib": 274800.0},
         "gather_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_valu.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "934ddfc41ecf959febe656a481bb345e324c89a228d216aef9e64da292b75669",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12599155.5, "write_kib": 51337.5},
+            "fetch_kib": 12593181.2, "write_kib": 51337.5},
     },
 }
 
