@@ -43,6 +43,7 @@ def _ctx(S=4, ns=5, P=256, H=16, dtype=saf.SAF_BF16):
     ((4, 5, 256, 16, 64, 7), saf.SAF_EINVAL),
     ((4, 5, 256, 16, 32, 1), saf.SAF_EUNSUPPORTED),
     ((100000, 5, 30000, 16, 64, 1), saf.SAF_EINVAL),
+    ((1 << 20, 0, 1 << 10, 16, 64, 1), saf.SAF_EINVAL),   # N = 2^30: key-slot counts must stay below 2^31
 ])
 def test_create_rejects_bad_geometry(geom, code):
     c = C.c_void_p()
@@ -206,3 +207,31 @@ def test_context_wrapper_raises_on_error():
     with pytest.raises(saf.SafError):
         ctx.workspace_size([(9, 0, 0, 0)] * 16)
     ctx.close()
+
+
+def test_create_accepts_n_just_below_the_limit():
+    c = C.c_void_p()
+    assert saf.saf_create(saf.saf_geometry_t((1 << 20) - 1, 0, 1 << 10, 16, 64, 1), c) == saf.SAF_OK
+    saf.saf_destroy(c)
+
+
+def test_dense_attention_needs_workspace_for_bf16():
+    """bf16 dense: the key-norm maxima live in the workspace (no device touched
+    before the check)."""
+    c = _ctx()
+    try:
+        need = C.c_size_t()
+        assert saf.saf_workspace_size(c, None, need) == saf.SAF_OK and need.value > 0
+        f = saf.saf_dense_attention
+        assert f(c, FAKE, FAKE, FAKE, FAKE, LAY, None, 0, None) == saf.SAF_EINVAL
+        assert "workspace" in saf.saf_last_error(c)
+        assert f(c, FAKE, FAKE, FAKE, FAKE, LAY, FAKE, need.value - 1, None) == saf.SAF_EINVAL
+        assert f(c, FAKE, FAKE, FAKE, FAKE, LAY, FAKE + 8, need.value, None) == saf.SAF_EINVAL  # misaligned
+    finally:
+        saf.saf_destroy(c)
+    c = _ctx(dtype=saf.SAF_F32)
+    try:
+        need = C.c_size_t()
+        assert saf.saf_workspace_size(c, None, need) == saf.SAF_OK and need.value == 0
+    finally:
+        saf.saf_destroy(c)
