@@ -300,6 +300,18 @@ __device__ __forceinline__ float max_groups(float x) {
 // group hold one key row, 16 bytes each.
 constexpr int kIdxRun = 256;  // index entries staged in LDS per wave at a time
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// q . k over a lane's 8 channels: four v_dot2 on the packed bf16 pairs (the
+// products are exact in fp32), one call per 32-bit word
+__device__ __forceinline__ float dot2_word(uint32_t q, uint32_t k, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q), __builtin_bit_cast(bf16x2, k), acc, false);
+}
+__device__ __forceinline__ float dot8_bf16(u32x4 q, u32x4 k) {
+    const uint32_t q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
+    const uint32_t k0 = k.x, k1 = k.y, k2 = k.z, k3 = k.w;
+    return dot2_word(q3, k3, dot2_word(q2, k2, dot2_word(q1, k1, dot2_word(q0, k0, 0.f))));
+}
+
 template <int NH, int NP>
 __device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u, int64_t tok, int lane,
                              int32_t *sidx) {
@@ -309,14 +321,15 @@ __device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u,
     const int64_t ts = L.token_stride;
     const float sc = kLog2e * 0.125f;
     const uint16_t *Kh[NH], *Vh[NH];
-    float q[NH][8], o[NH][8], m[NH], l[NH];
+    u32x4 q[NH];
+    float o[NH][8], m[NH], l[NH];
     int32_t skip[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
         const int64_t hoff = (int64_t)hw[h].head * L.head_stride + sub * 8;
         Kh[h] = (const uint16_t *)L.k + hoff;
         Vh[h] = (const uint16_t *)L.v + hoff;
-        Lanes<uint16_t>::load((const uint16_t *)L.q + hoff + tok * ts, q[h]);
+        q[h] = *(const u32x4 *)((const uint16_t *)L.q + hoff + tok * ts);
         m[h] = -INFINITY;
         l[h] = 0.f;
 #pragma unroll
@@ -360,12 +373,7 @@ __device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u,
             float s[NP], cm = -INFINITY;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                float kx[8];
-                Lanes<uint16_t>::unpack_raw(kr[h][p], kx);
-                float dot = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dot = fmaf(q[h][e], kx[e], dot);
-                dot = sum8(dot);
+                const float dot = sum8(dot8_bf16(q[h], kr[h][p]));
                 const bool ok = in[p] && !(skip[h] > 0 && t[p] % skip[h] == 0);
                 s[p] = ok ? dot * sc : -INFINITY;
                 cm = fmaxf(cm, s[p]);

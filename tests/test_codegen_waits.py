@@ -75,3 +75,18 @@ def test_shared_key_kernel_mfma_never_waits_for_all_loads(tmp_path):
         assert len(mfma) >= 32
         waited = [i for i in mfma if ins[i - 1].startswith("s_waitcnt") and "vmcnt(0)" in ins[i - 1]]
         assert not waited, [ins[i - 1] for i in waited]
+
+
+def test_bf16_dot2_reads_every_word_of_a_pack(tmp_path):
+    """Each v_dot2 of a packed 8-channel product reads its own 32-bit word.
+    When the four words of a 128-bit vector were bit-cast element by element,
+    this compiler emitted all four dot2 on the first word (wrong sums with no
+    error); the kernels extract the words first.  The gather kernel's q . k
+    takes four dot2 per key row, dot2s that read the same registers as the
+    one before would be that defect."""
+    fns = _functions(_assembly("attn_valu.hip", tmp_path))
+    ins = [v for k, v in fns.items() if "gather_attn_kernel" in k][0]
+    dots = [re.split(r"[\s,]+", t)[1:4] for t in ins if t.startswith("v_dot2")]
+    assert len(dots) >= 48, len(dots)
+    repeats = [(a, b) for a, b in zip(dots, dots[1:]) if a[0] == b[0] and a[1:] == b[1:]]
+    assert not repeats, repeats[:4]
