@@ -382,11 +382,16 @@ __device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u,
             if (cm == -INFINITY) continue;  // wave-uniform: every slot masked
             const float m_new = fmaxf(m[h], cm);
             const float alpha = fast_exp2(m[h] - m_new);
+            // weights rounded to bf16 once; the sum and P.V take the same
+            // rounded values (an exact convex combination of V rows under
+            // them), P.V as two dot2 per channel pair against (p, 0) and
+            // (0, p).  Masked slots weigh 0 and read a listed (finite) row.
+            uint32_t pw[NP];
             float lsum = 0.f;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                s[p] = fast_exp2(s[p] - m_new);
-                lsum += s[p];
+                pw[p] = pack_bf16x2(fast_exp2(s[p] - m_new), 0.f);
+                lsum += __uint_as_float(pw[p] << 16);
             }
             l[h] = l[h] * alpha + lsum;
             m[h] = m_new;
@@ -394,11 +399,17 @@ __device__ void gather_group(const ValuLaunch &L, const HeadWork *hw, int64_t u,
             for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                float vx[8];
-                Lanes<uint16_t>::unpack_raw(vr[h][p], vx);
-                const bool ok = s[p] > 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[h][e] = ok ? fmaf(s[p], vx[e], o[h][e]) : o[h][e];
+                const uint32_t plo = pw[p], phi = pw[p] << 16;
+                const u32x4 vv = vr[h][p];
+                const uint32_t v0 = vv.x, v1 = vv.y, v2 = vv.z, v3 = vv.w;
+                o[h][0] = dot2_word(v0, plo, o[h][0]);
+                o[h][1] = dot2_word(v0, phi, o[h][1]);
+                o[h][2] = dot2_word(v1, plo, o[h][2]);
+                o[h][3] = dot2_word(v1, phi, o[h][3]);
+                o[h][4] = dot2_word(v2, plo, o[h][4]);
+                o[h][5] = dot2_word(v2, phi, o[h][5]);
+                o[h][6] = dot2_word(v3, plo, o[h][6]);
+                o[h][7] = dot2_word(v3, phi, o[h][7]);
             }
         }
     }
