@@ -56,28 +56,28 @@ COUNTERS = {
     "groups": {
         "cosine_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "bddb6f37cfe3da0e81df60bc8b8afe971104fa7b5dd0fcbca6c6f787b96d5421",
-            "executed_tflop": 20.034, "mfma_busy": 0.4387,
-            "fetch_kib": 38525553.1, "write_kib": 2033150.0},
+            "executed_tflop": 20.034, "mfma_busy": 0.4376,
+            "fetch_kib": 38536054.0, "write_kib": 2032181.4},
         "per_frame_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "bddb6f37cfe3da0e81df60bc8b8afe971104fa7b5dd0fcbca6c6f787b96d5421",
-            "executed_tflop": 22.8345, "mfma_busy": 0.349,
-            "fetch_kib": 40186736.2, "write_kib": 6027702.6},
+            "executed_tflop": 22.8345, "mfma_busy": 0.3495,
+            "fetch_kib": 40220987.9, "write_kib": 6031418.3},
         "shared_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
-            "executed_tflop": 2.7005, "mfma_busy": 0.2965,
-            "fetch_kib": 811392.9, "write_kib": 230480.8},
+            "executed_tflop": 2.7005, "mfma_busy": 0.2947,
+            "fetch_kib": 811629.3, "write_kib": 230480.7},
         "shared_attention_alone": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
-            "executed_tflop": 2.6465, "mfma_busy": 0.4383,
-            "fetch_kib": 698840.3, "write_kib": 223277.2},
+            "executed_tflop": 2.6465, "mfma_busy": 0.4365,
+            "fetch_kib": 698808.8, "write_kib": 223275.1},
         "dense": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "f673892d4439a6a979578f513b7bf4d9f776dd65fa48ce7a3535f993a74d4088",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4919,
-            "fetch_kib": 26327779.8, "write_kib": 274800.0},
+            "executed_tflop": 77.3724, "mfma_busy": 0.4982,
+            "fetch_kib": 30023941.3, "write_kib": 274800.0},
         "gather_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_valu.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "934ddfc41ecf959febe656a481bb345e324c89a228d216aef9e64da292b75669",
+            "sha256": "4e72520c965dbe28b4901cab90e9cc3de65aa9fb7cf0e5ecaba16cc730c799b2",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12593181.2, "write_kib": 51337.5},
+            "fetch_kib": 12557703.6, "write_kib": 51337.5},
     },
 }
 
