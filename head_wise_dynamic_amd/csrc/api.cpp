@@ -937,10 +937,12 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
     // SIMD's registers, and the gather's waves would wait for them to
     // finish.  About as many blocks as finish while the gather runs: its
     // K/V row bytes and the blocks' logit FLOP at the rates the two kernels
-    // reach side by side on MI355X (S = 100: ~5 TB/s and ~0.9 PFLOP/s;
-    // measured, the layer time stays within 1 % from 0.6x to 1.5x this many
-    // blocks, is 1.5 % longer at half of them and 15 % longer at none).
-    constexpr double kShareGatherBytesPerMs = 5.0e9, kShareMfmaFlopPerMs = 0.9e12;
+    // reach side by side on MI355X (~5 TB/s and ~0.72 PFLOP/s, the values
+    // that time best: at S = 100 every block shares and the layer is flat
+    // from half to all of them; at S = 500, 0.8x this many blocks is 2 %
+    // faster than 1.25x and 4 % faster than 0.5x, where the gather is left
+    // to finish behind full-occupancy blocks).
+    constexpr double kShareGatherBytesPerMs = 5.0e9, kShareMfmaFlopPerMs = 0.72e12;
     double share_ms = 0.0;
     if (forked) {
         double gather_bytes = 0.0;
