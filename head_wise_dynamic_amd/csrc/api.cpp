@@ -172,8 +172,26 @@ struct PlanInfo {
     int64_t split_ws = 0;     // bytes for dense-row split partials
     int64_t union_ws = 0;     // bytes for the records of correspondence + stride heads
     int64_t norm_ws = 0;      // bytes for the key-norm maxima of the matrix-core launches
+    int64_t pack_ws = 0;      // bytes for the packed key sets of the scanning heads
     int corr_splits = 1;
 };
+
+// Rows of a scanning head's packed key set: the stride tokens, then the
+// specials off the stride; 0 when the set is not packed (fp32, or more
+// specials than the packing kernel holds).
+int64_t scan_pack_rows(const saf::Geom &g, int32_t stride) {
+    if (g.dtype != saf::BF16 || stride < 1 || (int64_t)g.ns * g.S > saf::kPackSpecials) return 0;
+    int64_t on = 0;
+    for (int64_t f = 0; f < g.S; ++f)
+        for (int64_t t = 0; t < g.ns; ++t) on += ((f * g.T + t) % stride == 0);
+    return (g.N + stride - 1) / stride + (int64_t)g.ns * g.S - on;
+}
+int64_t scan_pack_bytes(const saf::Geom &g, int32_t stride) {
+    const int64_t rows = scan_pack_rows(g, stride);
+    if (rows == 0) return 0;
+    return 2 * (int64_t)align256(sizeof(uint16_t) * 64 * (size_t)rows) +
+           (int64_t)align256(sizeof(int32_t) * (size_t)g.ns * g.S + 4);
+}
 
 // key-norm maxima of one matrix-core launch group (bf16 contexts)
 int64_t norm_bytes(const saf::Geom &g) {
@@ -254,6 +272,8 @@ saf_status_t check_plan(saf_ctx_t *c, const saf_head_plan_t *plan, PlanInfo *pi)
         pi->union_ws = (int64_t)pi->nunion * union_rec_bytes(g);
     }
     pi->norm_ws = norm_bytes(g);
+    for (int h = 0; h < g.H; ++h)
+        if (plan[h].role == SAF_SCANNING) pi->pack_ws += scan_pack_bytes(g, plan[h].budget);
     return SAF_OK;
 }
 
@@ -330,7 +350,7 @@ saf_status_t saf_workspace_size(const saf_ctx_t *cc, const saf_head_plan_t *plan
     PlanInfo pi;
     const saf_status_t st = check_plan(c, plan, &pi);
     if (st != SAF_OK) return st;
-    *bytes = (size_t)(pi.vert_ws + pi.split_ws + pi.union_ws + pi.norm_ws) + 256;
+    *bytes = (size_t)(pi.vert_ws + pi.split_ws + pi.union_ws + pi.norm_ws + pi.pack_ws) + 256;
     return SAF_OK;
 }
 
@@ -684,7 +704,7 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
                 return fail(c, SAF_ESTATE, "head %d budget %d differs from the index's K %d (row length %d)", h,
                             plan[h].budget, c->corr_build_k, c->corr_k);
     }
-    size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws + pi.norm_ws);
+    size_t need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws + pi.norm_ws + pi.pack_ws);
     if (need > 0) need += 256;  // room to align the start to 256 bytes
     if (need > 0 && (!ws || ws_bytes < need))
         return fail(c, SAF_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -775,6 +795,44 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
     // correspondence rows (HBM-bound) while the caller's stream runs one
     // matrix-core launch group for every shared-key head; the caller's
     // stream joins the side stream at the end of the call.
+    // Scanning heads' key sets packed into contiguous rows first, while the
+    // GPU is idle (beside the gather their small copies wait for free slots)
+    std::vector<saf::HeadWork> packed(g.H);
+    {
+        saf::MfmaLaunch P{};
+        P.g = g;
+        P.k = k;
+        P.v = v;
+        P.head_stride = lay.head_stride;
+        P.token_stride = lay.token_stride;
+        hipError_t pe = hipSuccess;
+        for (int h = 0; h < g.H && pe == hipSuccess; ++h) {
+            if (plan[h].role != SAF_SCANNING) continue;
+            const int64_t rows = scan_pack_rows(g, plan[h].budget);
+            if (rows == 0) continue;
+            const int64_t half = (int64_t)align256(sizeof(uint16_t) * 64 * (size_t)rows);
+            saf::HeadWork &w = packed[h];
+            w.head = h;
+            w.role = saf::SCANNING;
+            w.budget = plan[h].budget;
+            w.pk = (uint16_t *)wp;
+            w.pv = (uint16_t *)(wp + half);
+            w.pspec = (int32_t *)(wp + 2 * half);
+            w.pcount = (int32_t)rows;
+            wp += scan_pack_bytes(g, plan[h].budget);
+            P.work[P.nwork++] = w;
+            if (P.nwork == saf::kMaxWork) {
+                Timed tm(c, s, "pack_keys");
+                pe = saf::launch_pack_keys(P, s);
+                P.nwork = 0;
+            }
+        }
+        if (pe == hipSuccess && P.nwork) {
+            Timed tm(c, s, "pack_keys");
+            pe = saf::launch_pack_keys(P, s);
+        }
+        if (pe != hipSuccess) return hip_fail(c, pe, "key packing kernels");
+    }
     hipError_t e = build_vertical(s);
     if (e != hipSuccess) return hip_fail(c, e, "vertical index kernels");
     bool forked = false;
@@ -887,11 +945,17 @@ static saf_status_t sparse_attention(saf_ctx_t *c, const saf_head_plan_t *plan, 
             it.tiles = all_tiles;
             it.cost = w.list_len;
             break;
-        case SAF_SCANNING:
+        case SAF_SCANNING: {
             w.rows = saf::ROWS_ALL;
             it.tiles = all_tiles;
             it.cost = (double)((g.N + w.budget - 1) / w.budget) + (double)g.ns * g.S;
+            // one key set for every query, packed above
+            w.pk = packed[h].pk;
+            w.pv = packed[h].pv;
+            w.pspec = packed[h].pspec;
+            w.pcount = packed[h].pcount;
             break;
+        }
         case SAF_DENSE:
             w.rows = saf::ROWS_ALL;
             it.tiles = all_tiles;
@@ -1167,7 +1231,7 @@ saf_status_t saf_layer_internal(saf_ctx_t *c, const saf_head_plan_t *plan, const
     PlanInfo pi;
     saf_status_t st = check_plan(c, plan, &pi);
     if (st != SAF_OK) return st;
-    *ws_need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws + pi.norm_ws) + 256;
+    *ws_need = (size_t)((vert_idx ? 0 : pi.vert_ws) + pi.split_ws + pi.union_ws + pi.norm_ws + pi.pack_ws) + 256;
     if (*ws_need > ws_cap)
         return fail(c, SAF_EUNSUPPORTED, "this plan needs %zu bytes of workspace; the static scratch holds %zu",
                     *ws_need, ws_cap);

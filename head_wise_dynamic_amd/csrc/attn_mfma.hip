@@ -155,22 +155,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const int64_t hoff = (int64_t)w.head * L.head_stride;
     const int64_t ts = L.token_stride;
     const uint16_t *Q = (const uint16_t *)L.q + hoff;
-    const uint16_t *K = (const uint16_t *)L.k + hoff;
-    const uint16_t *V = (const uint16_t *)L.v + hoff;
+    // a packed key set: contiguous rows, key slot = row, no masked slot
+    const bool packed = !DENSE && w.pk != nullptr;
+    const uint16_t *K = packed ? w.pk : (const uint16_t *)L.k + hoff;
+    const uint16_t *V = packed ? w.pv : (const uint16_t *)L.v + hoff;
+    const int64_t kts = packed ? 64 : ts;  // key row stride
 
     // key slots in 32 bits: a key set holds at most N + ns S < 2^31 slots
-    const int32_t count = (int32_t)(DENSE ? g.N : key_count(w, g, rm.qsel));
+    const int32_t count = (int32_t)(DENSE ? g.N : packed ? w.pcount : key_count(w, g, rm.qsel));
     const int32_t per = ((count + w.nsplit - 1) / w.nsplit + KT - 1) / KT * KT;
     const int32_t kbeg = split * per;
     const int32_t kend = min(count, kbeg + per);
-    const int32_t first_masked = DENSE ? INT32_MAX : (int32_t)min<int64_t>(key_first_masked(w, g), INT32_MAX);
+    const int32_t first_masked =
+        (DENSE || packed) ? INT32_MAX : (int32_t)min<int64_t>(key_first_masked(w, g), INT32_MAX);
 
     // Key enumeration without 64-bit divisions (N < 2^31): position and
     // scanning sets are the special tokens (from an LDS table built once per
     // work-group) and affine token ranges; vertical sets come from their
     // list; broadcast sets keep the general enumeration.
     const int32_t nsS = g.ns * g.S;
-    const bool table = !DENSE && (w.role == POSITION || w.role == SCANNING) && nsS <= kSpecTable;
+    const bool table = !DENSE && !packed && (w.role == POSITION || w.role == SCANNING) && nsS <= kSpecTable;
     if (table) {
         for (int i = tid; i < nsS; i += kAttnThreads) {
             const int32_t tok = (i / g.ns) * g.T + i % g.ns;
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const int32_t anchor_base = w.anchor * g.T + g.ns, own_base = rm.qsel * g.T + g.ns;
     const int32_t nst = w.role == SCANNING ? (int32_t)((g.N + w.budget - 1) / w.budget) : 0;
     auto token_of = [&](int64_t m64) -> int64_t {
-        if (DENSE) return m64;
+        if (DENSE || packed) return m64;
         if (!table) return key_token(w, g, m64, rm.qsel);
         const int32_t m = (int32_t)m64;
         if (w.role == POSITION) {
@@ -276,8 +280,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
             for (int i = 0; i < 2; ++i) {
                 kval[j][i] = tk[i] >= 0;
                 const int64_t tc = kval[j][i] ? tk[i] : 0;
-                kreg[j][i] = *(const u32x4 *)(K + tc * ts + 8 * lseg);
-                vreg[j][i] = *(const u32x4 *)(V + tc * ts + 8 * lseg);
+                kreg[j][i] = *(const u32x4 *)(K + tc * kts + 8 * lseg);
+                vreg[j][i] = *(const u32x4 *)(V + tc * kts + 8 * lseg);
             }
         }
     };
@@ -558,6 +562,61 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const MfmaLaunch L, float
     if (tid == 0) parts[wi * kNormParts + p] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// Packed scanning sets: rows [0, nst) are the stride tokens m * s, then the
+// specials not on the stride, in token order.  pack_specials_kernel (one
+// block per work) lists those specials' tokens in order (per-thread keep
+// masks and a block-wide scan of their counts); pack_rows_kernel then copies
+// every row, 8 lanes per 128-byte K or V row, all rows in parallel.
+__global__ __launch_bounds__(256) void pack_specials_kernel(const MfmaLaunch L) {
+    __shared__ uint32_t wsum[4];
+    const HeadWork &w = L.work[blockIdx.y];
+    const Geom &g = L.g;
+    if (!w.pk || g.ns == 0) return;
+    constexpr int kPer = kPackSpecials / 256;  // thread t owns specials [kPer t, kPer t + kPer)
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int32_t s = w.budget, nsS = g.ns * g.S;
+    uint32_t keep = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int32_t m = kPer * tid + i;
+        const int64_t tok = (int64_t)(m / g.ns) * g.T + m % g.ns;
+        if (m < nsS && tok % s != 0) keep |= 1u << i;
+    }
+    const uint32_t c = __popc(keep);
+    uint32_t incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    uint32_t pos = incl - c;
+    for (int i = 0; i < wv; ++i) pos += wsum[i];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if ((keep >> i) & 1u) {
+            const int32_t m = kPer * tid + i;
+            w.pspec[pos++] = (m / g.ns) * g.T + m % g.ns;
+        }
+}
+
+__global__ __launch_bounds__(256) void pack_rows_kernel(const MfmaLaunch L) {
+    const HeadWork &w = L.work[blockIdx.y];
+    if (!w.pk) return;
+    const Geom &g = L.g;
+    const int seg = threadIdx.x & 7;
+    const int64_t hoff = (int64_t)w.head * L.head_stride, ts = L.token_stride;
+    const uint16_t *K = (const uint16_t *)L.k + hoff, *V = (const uint16_t *)L.v + hoff;
+    const int32_t s = w.budget, nst = (int32_t)((g.N + s - 1) / s);
+    for (int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); r < w.pcount; r += (int64_t)gridDim.x * 32) {
+        const int64_t tok = r < nst ? r * s : (int64_t)w.pspec[r - nst];
+        const u32x4 kx = *(const u32x4 *)(K + tok * ts + 8 * seg), vx = *(const u32x4 *)(V + tok * ts + 8 * seg);
+        *(u32x4 *)(w.pk + r * 64 + 8 * seg) = kx;
+        *(u32x4 *)(w.pv + r * 64 + 8 * seg) = vx;
+    }
+}
+
 // Combine key splits: one wave per query row, lane = channel.
 __global__ __launch_bounds__(256) void split_combine_kernel(const MfmaLaunch L) {
     const Geom &g = L.g;
@@ -639,6 +698,17 @@ hipError_t launch_mfma_attention(const MfmaLaunch &L, int32_t nblocks, bool shar
 hipError_t launch_key_norms(const MfmaLaunch &L, float *parts, hipStream_t stream) {
     if (L.nwork <= 0) return hipSuccess;
     hipLaunchKernelGGL(key_norm_kernel, dim3(kNormParts, L.nwork), dim3(256), 0, stream, L, parts);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_keys(const MfmaLaunch &L, hipStream_t stream) {
+    bool any = false;
+    for (int i = 0; i < L.nwork; ++i) any = any || L.work[i].pk != nullptr;
+    if (!any) return hipSuccess;
+    int32_t rows = 0;
+    for (int i = 0; i < L.nwork; ++i) rows = max(rows, L.work[i].pk ? L.work[i].pcount : 0);
+    hipLaunchKernelGGL(pack_specials_kernel, dim3(1, L.nwork), dim3(256), 0, stream, L);
+    hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((rows + 31) / 32), L.nwork), dim3(256), 0, stream, L);
     return hipGetLastError();
 }
 

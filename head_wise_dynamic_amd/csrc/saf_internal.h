@@ -52,6 +52,12 @@ struct HeadWork {
     const int32_t *list;// VERTICAL key list (device, ascending)
     float *part;        // split partials (nsplit > 1 or rec_out): [tiles*QT rows][nsplit] x (m, l, o[64])
     int32_t rec_out;    // write the (m, l, o) record even with nsplit == 1 (merged later)
+    // SCANNING, bf16: the key set gathered once into contiguous rows (the
+    // stride tokens, then the specials off the stride), 64 bf16 per row;
+    // null: keys enumerated and gathered per tile
+    uint16_t *pk, *pv;
+    int32_t *pspec;     // the specials off the stride, in order (filled with pk, pv)
+    int32_t pcount;     // rows of the packed set
 };
 
 // Softmax partial record of one query row: running max m (log2 units of the
@@ -105,6 +111,10 @@ hipError_t launch_mfma_attention(const MfmaLaunch &L, int32_t nblocks, bool shar
 // work wi's head (bf16 K; parts holds kMaxWork * kNormParts floats)
 hipError_t launch_key_norms(const MfmaLaunch &L, float *parts, hipStream_t stream);
 hipError_t launch_split_combine(const MfmaLaunch &L, hipStream_t stream);
+// Fill the packed key sets (pk, pv) of every work of L that has them.
+hipError_t launch_pack_keys(const MfmaLaunch &L, hipStream_t stream);
+// Specials a packed scanning set can hold (ns S at most this).
+constexpr int kPackSpecials = 4096;
 hipError_t launch_valu_attention(const ValuLaunch &L, int64_t nrows, hipStream_t stream);
 // CORR_STRIDE heads (bf16): merge, for every patch row, the stride set's
 // record from the matrix-core kernel (rows = tokens) with the gathered
