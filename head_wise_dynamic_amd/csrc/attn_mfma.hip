@@ -182,10 +182,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
         }
         __syncthreads();
     }
+    // a vertical head's list in the same LDS table (read from memory per tile,
+    // a list entry is one more round trip before the tile's gathers)
+    const bool vtable = !DENSE && w.role == VERTICAL && w.list_len <= kSpecTable;
+    if (vtable) {
+        constexpr int kPer = kSpecTable / kAttnThreads;
+        int32_t e[kPer];  // every entry requested before any is stored (clamped indices)
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) e[j] = w.list[min(tid + kAttnThreads * j, w.list_len - 1)];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (tid + kAttnThreads * j < w.list_len) spec_tok[tid + kAttnThreads * j] = e[j];
+        __syncthreads();
+    }
     const int32_t anchor_base = w.anchor * g.T + g.ns, own_base = rm.qsel * g.T + g.ns;
     const int32_t nst = w.role == SCANNING ? (int32_t)((g.N + w.budget - 1) / w.budget) : 0;
     auto token_of = [&](int64_t m64) -> int64_t {
         if (DENSE || packed) return m64;
+        if (vtable) return spec_tok[(int32_t)m64];
         if (!table) return key_token(w, g, m64, rm.qsel);
         const int32_t m = (int32_t)m64;
         if (w.role == POSITION) {
