@@ -235,3 +235,34 @@ def test_dense_attention_needs_workspace_for_bf16():
         assert saf.saf_workspace_size(c, None, need) == saf.SAF_OK and need.value == 0
     finally:
         saf.saf_destroy(c)
+
+
+@pytest.mark.parametrize("S,ns,P,stride", [(4, 5, 256, 8), (4, 5, 256, 1), (4, 5, 256, 261), (7, 3, 200, 7),
+                                           (3, 0, 100, 16), (100, 5, 1369, 16), (819, 5, 16, 5)])
+def test_workspace_holds_the_packed_scanning_set(S, ns, P, stride):
+    """A bf16 scanning head's packed key set (the stride tokens, then the
+    specials off the stride, plus their token list) is in the workspace: the
+    size grows by exactly that over the same plan with a dense head, which
+    needs none.  Brute-force count of the specials on the stride."""
+    T, N = ns + P, S * (ns + P)
+    on = sum(1 for f in range(S) for t in range(ns) if (f * T + t) % stride == 0)
+    rows = (N + stride - 1) // stride + ns * S - on
+    a256 = lambda x: (x + 255) // 256 * 256
+    expect = 2 * a256(rows * 128) + a256(4 * ns * S + 4)
+    c = _ctx(S, ns, P)
+    try:
+        base = [(0, 0, 0, 0)] * 15
+        ws, wd = C.c_size_t(), C.c_size_t()
+        assert saf.saf_workspace_size(c, _plan(base + [(3, stride, 0, 0)]), ws) == saf.SAF_OK
+        assert saf.saf_workspace_size(c, _plan(base + [(4, 0, 0, 0)]), wd) == saf.SAF_OK
+        assert ws.value - wd.value == expect
+    finally:
+        saf.saf_destroy(c)
+    c = _ctx(S, ns, P, dtype=saf.SAF_F32)   # fp32: the row kernel enumerates the set, nothing packed
+    try:
+        ws, wd = C.c_size_t(), C.c_size_t()
+        assert saf.saf_workspace_size(c, _plan(base + [(3, stride, 0, 0)]), ws) == saf.SAF_OK
+        assert saf.saf_workspace_size(c, _plan(base + [(4, 0, 0, 0)]), wd) == saf.SAF_OK
+        assert ws.value == wd.value
+    finally:
+        saf.saf_destroy(c)
