@@ -343,6 +343,8 @@ def main():
             wl = make_layer_inputs(4, layer=l, dino=False)
             sets.append(tuple(dev(a) for a in (wl.q, wl.k, wl.v)))
             del wl
+            if args.stack_inputs > 3:
+                print(f"[bench] stack input set {l + 1}/{args.stack_inputs}", file=sys.stderr, flush=True)
         print(f"[bench] generated {len(sets)} stack input sets in {time.time() - t_gen:.1f}s", file=sys.stderr,
               flush=True)
         plans = []
