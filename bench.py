@@ -56,28 +56,28 @@ COUNTERS = {
     "groups": {
         "cosine_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "bddb6f37cfe3da0e81df60bc8b8afe971104fa7b5dd0fcbca6c6f787b96d5421",
-            "executed_tflop": 20.034, "mfma_busy": 0.4331,
-            "fetch_kib": 38543207.5, "write_kib": 2033063.6},
+            "executed_tflop": 20.034, "mfma_busy": 0.4367,
+            "fetch_kib": 38557448.1, "write_kib": 2028201.8},
         "per_frame_gemm": {"source": ["head_wise_dynamic_amd/csrc/corr_cos.hip", "head_wise_dynamic_amd/csrc/corr_index.hip"],
             "sha256": "bddb6f37cfe3da0e81df60bc8b8afe971104fa7b5dd0fcbca6c6f787b96d5421",
-            "executed_tflop": 22.8345, "mfma_busy": 0.3482,
-            "fetch_kib": 40211453.6, "write_kib": 6030958.8},
+            "executed_tflop": 22.8345, "mfma_busy": 0.3475,
+            "fetch_kib": 40189044.6, "write_kib": 6029793.2},
         "shared_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "2f832f9ddcb76646404ec6a998f0b43388e88aa72914afa74d710853a9edaf68",
-            "executed_tflop": 2.7005, "mfma_busy": 0.3139,
-            "fetch_kib": 811420.4, "write_kib": 230484.9},
+            "sha256": "ac511e4027adae7c4bc1b54987e0e2f7fde363fc5c4989dd9c5c43f9c5330ce3",
+            "executed_tflop": 2.7005, "mfma_busy": 0.3127,
+            "fetch_kib": 454424.6, "write_kib": 229973.2},
         "shared_attention_alone": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "2f832f9ddcb76646404ec6a998f0b43388e88aa72914afa74d710853a9edaf68",
-            "executed_tflop": 2.6465, "mfma_busy": 0.4472,
-            "fetch_kib": 701989.4, "write_kib": 223279.0},
+            "sha256": "ac511e4027adae7c4bc1b54987e0e2f7fde363fc5c4989dd9c5c43f9c5330ce3",
+            "executed_tflop": 2.6465, "mfma_busy": 0.447,
+            "fetch_kib": 347761.8, "write_kib": 223275.0},
         "dense": {"source": ["head_wise_dynamic_amd/csrc/attn_mfma.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
-            "sha256": "2f832f9ddcb76646404ec6a998f0b43388e88aa72914afa74d710853a9edaf68",
-            "executed_tflop": 77.3724, "mfma_busy": 0.4823,
-            "fetch_kib": 6831377.7, "write_kib": 274800.3},
+            "sha256": "ac511e4027adae7c4bc1b54987e0e2f7fde363fc5c4989dd9c5c43f9c5330ce3",
+            "executed_tflop": 77.3724, "mfma_busy": 0.4934,
+            "fetch_kib": 6825756.2, "write_kib": 274800.4},
         "gather_attention": {"source": ["head_wise_dynamic_amd/csrc/attn_valu.hip", "head_wise_dynamic_amd/csrc/api.cpp"],
             "sha256": "b3ebddeb6183537036f1220e4c0328f5c48983fa7b5e18cb434fe94dfc1add00",
             "executed_tflop": 0.0, "mfma_busy": None,
-            "fetch_kib": 12566659.6, "write_kib": 51337.5},
+            "fetch_kib": 12567492.6, "write_kib": 51337.5},
     },
 }
 

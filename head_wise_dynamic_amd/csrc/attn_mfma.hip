@@ -122,6 +122,18 @@ __device__ __forceinline__ RowMap make_rowmap(const HeadWork &w, const Geom &g, 
 constexpr int kAttnThreads = 256;  // 4 waves x 64 query rows
 constexpr int kSpecTable = 4096;   // special tokens an LDS table holds (ns S <= this)
 
+// Work-groups are dealt to the 8 XCDs in turn (block b runs on XCD b % 8).
+// Runs of kXcdRun consecutive logical blocks (neighbouring query tiles of one
+// head) are kept on one XCD, in dispatch order, so they share its L2.  A
+// bijection on [0, nb): the last nb mod (8 kXcdRun) blocks keep their number.
+constexpr int kXcdRun = 16;
+__device__ __forceinline__ int xcd_grouped(int bid, int nb) {
+    const int full = nb / (8 * kXcdRun) * (8 * kXcdRun);
+    if (bid >= full) return bid;
+    const int xcd = bid & 7, slot = bid >> 3;
+    return ((slot / kXcdRun) * 8 + xcd) * kXcdRun + slot % kXcdRun;
+}
+
 // DENSE = true is the dense flash-attention kernel: every head attends to all
 // N keys, so key tiles are contiguous token ranges [kt, kt + 64): no key-set
 // enumeration, no per-key validity tests except on the ragged last tile.
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void mfma_attn_kernel(const MfmaLa
     const int kx = 4 * ((n >> 2) & 1);  // K rows are read as swap_bits23(n): bit 3 of the row = bit 2 of n
 
     // ---- locate this work-group's head, query tile and key split
-    const int b = blockIdx.x + L.block_base;
+    const int b = (DENSE ? (int)blockIdx.x : xcd_grouped((int)blockIdx.x, (int)gridDim.x)) + L.block_base;
     int wi = 0;
     for (int i = 1; i < L.nwork; ++i)
         if (L.work[i].block0 <= b) wi = i;
